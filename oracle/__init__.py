@@ -1,0 +1,265 @@
+"""Python handle on the fp64 CPU oracle (``oracle/moe_oracle.c``).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the tests, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package.  It never
+imports the HIP library or its binding, and the HIP path never imports it.
+
+Inputs are numpy arrays: ``float32`` for fp32 data, ``uint16`` for bf16 bit
+patterns (the C side widens either exactly to fp64).  Everything the oracle
+computes is fp64.
+
+Each wrapper names the passage it follows; the readings taken where the pages
+are silent are listed at the top of ``moe_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+SOFTMAX_ALL = 0
+SOFTMAX_TOPK = 1
+EXPERT_CHOICE = 2
+GELU = 0
+SWIGLU = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (portable -O2, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.orc_logits.argtypes = [i32, i32, i32, i32, P, P, P, i64, P]
+    lib.orc_softmax.argtypes = [i32, i32, P, P]
+    lib.orc_topk.argtypes = [i32, i32, i32, P, P]
+    lib.orc_gate_weights.argtypes = [i32, i32, i32, i32, P, P, P]
+    lib.orc_capacity.argtypes = [f64, i32, i32, i32]
+    lib.orc_capacity.restype = i64
+    lib.orc_dispatch_topk.argtypes = [i32, i32, i32, i64, P, P, P, P, P, P]
+    lib.orc_dispatch_topk.restype = i64
+    lib.orc_ec_select.argtypes = [i32, i32, i32, P, P]
+    lib.orc_ffn_row.argtypes = [i32, i32, i32, i32, P, i64, P, i64, P, i64, P]
+    lib.orc_moe_rows_topk.argtypes = [i32] * 7 + [P] * 8 + [i32, P, P]
+    lib.orc_moe_rows_ec.argtypes = [i32] * 8 + [P] * 7 + [i32, P, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError(f"oracle input must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _c(a, dtype=None):
+    a = np.asarray(a)
+    if dtype is not None:
+        a = a.astype(dtype, copy=False)
+    return np.ascontiguousarray(a)
+
+
+# ---------------------------------------------------------------------------
+# Steps of the pass, one wrapper each.
+# ---------------------------------------------------------------------------
+
+def logits(x, wr, bias=None, bias_stride: int = 0) -> np.ndarray:
+    """Router logits in fp64 ("Routing Mechanisms": a learned linear gate)."""
+    x, wr = _c(x), _c(wr)
+    assert _dt(x) == _dt(wr)
+    T, d = x.shape
+    E = wr.shape[0]
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.empty((T, E), np.float64)
+    _load().orc_logits(T, d, E, _dt(x), _ptr(x), _ptr(wr), _ptr(b), bias_stride, _ptr(out))
+    return out
+
+
+def softmax(lg) -> np.ndarray:
+    lg = _c(lg, np.float64)
+    T, E = lg.shape
+    out = np.empty_like(lg)
+    _load().orc_softmax(T, E, _ptr(lg), _ptr(out))
+    return out
+
+
+def topk(lg, k: int) -> np.ndarray:
+    """Top-k experts per token by (logit desc, expert asc)."""
+    lg = _c(lg, np.float64)
+    T, E = lg.shape
+    idx = np.empty((T, k), np.int32)
+    _load().orc_topk(T, E, k, _ptr(lg), _ptr(idx))
+    return idx
+
+
+def gate_weights(lg, idx, mode: int) -> np.ndarray:
+    lg, idx = _c(lg, np.float64), _c(idx, np.int32)
+    T, E = lg.shape
+    k = idx.shape[1]
+    w = np.empty((T, k), np.float64)
+    _load().orc_gate_weights(T, E, k, mode, _ptr(lg), _ptr(idx), _ptr(w))
+    return w
+
+
+def capacity(cf: float, T: int, k: int, E: int) -> int:
+    """Capacity per expert ("Expert Parallelism > Key Parameters",
+    capacity_factor); -1 for dropless."""
+    return int(_load().orc_capacity(float(cf), T, k, E))
+
+
+@dataclass
+class Dispatch:
+    slot_row: np.ndarray      # [T,k] int32, -1 = dropped
+    row_token: np.ndarray     # [N] int32
+    expert_count: np.ndarray  # [E] kept rows per expert
+    expert_load: np.ndarray   # [E] assignments per expert before dropping
+    expert_offset: np.ndarray  # [E+1]
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.expert_offset[-1])
+
+
+def dispatch_topk(idx, E: int, cap: int) -> Dispatch:
+    """token_permutation with the capacity drop rule."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    slot_row = np.empty((T, k), np.int32)
+    row_token = np.full(max(T * k, 1), -1, np.int32)
+    cnt = np.empty(E, np.int32)
+    load = np.empty(E, np.int32)
+    off = np.empty(E + 1, np.int32)
+    n = _load().orc_dispatch_topk(T, E, k, cap, _ptr(idx), _ptr(slot_row), _ptr(row_token),
+                                  _ptr(cnt), _ptr(load), _ptr(off))
+    return Dispatch(slot_row, row_token[:n].copy(), cnt, load, off)
+
+
+def ec_select(scores, C: int) -> np.ndarray:
+    """ExpertChoice: the C best tokens of each expert column, ascending token."""
+    s = _c(scores, np.float64)
+    T, E = s.shape
+    out = np.empty((E, C), np.int32)
+    _load().orc_ec_select(T, E, C, _ptr(s), _ptr(out))
+    return out
+
+
+def ffn_row(x_row, w1_e, w2_e, act: int) -> np.ndarray:
+    """One expert FFN on one row (fp64)."""
+    x_row, w1_e, w2_e = _c(x_row), _c(w1_e), _c(w2_e)
+    d = x_row.shape[-1]
+    dff = w2_e.shape[-1]
+    y = np.empty(d, np.float64)
+    _load().orc_ffn_row(d, dff, act, _dt(x_row), _ptr(x_row), 0, _ptr(w1_e), 0, _ptr(w2_e), 0, _ptr(y))
+    return y
+
+
+def moe_rows_topk(x, idx, w, slot_row, w1, w2, act: int, toks, ws1=None, ws2=None) -> np.ndarray:
+    """Layer output rows for the listed tokens, top-k routing."""
+    x, idx, slot_row = _c(x), _c(idx, np.int32), _c(slot_row, np.int32)
+    w = _c(w, np.float64)
+    w1, w2 = _c(w1), _c(w2)
+    toks = _c(toks, np.int32)
+    T, d = x.shape
+    E, _, dff = w2.shape
+    k = idx.shape[1]
+    dffs = 0 if ws2 is None else ws2.shape[-1]
+    ws1 = None if ws1 is None else _c(ws1)
+    ws2 = None if ws2 is None else _c(ws2)
+    y = np.empty((len(toks), d), np.float64)
+    _load().orc_moe_rows_topk(d, E, k, dff, dffs, act, _dt(x), _ptr(x), _ptr(idx), _ptr(w),
+                              _ptr(slot_row), _ptr(w1), _ptr(w2), _ptr(ws1), _ptr(ws2),
+                              len(toks), _ptr(toks), _ptr(y))
+    return y
+
+
+def moe_rows_ec(x, ec_token, scores, w1, w2, act: int, toks, ws1=None, ws2=None) -> np.ndarray:
+    """Layer output rows for the listed tokens, ExpertChoice routing."""
+    x, ec_token = _c(x), _c(ec_token, np.int32)
+    scores = _c(scores, np.float64)
+    w1, w2 = _c(w1), _c(w2)
+    toks = _c(toks, np.int32)
+    T, d = x.shape
+    E, C = ec_token.shape
+    dff = w2.shape[-1]
+    dffs = 0 if ws2 is None else ws2.shape[-1]
+    ws1 = None if ws1 is None else _c(ws1)
+    ws2 = None if ws2 is None else _c(ws2)
+    y = np.empty((len(toks), d), np.float64)
+    _load().orc_moe_rows_ec(T, d, E, C, dff, dffs, act, _dt(x), _ptr(x), _ptr(ec_token), _ptr(scores),
+                            _ptr(w1), _ptr(w2), _ptr(ws1), _ptr(ws2), len(toks), _ptr(toks), _ptr(y))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# The whole pass, composed from the steps above.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class LayerResult:
+    logits: np.ndarray                 # [T,E] fp64 (or the fp32 logits it was given)
+    idx: Optional[np.ndarray] = None   # top-k [T,k]
+    w: Optional[np.ndarray] = None     # top-k weights [T,k]
+    dispatch: Optional[Dispatch] = None
+    scores: Optional[np.ndarray] = None  # EC softmax [T,E]
+    ec_token: Optional[np.ndarray] = None  # EC [E,C]
+    y: Optional[np.ndarray] = None     # [len(toks), d]
+    toks: Optional[np.ndarray] = None
+
+
+def layer(x, wr, w1, w2, *, k: int, routing: int, act: int, cf: float = 0.0, ec_capacity: int = 0,
+          bias=None, bias_stride: int = 0, ws1=None, ws2=None, given_logits=None, given_scores=None,
+          toks=None) -> LayerResult:
+    """The forward pass of one MoE block ("Core MoE Layer Architecture",
+    MoELayer / MoELayerExpertChoice), in fp64, for the listed tokens.
+
+    ``given_logits`` (fp32 values) replaces the oracle's own fp64 logits for
+    every decision that floating point turns into an integer; ``given_scores``
+    does the same for the ExpertChoice scores."""
+    T = x.shape[0]
+    E = wr.shape[0]
+    lg = logits(x, wr, bias, bias_stride) if given_logits is None else _c(given_logits, np.float64)
+    if toks is None:
+        toks = np.arange(T, dtype=np.int32)
+    res = LayerResult(logits=lg, toks=np.asarray(toks, np.int32))
+    if routing == EXPERT_CHOICE:
+        sc = softmax(lg) if given_scores is None else _c(given_scores, np.float64)
+        res.scores = sc
+        res.ec_token = ec_select(sc, ec_capacity)
+        # weights are the oracle's own fp64 softmax at the chosen entries
+        res.y = moe_rows_ec(x, res.ec_token, softmax(lg), w1, w2, act, res.toks, ws1, ws2)
+        return res
+    res.idx = topk(lg, k)
+    res.w = gate_weights(lg, res.idx, routing)
+    res.dispatch = dispatch_topk(res.idx, E, capacity(cf, T, k, E))
+    res.y = moe_rows_topk(x, res.idx, res.w, res.dispatch.slot_row, w1, w2, act, res.toks, ws1, ws2)
+    return res
