@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE layer forward tokens/s on one MI355X.
+
+One step = the whole forward pass of one MoE block (route, permute, grouped
+expert FFN, shared expert when present, unpermute) over one batch of seeded
+synthetic tokens already resident in HBM, through the C ABI.  The timed loop
+calls the entry points back to back on one stream (the same kernels, in the
+same order, as moe_layer_fwd) and records a HIP event between the stages, so
+each stage's average duration comes from the timed region itself.
+
+Prints one JSON line.  ``roofline`` reports the grouped expert FFN (the
+dominant stage: its two GEMM launches) against the bf16 MFMA peak;
+``stages`` gives every stage's time and its algorithmic HBM rate or FLOP rate;
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DEFAULT_WORKLOAD = "mixtral_top2_bf16"
+METRIC = "MoE layer fwd tokens/sec at 1 GPU; grouped-GEMM % MFMA peak; permute GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-sample", type=int, default=48, help="tokens the oracle computes for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic(w, n_rows: int, n_active: int):
+    """Algorithmic work per stage (bytes or flops), from the kept rows N and
+    the number of experts that received rows."""
+    s = w.elem_bytes
+    T, d, E = w.T, w.d, w.E
+    k = w.k if w.routing != 2 else 0
+    A = w.assignments
+    n_mat = 3 if w.act == 1 else 2
+    out = {}
+    route_b = T * d * s + E * d * s + T * E * 4 + (T * k * 8 if k else T * E * 4 + E * w.ec_capacity * 8)
+    out["route"] = ("bytes", route_b)
+    out["permute"] = ("bytes", T * d * s + n_rows * d * s + A * 12)
+    ffn_flops = n_rows * 2 * n_mat * d * w.d_ff
+    w_bytes = n_active * n_mat * d * w.d_ff * s
+    out["expert_ffn"] = ("flops", ffn_flops, w_bytes + n_rows * d * s * 2 + n_rows * w.d_ff * s * 2)
+    if w.d_ff_shared:
+        out["shared_ffn"] = ("flops", T * 2 * n_mat * d * w.d_ff_shared)
+    out["unpermute"] = ("bytes", n_rows * d * s + T * d * s + (T * d * s if w.d_ff_shared else 0) + A * 8)
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU exchange is not built",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_layer_topkrouter_amd import moe
+    from mixture_experts_layer_topkrouter_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+    t_gen = time.time()
+    inp = W.make_inputs(w, seed=0)
+    t_gen = time.time() - t_gen
+    cfg = moe.make_config(w)
+    dev = moe.upload(inp)
+    layer = moe.MoELayer(cfg, dev)  # owns the workspace and y; its views are the intermediates
+    T, E, d = w.T, w.E, w.d
+    ec = w.routing == W.EXPERT_CHOICE
+    k = 0 if ec else w.k
+    V = layer.view
+    logits = V("logits")
+    x_perm, row_token, slot_row = V("x_perm"), V("row_token"), V("slot_row")
+    cnt, load, off = V("expert_count"), V("expert_load"), V("expert_offset")
+    h, y_perm = V("h"), V("y_perm")
+    L = layer.layout
+    scratch = layer.workspace[L["scratch"]:L["scratch"] + max(L["scratch_bytes"], 1)]
+    if ec:
+        scores, ec_token, ec_w = V("scores"), V("ec_token"), V("ec_w")
+        slot_w, tok_ptr = V("slot_w"), V("tok_ptr")
+    else:
+        topk_idx, topk_w = V("topk_idx"), V("topk_w")
+    if w.d_ff_shared:
+        scfg = moe.MoeConfig(T, d, 1, 1, w.d_ff_shared, 0, 0.0, 0, w.dtype, w.act, W.SOFTMAX_ALL)
+        soff = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+        hs, ys = V("shared_h"), V("shared_y")
+    stream = torch.cuda.current_stream()
+    names = ["route", "permute", "expert_ffn"] + (["shared_ffn"] if w.d_ff_shared else []) + ["unpermute"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if ec:
+            moe.route(cfg, dev.x, dev.wr, logits, bias=dev.bias, bias_stride=dev.bias_stride, scores=scores,
+                      ec_token=ec_token, ec_w=ec_w)
+        else:
+            moe.route(cfg, dev.x, dev.wr, logits, topk_idx, topk_w, bias=dev.bias, bias_stride=dev.bias_stride)
+        if ev is not None:
+            ev[1].record(stream)
+        if ec:
+            moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off, ec_token=ec_token, ec_w=ec_w,
+                        slot_w=slot_w, tok_ptr=tok_ptr)
+        else:
+            moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off, topk_idx=topk_idx, scratch=scratch)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.expert_ffn(cfg, x_perm, off, dev.w1, dev.w2, h, y_perm)
+        i = 3
+        if ev is not None:
+            ev[i].record(stream)
+        y_sh = None
+        if w.d_ff_shared:
+            moe.expert_ffn(scfg, dev.x, soff, dev.ws1, dev.ws2, hs, ys)
+            y_sh = ys
+            i += 1
+            if ev is not None:
+                ev[i].record(stream)
+        if ec:
+            moe.unpermute(cfg, y_perm, slot_row, slot_w, layer.y, tok_ptr=tok_ptr, y_shared=y_sh)
+        else:
+            moe.unpermute(cfg, y_perm, slot_row, topk_w, layer.y, y_shared=y_sh)
+        if ev is not None:
+            ev[i + 1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(names)}
+    ev_total_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][-1]) for i in range(args.steps)]))
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # the layer entry point gives the same bits (checked by the tests); run it once here as well
+    y_steps = layer.y.clone()
+    layer.forward()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y_steps.view(torch.int16) if y_steps.dtype == torch.bfloat16 else y_steps,
+                            layer.y.view(torch.int16) if layer.y.dtype == torch.bfloat16 else layer.y))
+
+    n_rows = int(off[-1].item())
+    counts = cnt.cpu().numpy()
+    n_active = int((counts > 0).sum())
+    work = algorithmic(w, n_rows, n_active)
+    stages = {}
+    for n in names:
+        kind = work[n][0]
+        sec = stage_ms[n] / 1e3
+        ent = {"ms": round(stage_ms[n], 4)}
+        if kind == "bytes":
+            ent["GB/s"] = round(work[n][1] / sec / 1e9, 1)
+            ent["hbm_frac"] = round(work[n][1] / sec / 1e9 / PEAK_HBM_GBS, 4)
+            ent["bytes"] = int(work[n][1])
+        else:
+            tf = work[n][1] / sec / 1e12
+            peak = PEAK_BF16_TFLOPS if w.dtype == W.BF16 else PEAK_F32_TFLOPS
+            ent["TFLOP/s"] = round(tf, 1)
+            ent["mfma_frac" if w.dtype == W.BF16 else "fp32_frac"] = round(tf / peak, 4)
+            ent["flops"] = int(work[n][1])
+            if len(work[n]) > 2:
+                ent["min_bytes"] = int(work[n][2])
+        stages[n] = ent
+
+    ffn_flops = work["expert_ffn"][1]
+    ffn_s = stage_ms["expert_ffn"] / 1e3
+    peak = PEAK_BF16_TFLOPS if w.dtype == W.BF16 else PEAK_F32_TFLOPS
+    achieved = ffn_flops / ffn_s / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "grouped expert FFN: gemm_bf16_kernel GEMM1 (SwiGLU) + GEMM2, one moe_expert_ffn call",
+                "avg_ms": round(stage_ms["expert_ffn"], 4), "flops_per_launch": int(ffn_flops)}
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rng = np.random.default_rng(123)
+        toks = np.sort(rng.choice(T, size=min(args.cpu_sample, T), replace=False)).astype(np.int32)
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        tc = time.perf_counter()
+        ref = oracle.layer(inp["x"], inp["wr"], inp["w1"], inp["w2"], k=w.k, routing=w.routing, act=w.act, cf=w.cf,
+                           ec_capacity=w.ec_capacity, bias=inp["bias"], bias_stride=inp["bias_stride"],
+                           ws1=inp["ws1"], ws2=inp["ws2"], toks=toks)
+        tc = time.perf_counter() - tc
+        cpu = {"value": round(len(toks) / tc, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"fp64 oracle: router logits, gate and dispatch of all {T} tokens plus the expert FFN "
+                         f"and combine of {len(toks)} sampled tokens; value = sampled tokens / wall time "
+                         f"({tc:.1f} s)"}
+        y = layer.y.float().cpu().numpy().astype(np.float64)[toks]
+        parity = float(np.max(np.abs(y - ref.y)) / np.max(np.abs(ref.y)))
+
+    out = {
+        "metric": METRIC,
+        "value": round(T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == W.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "d_model": d, "num_experts": E, "top_k": w.k, "d_ff": w.d_ff,
+                   "d_ff_shared": w.d_ff_shared, "capacity_factor": w.cf, "routing": w.routing, "act": w.act,
+                   "kept_rows": n_rows, "active_experts": n_active},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "event_ms_per_step": round(ev_total_ms, 4),
+        "layer_fwd_matches_steps": same,
+        "parity_max_rel_err_sampled": parity,
+        "device": dev_name,
+        "input_gen_s": round(t_gen, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) forward pass of one Mixture-of-Experts
+ * block on one GPU's share of tokens and its local experts.
+ *
+ * The operations follow two pages:
+ *   [P1] "How MegaDLMs Implements Mixture of Experts (MoE) Architectures"
+ *   [P3] "Expert Parallelism > Key Parameters"
+ * and are cited by page and section at each entry point.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are dense row-major device buffers.  Weights use the
+ *   [out_features, in_features] layout, so every contraction reads both
+ *   operands along their contiguous inner dimension.
+ * - Floating-point tensors hold `cfg->dtype` elements (fp32 or bf16) unless
+ *   the argument says fp32.  Indices are int32.
+ * - The caller owns every buffer.  The library never allocates, frees or
+ *   synchronises; every call only enqueues work on `stream` (a hipStream_t
+ *   passed as void*, NULL = the null stream) and returns.
+ * - Arguments are checked on the host before anything is enqueued.  A failed
+ *   check returns MOE_ERR_INVALID_ARG (or MOE_ERR_UNSUPPORTED for a valid but
+ *   unimplemented combination) and enqueues nothing.  A failed launch returns
+ *   MOE_ERR_HIP.  No exception crosses the ABI.
+ * - The host never learns how many assignments survive the capacity limit:
+ *   buffers indexed by permuted row are sized for moe_max_rows() rows, and
+ *   expert_offset[E] (device) holds the number actually used.
+ * - Same inputs give bitwise-identical outputs (no floating-point atomics).
+ * - Pointers to floating-point tensors must be 16-byte aligned; d_model and
+ *   d_ff (and d_ff_shared) must be multiples of 8.
+ * - T = 0 is valid: every call returns MOE_OK and buffers whose size is zero
+ *   may be NULL; moe_permute still writes the (zero) counts and offsets.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a host-side check failed; nothing was enqueued */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. E > 256)        */
+  MOE_ERR_WORKSPACE = 3,   /* workspace/scratch smaller than required          */
+  MOE_ERR_HIP = 4          /* a HIP launch failed                              */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+
+/* [P1] "Routing Mechanisms: Top-K vs Expert Choice": the TopKRouter (softmax
+ * and top-k per token) and the ExpertChoiceRouter (each expert picks tokens).
+ * SOFTMAX_ALL: gate weight = softmax over all E logits at the chosen expert
+ *              (not renormalised over the k chosen).
+ * SOFTMAX_TOPK: gate weights = softmax over the k chosen logits.            */
+typedef enum {
+  MOE_TOPK_SOFTMAX_ALL = 0,
+  MOE_TOPK_SOFTMAX_TOPK = 1,
+  MOE_EXPERT_CHOICE = 2
+} moe_routing;
+
+/* The problem statement: [P1] "Configuration-Driven MoE Activation"
+ * (num_moe_experts, moe_shared_expert_intermediate_size) and [P3] (num_experts,
+ * top_k, capacity_factor). */
+typedef struct {
+  int32_t num_tokens;      /* T >= 0: tokens on this GPU                         */
+  int32_t d_model;         /* d: token width, multiple of 8                      */
+  int32_t num_experts;     /* E: local experts, 1..256                           */
+  int32_t top_k;           /* k: experts per token, 1..min(E,16) (top-k modes)   */
+  int32_t d_ff;            /* expert hidden width, multiple of 8                 */
+  int32_t d_ff_shared;     /* shared expert hidden width, 0 = no shared expert   */
+  float capacity_factor;   /* [P3] capacity_factor; 0 = dropless ([P1]
+                              "Activation Checkpointing and Constraints")       */
+  int32_t ec_capacity;     /* ExpertChoice: tokens per expert, 1..T             */
+  int32_t dtype;           /* moe_dtype of x, weights and activations            */
+  int32_t act;             /* moe_act of the routed and the shared experts       */
+  int32_t routing;         /* moe_routing                                        */
+} moe_config;
+
+/* Number of permuted rows buffers must hold: T*k dropless, min(T*k, E*C) with
+ * capacity C = ceil(capacity_factor*T*k/E), E*ec_capacity for ExpertChoice. */
+int64_t moe_max_rows(const moe_config *cfg);
+
+/* Capacity C = ceil(cf*T*k/E) of [P3] "Key Parameters" (capacity_factor: cf
+ * times the expected average load), or -1 when dropless or ExpertChoice. */
+int64_t moe_capacity(const moe_config *cfg);
+
+/* --------------------------------------------------------------------------
+ * moe_route -- [P1] "Routing Mechanisms: Top-K vs Expert Choice".
+ *
+ * logits[t,e] = sum_i x[t,i] * w_router[e,i] (+ bias), fp32 accumulation.
+ *   x         [T,d] dtype, or NULL: then `logits` is an INPUT and only the gate
+ *             below runs on it (bias is then ignored).
+ *   w_router  [E,d] dtype (ignored when x is NULL).
+ *   logit_bias fp32, NULL = none; bias_row_stride 0: bias[e] for every token,
+ *             E: bias[t*E+e].
+ *   logits    [T,E] fp32 output (or input, see x).
+ * Top-k modes: topk_idx [T,k] int32 gets the k best experts by logit, slot j
+ *   the j-th best, equal logits going to the lower expert index (IEEE
+ *   equality, -0 == +0); topk_w [T,k] fp32 gets the gate weights (see
+ *   moe_routing).  scores/ec_token/ec_w are ignored and may be NULL.
+ * ExpertChoice: scores [T,E] fp32 = softmax over E per token; expert e keeps
+ *   the ec_capacity tokens with the largest score in its column (equal scores
+ *   to the lower token), stored in ascending token order in ec_token [E,C];
+ *   ec_w [E,C] fp32 = their scores.  Requires T <= 16384.  topk_* ignored.
+ * ------------------------------------------------------------------------ */
+moe_status moe_route(const moe_config *cfg, const void *x, const void *w_router,
+                     const float *logit_bias, int64_t bias_row_stride, float *logits,
+                     int32_t *topk_idx, float *topk_w, float *scores, int32_t *ec_token,
+                     float *ec_w, void *stream);
+
+/* Bytes of device scratch moe_permute needs (per-block counts and ranks). */
+moe_status moe_permute_scratch_bytes(const moe_config *cfg, size_t *bytes);
+
+/* --------------------------------------------------------------------------
+ * moe_permute -- [P1] "Token Dispatching and Communication"
+ * (token_permutation, the single-GPU part) with the [P3] capacity_factor drop
+ * rule (overflow assignments are dropped and contribute zero).
+ *
+ * Top-k modes (reads topk_idx [T,k]):
+ *   Assignments (t,j) compete for capacity in token order, then slot order.
+ *   rank(t,j) = number of earlier assignments to the same expert; kept iff
+ *   rank < C (always when dropless).  Kept rows are expert-major, ascending
+ *   token inside an expert:
+ *     expert_load[E]    assignments per expert before dropping
+ *     expert_count[E]   kept rows per expert = min(load, C)
+ *     expert_offset[E+1] exclusive scan of expert_count; [E] = rows used
+ *     slot_row [T,k]    row of (t,j), or -1 when dropped (the drop mask)
+ *     row_token[rows]   token of each row
+ *     x_perm [rows,d]   x[row_token[r]] for r < expert_offset[E]
+ *   ec_token, ec_w, slot_w, tok_ptr are ignored (may be NULL).
+ * ExpertChoice (reads ec_token [E,C], ec_w [E,C]):
+ *   row e*C+i holds token ec_token[e,i]; expert_count = expert_load = C;
+ *   tok_ptr [T+1] and slot_row/slot_w [E*C] form a per-token list (CSR) of the
+ *   rows holding that token and their weights, in ascending expert order.
+ * scratch: moe_permute_scratch_bytes() bytes of device memory, 16-B aligned.
+ * ------------------------------------------------------------------------ */
+moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                       const int32_t *ec_token, const float *ec_w, void *x_perm,
+                       int32_t *row_token, int32_t *slot_row, float *slot_w, int32_t *tok_ptr,
+                       int32_t *expert_count, int32_t *expert_load, int32_t *expert_offset,
+                       void *scratch, size_t scratch_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * moe_expert_ffn -- [P1] "Core MoE Layer Architecture" (MoELayer step 2: the
+ * local experts process their dispatched tokens).  For every expert e, rows
+ * [expert_offset[e], expert_offset[e+1]) of x_perm go through
+ *   GELU:   h = gelu(x W1_e^T)                   (exact erf form)
+ *   SwiGLU: h = silu(x Wg_e^T) * (x Wu_e^T)      (W1_e rows: gate, then up)
+ *   y = h W2_e^T
+ * with fp32 accumulation; h and y are rounded to dtype once.
+ *   x_perm [rows,d], w1 [E, n_up*d_ff, d] (n_up = 2 for SwiGLU), w2 [E, d, d_ff],
+ *   expert_offset [E+1] int32 (device), h [rows,d_ff] (workspace the caller
+ *   owns), y_perm [rows,d].  rows = moe_max_rows(cfg).
+ * The shared expert ([P3] "Key Parameters", top_k paragraph: a shared expert
+ * every token uses) is this call with num_experts = 1, top_k = 1, dropless,
+ * d_ff = d_ff_shared, expert_offset = {0, T} and x_perm = x.
+ * ------------------------------------------------------------------------ */
+moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
+                          const void *w1, const void *w2, void *h, void *y_perm, void *stream);
+
+/* --------------------------------------------------------------------------
+ * moe_unpermute -- [P1] "Token Dispatching and Communication"
+ * (token_unpermutation) and "Core MoE Layer Architecture" step 3.
+ *   y[t] = sum over t's slots s with slot_row[s] >= 0, in slot order, of
+ *          slot_w[s] * y_perm[slot_row[s]]   (+ y_shared[t] if given)
+ * fp32 accumulation, one rounding to dtype.  Dropped slots contribute zero
+ * ([P3] capacity_factor paragraph); a token with no kept slot gets 0.
+ *   tok_ptr NULL: token t's slots are [t*k, t*k+k) (top-k: slot_row [T,k],
+ *                 slot_w = topk_w [T,k]);
+ *   tok_ptr [T+1]: slots [tok_ptr[t], tok_ptr[t+1]) (ExpertChoice CSR).
+ *   y_shared [T,d] or NULL; y [T,d].
+ * ------------------------------------------------------------------------ */
+moe_status moe_unpermute(const moe_config *cfg, const void *y_perm, const int32_t *tok_ptr,
+                         const int32_t *slot_row, const float *slot_w, const void *y_shared,
+                         void *y, void *stream);
+
+/* Byte offsets of every intermediate inside moe_layer_fwd's workspace, so a
+ * caller can inspect routing, permutation and expert outputs afterwards.
+ * Unused entries (e.g. scores under top-k) have size 0 and repeat an offset. */
+typedef struct {
+  size_t logits, topk_idx, topk_w, scores, ec_token, ec_w;
+  size_t x_perm, row_token, slot_row, slot_w, tok_ptr;
+  size_t expert_count, expert_load, expert_offset, shared_offset;
+  size_t h, y_perm, shared_h, shared_y, scratch, scratch_bytes;
+  size_t total; /* bytes the workspace must hold */
+} moe_workspace_layout;
+
+moe_status moe_layer_workspace(const moe_config *cfg, moe_workspace_layout *layout);
+
+/* --------------------------------------------------------------------------
+ * moe_layer_fwd -- the whole MoE block forward ([P1] "Core MoE Layer
+ * Architecture": MoELayer / MoELayerExpertChoice): route, permute, routed
+ * experts, shared expert (when d_ff_shared > 0, weight 1), unpermute; one
+ * stream, no host synchronisation.
+ *   x [T,d], w_router [E,d], logit_bias as in moe_route, w1/w2 as in
+ *   moe_expert_ffn, ws1 [n_up*d_ff_shared, d] / ws2 [d, d_ff_shared] (NULL
+ *   when d_ff_shared == 0), y [T,d] output.
+ *   workspace: moe_layer_workspace().total bytes, 256-B aligned.
+ * ------------------------------------------------------------------------ */
+moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_router,
+                         const float *logit_bias, int64_t bias_row_stride, const void *w1,
+                         const void *w2, const void *ws1, const void *ws2, void *y,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+const char *moe_status_string(moe_status s);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

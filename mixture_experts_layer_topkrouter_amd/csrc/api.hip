@@ -1,0 +1,393 @@
+// C ABI entry points (include/moe.h): host-side validation, workspace
+// layout and the enqueue sequence of the forward pass.  Every check runs
+// before anything is enqueued; nothing here allocates, frees or waits.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using moe::kEcMaxTokens;
+using moe::kMaxExperts;
+using moe::kMaxTopK;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(const moe_config *c) { return c->dtype == MOE_F32 ? 4 : 2; }
+
+// Shape checks shared by every entry point.
+moe_status check_config(const moe_config *c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->num_tokens < 0 || c->d_model <= 0 || c->num_experts <= 0 || c->d_ff <= 0 || c->d_ff_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->d_model % 8 || c->d_ff % 8 || c->d_ff_shared % 8) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (!(c->capacity_factor >= 0.f) || !isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (c->routing == MOE_EXPERT_CHOICE) {
+    if (c->num_tokens < 1 || c->ec_capacity < 1 || c->ec_capacity > c->num_tokens) return MOE_ERR_INVALID_ARG;
+    if (c->num_tokens > kEcMaxTokens) return MOE_ERR_UNSUPPORTED;
+  } else if (c->routing == MOE_TOPK_SOFTMAX_ALL || c->routing == MOE_TOPK_SOFTMAX_TOPK) {
+    if (c->top_k < 1 || c->top_k > c->num_experts) return MOE_ERR_INVALID_ARG;
+    if (c->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  } else {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (c->num_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t capacity_of(const moe_config *c) {
+  if (c->routing == MOE_EXPERT_CHOICE || c->capacity_factor == 0.f) return -1;
+  const double v = ceil(static_cast<double>(c->capacity_factor) * c->num_tokens * c->top_k / c->num_experts);
+  return static_cast<int64_t>(v);
+}
+
+int64_t max_rows_of(const moe_config *c) {
+  if (c->routing == MOE_EXPERT_CHOICE) return static_cast<int64_t>(c->num_experts) * c->ec_capacity;
+  const int64_t a = static_cast<int64_t>(c->num_tokens) * c->top_k;
+  const int64_t cap = capacity_of(c);
+  if (cap < 0) return a;
+  const int64_t lim = cap * c->num_experts;
+  return a < lim ? a : lim;
+}
+
+// 32-bit element offsets inside the GEMM kernels must not overflow.
+bool gemm_fits(const moe_config *c, int64_t rows, int dff) {
+  const int64_t lim = INT32_MAX;
+  const int64_t n_up = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+  return rows * c->d_model < lim && rows * dff < lim && n_up * dff * c->d_model < lim;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+moe_status route_impl(const moe_config *cfg, const void *x, const void *w_router, const float *bias,
+                      int64_t bias_stride, float *logits, int32_t *topk_idx, float *topk_w, float *scores,
+                      int32_t *ec_token, float *ec_w, void *stream) {
+  const int T = cfg->num_tokens, E = cfg->num_experts;
+  if (T == 0) return MOE_OK;  // nothing to route; empty buffers may be NULL
+  if (!logits) return MOE_ERR_INVALID_ARG;
+  if (x) {
+    if (!w_router || !aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+    if (bias && bias_stride != 0 && bias_stride != E) return MOE_ERR_INVALID_ARG;
+  }
+  if (cfg->routing == MOE_EXPERT_CHOICE) {
+    if (!scores || !ec_token || !ec_w) return MOE_ERR_INVALID_ARG;
+  } else if (!topk_idx || !topk_w) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  moe::RouteArgs a{};
+  a.dtype = cfg->dtype;
+  a.x = x;
+  a.wr = w_router;
+  a.bias = x ? bias : nullptr;
+  a.bias_stride = bias_stride;
+  a.T = T;
+  a.d = cfg->d_model;
+  a.E = E;
+  a.k = cfg->routing == MOE_EXPERT_CHOICE ? 0 : cfg->top_k;
+  a.routing = cfg->routing;
+  a.C = cfg->ec_capacity;
+  a.logits = logits;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.scores = scores;
+  a.ec_token = ec_token;
+  a.ec_w = ec_w;
+  return hip_status(moe::launch_route(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status permute_impl(const moe_config *cfg, const void *x, const int32_t *topk_idx, const int32_t *ec_token,
+                        const float *ec_w, void *x_perm, int32_t *row_token, int32_t *slot_row, float *slot_w,
+                        int32_t *tok_ptr, int32_t *expert_count, int32_t *expert_load, int32_t *expert_offset,
+                        void *scratch, size_t scratch_bytes, void *stream) {
+  if (!expert_count || !expert_load || !expert_offset) return MOE_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool empty = cfg->num_tokens == 0;  // only the (zero) counts and offsets are written
+  if (!empty && (!x || !x_perm || !row_token || !slot_row)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  if (cfg->routing == MOE_EXPERT_CHOICE) {
+    if (!ec_token || !ec_w || !slot_w || !tok_ptr) return MOE_ERR_INVALID_ARG;
+    moe::PermuteEcArgs a{};
+    a.T = cfg->num_tokens;
+    a.E = cfg->num_experts;
+    a.C = cfg->ec_capacity;
+    a.row_bytes = static_cast<size_t>(cfg->d_model) * elem_bytes(cfg);
+    a.x = x;
+    a.ec_token = ec_token;
+    a.ec_w = ec_w;
+    a.x_perm = x_perm;
+    a.row_token = row_token;
+    a.slot_row = slot_row;
+    a.tok_ptr = tok_ptr;
+    a.expert_count = expert_count;
+    a.expert_load = expert_load;
+    a.expert_offset = expert_offset;
+    a.slot_w = slot_w;
+    return hip_status(moe::launch_permute_ec(a, st));
+  }
+  if (!empty && !topk_idx) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::permute_scratch_bytes(cfg->num_tokens, cfg->top_k, cfg->num_experts);
+  if (need > 0 && (!scratch || scratch_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (scratch && !aligned16(scratch)) return MOE_ERR_INVALID_ARG;
+  const int64_t A = static_cast<int64_t>(cfg->num_tokens) * cfg->top_k;
+  const int64_t nblk = (A + moe::kPermuteBlock - 1) / moe::kPermuteBlock;
+  moe::PermuteArgs a{};
+  a.T = cfg->num_tokens;
+  a.k = cfg->top_k;
+  a.E = cfg->num_experts;
+  a.cap = capacity_of(cfg);
+  a.row_bytes = static_cast<size_t>(cfg->d_model) * elem_bytes(cfg);
+  a.x = x;
+  a.topk_idx = topk_idx;
+  a.x_perm = x_perm;
+  a.row_token = row_token;
+  a.slot_row = slot_row;
+  a.expert_count = expert_count;
+  a.expert_load = expert_load;
+  a.expert_offset = expert_offset;
+  a.blk = static_cast<int32_t *>(scratch);
+  a.rank = reinterpret_cast<int32_t *>(static_cast<char *>(scratch) +
+                                       align256(static_cast<size_t>(nblk * cfg->num_experts) * 4));
+  return hip_status(moe::launch_permute_topk(a, st));
+}
+
+moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset, const void *w1,
+                    const void *w2, void *h, void *y_perm, void *stream) {
+  if (max_rows_of(cfg) == 0) return MOE_OK;  // no rows: nothing to compute, empty buffers may be NULL
+  if (!x_perm || !expert_offset || !w1 || !w2 || !h || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) || !aligned16(y_perm))
+    return MOE_ERR_INVALID_ARG;
+  const int64_t rows = max_rows_of(cfg);
+  if (!gemm_fits(cfg, rows, cfg->d_ff)) return MOE_ERR_UNSUPPORTED;
+  moe::FfnArgs a{};
+  a.dtype = cfg->dtype;
+  a.act = cfg->act;
+  a.E = cfg->num_experts;
+  a.d = cfg->d_model;
+  a.d_ff = cfg->d_ff;
+  a.max_rows = rows;
+  a.x_perm = x_perm;
+  a.expert_offset = expert_offset;
+  a.w1 = w1;
+  a.w2 = w2;
+  a.h = h;
+  a.y_perm = y_perm;
+  return hip_status(moe::launch_expert_ffn(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status unpermute_impl(const moe_config *cfg, const void *y_perm, const int32_t *tok_ptr,
+                          const int32_t *slot_row, const float *slot_w, const void *y_shared, void *y,
+                          void *stream) {
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!y_perm || !slot_row || !slot_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(y) || (y_shared && !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
+  if (cfg->routing == MOE_EXPERT_CHOICE && !tok_ptr) return MOE_ERR_INVALID_ARG;
+  moe::CombineArgs a{};
+  a.dtype = cfg->dtype;
+  a.T = cfg->num_tokens;
+  a.d = cfg->d_model;
+  a.k = cfg->routing == MOE_EXPERT_CHOICE ? 0 : cfg->top_k;
+  a.y_perm = y_perm;
+  a.tok_ptr = cfg->routing == MOE_EXPERT_CHOICE ? tok_ptr : nullptr;
+  a.slot_row = slot_row;
+  a.slot_w = slot_w;
+  a.y_shared = y_shared;
+  a.y = y;
+  a.rows = max_rows_of(cfg);
+  a.nslots = cfg->routing == MOE_EXPERT_CHOICE ? static_cast<int64_t>(cfg->num_experts) * cfg->ec_capacity
+                                                : static_cast<int64_t>(cfg->num_tokens) * cfg->top_k;
+  return hip_status(moe::launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_config shared_config(const moe_config *cfg) {
+  moe_config s = *cfg;
+  s.num_experts = 1;
+  s.top_k = 1;
+  s.capacity_factor = 0.f;
+  s.routing = MOE_TOPK_SOFTMAX_ALL;
+  s.d_ff = cfg->d_ff_shared;
+  s.d_ff_shared = 0;
+  s.ec_capacity = 0;
+  return s;
+}
+
+void make_layout(const moe_config *c, moe_workspace_layout *L) {
+  const size_t T = static_cast<size_t>(c->num_tokens), E = static_cast<size_t>(c->num_experts);
+  const size_t d = static_cast<size_t>(c->d_model), s = elem_bytes(c);
+  const bool ec = c->routing == MOE_EXPERT_CHOICE;
+  const size_t k = ec ? 0 : static_cast<size_t>(c->top_k);
+  const size_t C = ec ? static_cast<size_t>(c->ec_capacity) : 0;
+  const size_t rows = static_cast<size_t>(max_rows_of(c));
+  const size_t nslots = ec ? E * C : T * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  memset(L, 0, sizeof(*L));
+  L->logits = take(T * E * 4);
+  L->topk_idx = take(T * k * 4);
+  L->topk_w = take(T * k * 4);
+  L->scores = take(ec ? T * E * 4 : 0);
+  L->ec_token = take(E * C * 4);
+  L->ec_w = take(E * C * 4);
+  L->x_perm = take(rows * d * s);
+  L->row_token = take(rows * 4);
+  L->slot_row = take(nslots * 4);
+  L->slot_w = take(ec ? nslots * 4 : 0);
+  L->tok_ptr = take(ec ? (T + 1) * 4 : 0);
+  L->expert_count = take(E * 4);
+  L->expert_load = take(E * 4);
+  L->expert_offset = take((E + 1) * 4);
+  L->shared_offset = take(c->d_ff_shared ? 2 * 4 : 0);
+  L->h = take(rows * static_cast<size_t>(c->d_ff) * s);
+  L->y_perm = take(rows * d * s);
+  L->shared_h = take(c->d_ff_shared ? T * static_cast<size_t>(c->d_ff_shared) * s : 0);
+  L->shared_y = take(c->d_ff_shared ? T * d * s : 0);
+  L->scratch_bytes = ec ? 0 : moe::permute_scratch_bytes(c->num_tokens, c->top_k, c->num_experts);
+  L->scratch = take(L->scratch_bytes);
+  L->total = off;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char *moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int64_t moe_max_rows(const moe_config *cfg) {
+  if (check_config(cfg) != MOE_OK) return -1;
+  return max_rows_of(cfg);
+}
+
+int64_t moe_capacity(const moe_config *cfg) {
+  if (check_config(cfg) != MOE_OK) return -1;
+  return capacity_of(cfg);
+}
+
+moe_status moe_route(const moe_config *cfg, const void *x, const void *w_router, const float *logit_bias,
+                     int64_t bias_row_stride, float *logits, int32_t *topk_idx, float *topk_w, float *scores,
+                     int32_t *ec_token, float *ec_w, void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  return route_impl(cfg, x, w_router, logit_bias, bias_row_stride, logits, topk_idx, topk_w, scores, ec_token,
+                    ec_w, stream);
+}
+
+moe_status moe_permute_scratch_bytes(const moe_config *cfg, size_t *bytes) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = cfg->routing == MOE_EXPERT_CHOICE
+               ? 0
+               : moe::permute_scratch_bytes(cfg->num_tokens, cfg->top_k, cfg->num_experts);
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk_idx, const int32_t *ec_token,
+                       const float *ec_w, void *x_perm, int32_t *row_token, int32_t *slot_row, float *slot_w,
+                       int32_t *tok_ptr, int32_t *expert_count, int32_t *expert_load, int32_t *expert_offset,
+                       void *scratch, size_t scratch_bytes, void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  return permute_impl(cfg, x, topk_idx, ec_token, ec_w, x_perm, row_token, slot_row, slot_w, tok_ptr,
+                      expert_count, expert_load, expert_offset, scratch, scratch_bytes, stream);
+}
+
+moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
+                          const void *w1, const void *w2, void *h, void *y_perm, void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  return ffn_impl(cfg, x_perm, expert_offset, w1, w2, h, y_perm, stream);
+}
+
+moe_status moe_unpermute(const moe_config *cfg, const void *y_perm, const int32_t *tok_ptr,
+                         const int32_t *slot_row, const float *slot_w, const void *y_shared, void *y,
+                         void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  return unpermute_impl(cfg, y_perm, tok_ptr, slot_row, slot_w, y_shared, y, stream);
+}
+
+moe_status moe_layer_workspace(const moe_config *cfg, moe_workspace_layout *layout) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  make_layout(cfg, layout);
+  return MOE_OK;
+}
+
+moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_router, const float *logit_bias,
+                         int64_t bias_row_stride, const void *w1, const void *w2, const void *ws1,
+                         const void *ws2, void *y, void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do, empty buffers may be NULL
+  if (!x || !w_router || !w1 || !w2 || !y || !workspace) return MOE_ERR_INVALID_ARG;
+  if (cfg->d_ff_shared > 0 && (!ws1 || !ws2)) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_ERR_INVALID_ARG;
+  if (bias_row_stride != 0 && bias_row_stride != cfg->num_experts) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w2) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->d_ff_shared > 0 && (!aligned16(ws1) || !aligned16(ws2))) return MOE_ERR_INVALID_ARG;
+  moe_workspace_layout L;
+  make_layout(cfg, &L);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const int64_t rows = max_rows_of(cfg);
+  if (!gemm_fits(cfg, rows, cfg->d_ff)) return MOE_ERR_UNSUPPORTED;
+  moe_config sc = shared_config(cfg);
+  if (cfg->d_ff_shared > 0 && !gemm_fits(&sc, cfg->num_tokens, cfg->d_ff_shared)) return MOE_ERR_UNSUPPORTED;
+
+  char *ws = static_cast<char *>(workspace);
+  auto P = [&](size_t off) { return static_cast<void *>(ws + off); };
+  const bool ec = cfg->routing == MOE_EXPERT_CHOICE;
+  float *logits = static_cast<float *>(P(L.logits));
+  int32_t *topk_idx = static_cast<int32_t *>(P(L.topk_idx));
+  float *topk_w = static_cast<float *>(P(L.topk_w));
+  float *scores = static_cast<float *>(P(L.scores));
+  int32_t *ec_token = static_cast<int32_t *>(P(L.ec_token));
+  float *ec_w = static_cast<float *>(P(L.ec_w));
+  int32_t *slot_row = static_cast<int32_t *>(P(L.slot_row));
+  float *slot_w = ec ? static_cast<float *>(P(L.slot_w)) : topk_w;
+  int32_t *tok_ptr = static_cast<int32_t *>(P(L.tok_ptr));
+  int32_t *expert_offset = static_cast<int32_t *>(P(L.expert_offset));
+
+  s = route_impl(cfg, x, w_router, logit_bias, bias_row_stride, logits, topk_idx, topk_w, scores, ec_token, ec_w,
+                 stream);
+  if (s != MOE_OK) return s;
+  s = permute_impl(cfg, x, topk_idx, ec_token, ec_w, P(L.x_perm), static_cast<int32_t *>(P(L.row_token)), slot_row,
+                   static_cast<float *>(P(L.slot_w)), tok_ptr, static_cast<int32_t *>(P(L.expert_count)),
+                   static_cast<int32_t *>(P(L.expert_load)), expert_offset, P(L.scratch), L.scratch_bytes, stream);
+  if (s != MOE_OK) return s;
+  s = ffn_impl(cfg, P(L.x_perm), expert_offset, w1, w2, P(L.h), P(L.y_perm), stream);
+  if (s != MOE_OK) return s;
+  const void *y_shared = nullptr;
+  if (cfg->d_ff_shared > 0) {
+    int32_t *so = static_cast<int32_t *>(P(L.shared_offset));
+    if (moe::launch_fill_offsets(so, cfg->num_tokens, static_cast<hipStream_t>(stream)) != hipSuccess)
+      return MOE_ERR_HIP;
+    s = ffn_impl(&sc, x, so, ws1, ws2, P(L.shared_h), P(L.shared_y), stream);
+    if (s != MOE_OK) return s;
+    y_shared = P(L.shared_y);
+  }
+  return unpermute_impl(cfg, P(L.y_perm), tok_ptr, slot_row, slot_w, y_shared, y, stream);
+}
+
+}  // extern "C"

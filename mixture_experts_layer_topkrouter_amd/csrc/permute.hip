@@ -1,0 +1,285 @@
+// token_permutation on one GPU: per-expert histogram, stable ranks, capacity
+// dropping, prefix-sum offsets and the row scatter into expert-major order.
+//
+// "How MegaDLMs Implements Mixture of Experts (MoE) Architectures", section
+// "Token Dispatching and Communication" (token_permutation moves tokens to
+// their experts) and "Expert Parallelism > Key Parameters", capacity_factor
+// paragraph (assignments beyond an expert's capacity are dropped and add
+// nothing to the output).
+//
+// gfx950 design (three launches, no floating point, no global atomics, so
+// the result is bit-reproducible):
+// 1. count: a block takes 1024 consecutive assignments (token-major order).
+//    Each wave labels 64 of them at a time: a lane finds the lanes holding the
+//    same expert with one ballot per bit of the expert id, so its rank inside
+//    the 64 is a popcount and the lowest such lane writes the group size to a
+//    private LDS slot.  A per-expert scan over the 16 groups gives block-local
+//    ranks and the block's histogram row.
+// 2. scan: one workgroup turns the [blocks x E] histogram into per-block
+//    bases (exclusive over blocks), the loads, the kept counts min(load, C)
+//    and the exclusive expert offsets.
+// 3. scatter: one wave per token computes its k rows (or -1 when the rank is
+//    at or above the capacity), loads the token row once with 16-B loads and
+//    stores it to each kept row.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGroups = kPermuteBlock / kWave;  // 16 groups of 64 per block
+
+__global__ __launch_bounds__(kThreads) void count_kernel(const int32_t *__restrict__ idx, int64_t A, int E,
+                                                         int ebits, int32_t *__restrict__ blk,
+                                                         int32_t *__restrict__ rank) {
+  __shared__ int grp[kGroups][kMaxExperts];
+  const int l = lane_id(), w = wave_id();
+  for (int i = threadIdx.x; i < kGroups * E; i += blockDim.x) grp[i / E][i % E] = 0;
+  __syncthreads();
+  constexpr int per_wave = kGroups / (kThreads / kWave);
+  int e_reg[per_wave], r_reg[per_wave];
+#pragma unroll
+  for (int i = 0; i < per_wave; ++i) {
+    const int g = w * per_wave + i;
+    const int64_t a = static_cast<int64_t>(blockIdx.x) * kPermuteBlock + g * kWave + l;
+    bool valid = a < A;
+    int e = valid ? idx[a] : E;  // E marks an empty lane
+    if (e < 0 || e > E) e = E;     // an id outside [0,E) is never counted
+    uint64_t peers = ~static_cast<uint64_t>(0);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int r = __popcll(peers & lanemask_lt());
+    valid = valid && e < E;
+    if (valid && r == 0) grp[g][e] = __popcll(peers);
+    e_reg[i] = e;
+    r_reg[i] = r;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int g = 0; g < kGroups; ++g) {
+      const int c = grp[g][e];
+      grp[g][e] = run;
+      run += c;
+    }
+    blk[static_cast<int64_t>(blockIdx.x) * E + e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < per_wave; ++i) {
+    const int g = w * per_wave + i;
+    const int64_t a = static_cast<int64_t>(blockIdx.x) * kPermuteBlock + g * kWave + l;
+    if (a < A && e_reg[i] < E) rank[a] = grp[g][e_reg[i]] + r_reg[i];
+  }
+}
+
+constexpr int kScanThreads = 256;
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t *__restrict__ blk, int nblk, int E,
+                                                            int64_t cap, int32_t *__restrict__ expert_count,
+                                                            int32_t *__restrict__ expert_load,
+                                                            int32_t *__restrict__ expert_offset) {
+  __shared__ int tmp[kScanThreads / kWave + 1];
+  const int e = threadIdx.x;  // E <= 256 = blockDim.x
+  int cnt = 0;
+  if (e < E) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk[static_cast<int64_t>(b) * E + e];
+      blk[static_cast<int64_t>(b) * E + e] = run;
+      run += c;
+    }
+    cnt = (cap >= 0 && run > cap) ? static_cast<int>(cap) : run;
+    expert_load[e] = run;
+    expert_count[e] = cnt;
+  }
+  int total;
+  const int off = block_excl_scan(cnt, tmp, &total);
+  if (e < E) expert_offset[e] = off;
+  if (e == 0) expert_offset[E] = total;
+}
+
+constexpr int kScatterTokens = kThreads / kWave;  // one wave per token
+
+__global__ __launch_bounds__(kThreads) void scatter_kernel(
+    const uint8_t *__restrict__ x, size_t row_bytes, const int32_t *__restrict__ idx, int T, int k, int E,
+    int64_t cap, const int32_t *__restrict__ blk, const int32_t *__restrict__ rank,
+    const int32_t *__restrict__ expert_offset, uint8_t *__restrict__ x_perm, int32_t *__restrict__ row_token,
+    int32_t *__restrict__ slot_row) {
+  const int t = blockIdx.x * kScatterTokens + wave_id();
+  if (t >= T) return;
+  const int l = lane_id();
+  int row = -1;
+  if (l < k) {
+    const int64_t a = static_cast<int64_t>(t) * k + l;
+    const int e = idx[a];
+    const int r = (e >= 0 && e < E) ? blk[(a / kPermuteBlock) * E + e] + rank[a] : -1;
+    if (r >= 0 && (cap < 0 || r < cap)) {
+      row = expert_offset[e] + r;
+      row_token[row] = t;
+    }
+    slot_row[a] = row;
+  }
+  const int nchunk = static_cast<int>(row_bytes / 16);
+  const uint8_t *src = x + static_cast<size_t>(t) * row_bytes;
+  for (int c0 = 0; c0 < nchunk; c0 += 4 * kWave) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * kWave + l;
+      if (c < nchunk) v[u] = ld16(src + static_cast<size_t>(c) * 16);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int rj = __shfl(row, j, kWave);
+      if (rj < 0) continue;
+      uint8_t *dst = x_perm + static_cast<size_t>(rj) * row_bytes;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * kWave + l;
+        if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- ExpertChoice
+
+// Row copy for ExpertChoice: row r = e*C + i holds token ec_token[r].
+__global__ __launch_bounds__(kThreads) void ec_rows_kernel(const uint8_t *__restrict__ x, size_t row_bytes,
+                                                           const int32_t *__restrict__ ec_token, int64_t rows,
+                                                           int E, int C, uint8_t *__restrict__ x_perm,
+                                                           int32_t *__restrict__ row_token,
+                                                           int32_t *__restrict__ expert_count,
+                                                           int32_t *__restrict__ expert_load,
+                                                           int32_t *__restrict__ expert_offset) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kScatterTokens + wave_id();
+  const int l = lane_id();
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+      if (e < E) {
+        expert_count[e] = C;
+        expert_load[e] = C;
+      }
+      expert_offset[e] = e * C;
+    }
+  }
+  if (r >= rows) return;
+  const int t = ec_token[r];
+  if (l == 0) row_token[r] = t;
+  const int nchunk = static_cast<int>(row_bytes / 16);
+  const uint8_t *src = x + static_cast<size_t>(t) * row_bytes;
+  uint8_t *dst = x_perm + static_cast<size_t>(r) * row_bytes;
+  for (int c = l; c < nchunk; c += kWave) st16(dst + static_cast<size_t>(c) * 16, ld16(src + static_cast<size_t>(c) * 16));
+}
+
+// Position of token t in expert e's ascending list, or -1.
+__device__ __forceinline__ int ec_find(const int32_t *__restrict__ list, int C, int t) {
+  int lo = 0, hi = C;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] < t) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < C && list[lo] == t) ? lo : -1;
+}
+
+// Per token: how many experts hold it (written to tok_ptr[t+1]).
+__global__ __launch_bounds__(kThreads) void ec_count_kernel(const int32_t *__restrict__ ec_token, int T, int E,
+                                                            int C, int32_t *__restrict__ tok_ptr) {
+  const int t = blockIdx.x * kScatterTokens + wave_id();
+  if (t >= T) return;
+  const int l = lane_id();
+  int n = 0;
+  for (int e = l; e < E; e += kWave) n += ec_find(ec_token + static_cast<int64_t>(e) * C, C, t) >= 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, kWave);
+  if (l == 0) tok_ptr[t + 1] = n;
+  if (t == 0 && l == 0) tok_ptr[0] = 0;
+}
+
+constexpr int kPtrThreads = 1024;
+
+// In-place inclusive scan of tok_ptr[1..T] (single workgroup).
+__global__ __launch_bounds__(kPtrThreads) void ec_ptr_scan_kernel(int32_t *__restrict__ tok_ptr, int T) {
+  __shared__ int tmp[kPtrThreads / kWave + 1];
+  const int per = (T + kPtrThreads - 1) / kPtrThreads;
+  const int b0 = min(T, static_cast<int>(threadIdx.x) * per), b1 = min(T, b0 + per);
+  int s = 0;
+  for (int i = b0; i < b1; ++i) s += tok_ptr[i + 1];
+  int tot;
+  int run = block_excl_scan(s, tmp, &tot);
+  for (int i = b0; i < b1; ++i) {
+    run += tok_ptr[i + 1];
+    tok_ptr[i + 1] = run;
+  }
+}
+
+// Per token: its rows and weights in ascending expert order.
+__global__ __launch_bounds__(kThreads) void ec_fill_kernel(const int32_t *__restrict__ ec_token,
+                                                           const float *__restrict__ ec_w, int T, int E, int C,
+                                                           const int32_t *__restrict__ tok_ptr,
+                                                           int32_t *__restrict__ slot_row,
+                                                           float *__restrict__ slot_w) {
+  const int t = blockIdx.x * kScatterTokens + wave_id();
+  if (t >= T) return;
+  const int l = lane_id();
+  int base = tok_ptr[t];
+  for (int e0 = 0; e0 < E; e0 += kWave) {
+    const int e = e0 + l;
+    const int pos = (e < E) ? ec_find(ec_token + static_cast<int64_t>(e) * C, C, t) : -1;
+    const uint64_t hit = __ballot(pos >= 0);
+    if (pos >= 0) {
+      const int s = base + __popcll(hit & lanemask_lt());
+      const int64_t r = static_cast<int64_t>(e) * C + pos;
+      slot_row[s] = static_cast<int32_t>(r);
+      slot_w[s] = ec_w[r];
+    }
+    base += __popcll(hit);
+  }
+}
+
+}  // namespace
+
+size_t permute_scratch_bytes(int T, int k, int E) {
+  const int64_t A = static_cast<int64_t>(T) * k;
+  const int64_t nblk = (A + kPermuteBlock - 1) / kPermuteBlock;
+  size_t b = static_cast<size_t>(nblk * E) * 4;
+  b = (b + 255) & ~static_cast<size_t>(255);
+  b += static_cast<size_t>(A) * 4;
+  return (b + 255) & ~static_cast<size_t>(255);
+}
+
+hipError_t launch_permute_topk(const PermuteArgs &a, hipStream_t st) {
+  const int64_t A = static_cast<int64_t>(a.T) * a.k;
+  const int nblk = static_cast<int>((A + kPermuteBlock - 1) / kPermuteBlock);
+  int ebits = 0;
+  while ((1 << ebits) <= a.E) ++ebits;  // ids 0..E (E marks an empty lane)
+  if (nblk > 0) count_kernel<<<nblk, kThreads, 0, st>>>(a.topk_idx, A, a.E, ebits, a.blk, a.rank);
+  scan_kernel<<<1, kScanThreads, 0, st>>>(a.blk, nblk, a.E, a.cap, a.expert_count, a.expert_load,
+                                          a.expert_offset);
+  if (a.T > 0)
+    scatter_kernel<<<(a.T + kScatterTokens - 1) / kScatterTokens, kThreads, 0, st>>>(
+        static_cast<const uint8_t *>(a.x), a.row_bytes, a.topk_idx, a.T, a.k, a.E, a.cap, a.blk, a.rank,
+        a.expert_offset, static_cast<uint8_t *>(a.x_perm), a.row_token, a.slot_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_ec(const PermuteEcArgs &a, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(a.E) * a.C;
+  const int rblocks = static_cast<int>((rows + kScatterTokens - 1) / kScatterTokens);
+  ec_rows_kernel<<<rblocks > 0 ? rblocks : 1, kThreads, 0, st>>>(
+      static_cast<const uint8_t *>(a.x), a.row_bytes, a.ec_token, rows, a.E, a.C,
+      static_cast<uint8_t *>(a.x_perm), a.row_token, a.expert_count, a.expert_load, a.expert_offset);
+  const int tblocks = (a.T + kScatterTokens - 1) / kScatterTokens;
+  ec_count_kernel<<<tblocks, kThreads, 0, st>>>(a.ec_token, a.T, a.E, a.C, a.tok_ptr);
+  ec_ptr_scan_kernel<<<1, kPtrThreads, 0, st>>>(a.tok_ptr, a.T);
+  ec_fill_kernel<<<tblocks, kThreads, 0, st>>>(a.ec_token, a.ec_w, a.T, a.E, a.C, a.tok_ptr, a.slot_row,
+                                              a.slot_w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

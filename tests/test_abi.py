@@ -1,0 +1,90 @@
+"""The C-ABI library: it loads, exports every function include/moe.h declares,
+and rejects invalid arguments on the host before anything reaches a GPU
+(these calls enqueue nothing, so they run without one)."""
+import ctypes
+
+import pytest
+
+from mixture_experts_layer_topkrouter_amd import moe
+from mixture_experts_layer_topkrouter_amd import workloads as W
+
+
+def test_library_exports_every_header_symbol():
+    lib = moe.load_library()
+    syms = moe.header_symbols()
+    assert len(syms) >= 11
+    for s in syms:
+        assert hasattr(lib, s), s
+    for s in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_unpermute", "moe_layer_fwd"):
+        assert s in syms
+
+
+def test_status_strings_and_version():
+    lib = moe.load_library()
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_string(0) == b"ok"
+    assert lib.moe_status_string(3) == b"workspace too small"
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_rows_capacity_and_workspace_sizes(name):
+    w = W.WORKLOADS[name]
+    cfg = moe.make_config(w)
+    cap = moe.capacity(cfg)
+    if w.routing == W.EXPERT_CHOICE:
+        assert cap == -1 and moe.max_rows(cfg) == w.E * w.ec_capacity
+    elif w.cf == 0:
+        assert cap == -1 and moe.max_rows(cfg) == w.T * w.k
+    else:
+        assert cap == {"tiny_top2_fp32": 80, "switch_top1_bf16": 128}[name]
+        assert moe.max_rows(cfg) == min(w.T * w.k, cap * w.E)
+    L = moe.layer_workspace(cfg)
+    assert L["total"] >= L["y_perm"] + moe.max_rows(cfg) * w.d * w.elem_bytes
+    offs = [L[n] for n in ("logits", "x_perm", "h", "y_perm", "total")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+
+
+def _cfg(**kw):
+    base = dict(num_tokens=64, d_model=64, num_experts=8, top_k=2, d_ff=64, d_ff_shared=0, capacity_factor=0.0,
+                ec_capacity=0, dtype=1, act=1, routing=0)
+    base.update(kw)
+    return moe.MoeConfig(**base)
+
+
+@pytest.mark.parametrize("bad", [dict(top_k=0), dict(top_k=9), dict(num_tokens=-1), dict(d_model=60),
+                                 dict(d_ff=100), dict(capacity_factor=-1.0), dict(capacity_factor=float("nan")),
+                                 dict(routing=7), dict(dtype=5), dict(act=3), dict(num_experts=0),
+                                 dict(routing=2, ec_capacity=0), dict(routing=2, ec_capacity=65)])
+def test_invalid_configs_are_rejected_before_launch(bad):
+    lib = moe.load_library()
+    cfg = _cfg(**bad)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_permute_scratch_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 1
+    L = moe.WorkspaceLayout()
+    assert lib.moe_layer_workspace(ctypes.byref(cfg), ctypes.byref(L)) == 1
+    # compute entry points refuse too, without touching (fake) pointers
+    fake = ctypes.c_void_p(16)
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), fake, fake, None, 0, fake, fake, None, None, fake, ctypes.c_void_p(256),
+                           1 << 30, None)
+    assert st == 1
+
+
+def test_unsupported_and_workspace_errors():
+    lib = moe.load_library()
+    assert lib.moe_max_rows(ctypes.byref(_cfg(num_experts=300, top_k=2))) == -1
+    L = moe.WorkspaceLayout()
+    assert lib.moe_layer_workspace(ctypes.byref(_cfg(num_experts=300)), ctypes.byref(L)) == 2
+    assert lib.moe_layer_workspace(ctypes.byref(_cfg(routing=2, ec_capacity=4, num_tokens=20000)),
+                                   ctypes.byref(L)) == 2
+    cfg = _cfg()
+    fake = ctypes.c_void_p(256)
+    # workspace too small -> MOE_ERR_WORKSPACE, nothing enqueued
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), fake, fake, None, 0, fake, fake, None, None, fake, fake, 16, None)
+    assert st == 3
+    # misaligned pointer -> invalid argument
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), ctypes.c_void_p(8), fake, None, 0, fake, fake, None, None, fake, fake,
+                           1 << 30, None)
+    assert st == 1
+    # null output -> invalid argument
+    st = lib.moe_unpermute(ctypes.byref(cfg), fake, None, fake, fake, None, None, None)
+    assert st == 1
