@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-sample", type=int, default=48, help="tokens the oracle computes for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -164,6 +166,14 @@ def main():
     torch.cuda.synchronize()
     same = bool(torch.equal(y_steps.view(torch.int16) if y_steps.dtype == torch.bfloat16 else y_steps,
                             layer.y.view(torch.int16) if layer.y.dtype == torch.bfloat16 else layer.y))
+
+    if args.copy_probe_mib:
+        a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     n_rows = int(off[-1].item())
     counts = cnt.cpu().numpy()

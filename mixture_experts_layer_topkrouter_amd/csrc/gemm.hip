@@ -31,6 +31,10 @@
 #include "common.h"
 #include "kernels.h"
 
+// the direct-to-LDS loads name M0, which the compiler reserves (it uses M0
+// nowhere else in these kernels)
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace moe {
 namespace {
 
@@ -57,60 +61,75 @@ struct GemmParams {
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = nblocks >> 3, rem = nblocks & 7;
-  return xcd * per + min(xcd, rem) + slot;
+// Block -> tile for the grouped GEMMs, done by every wave on its own (no LDS).
+// The grid is an upper bound on the tile count; the real count follows from
+// the device-side expert offsets.  Only block ids below the real count get a
+// tile, and those ids are spread over the 8 XCDs (ids are dispatched to XCDs
+// round-robin) before being remapped so that each XCD walks a contiguous run
+// of tiles, in groups of kGroupM row tiles.  Returns false for surplus blocks.
+// Rows of expert e, clamped to the buffer so a bad offset cannot address
+// outside it.
+__device__ __forceinline__ void expert_rows(const int32_t *__restrict__ offs, int e, int64_t max_rows, int *o0,
+                                            int *me) {
+  const int64_t a0 = min(max(static_cast<int64_t>(offs[e]), static_cast<int64_t>(0)), max_rows);
+  const int64_t a1 = min(max(static_cast<int64_t>(offs[e + 1]), a0), max_rows);
+  *o0 = static_cast<int>(a0);
+  *me = static_cast<int>(a1 - a0);
 }
 
-// Global m-tile index -> (expert, first row, valid rows).  Wave 0 scans the
-// per-expert tile counts; the result is broadcast through LDS.
 template <int BM>
-__device__ __forceinline__ void find_tile(const int32_t *__restrict__ offs, int E, int64_t max_rows, int mt,
-                                          int *info) {
-  if (wave_id() == 0) {
-    const int l = lane_id();
-    int carry = 0;
-    bool found = false;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-      const int e = e0 + l;
-      int o0 = 0, me = 0;
-      if (e < E) {  // offsets are clamped to the buffer, so a bad offset cannot address outside it
-        const int64_t a0 = min(max(static_cast<int64_t>(offs[e]), static_cast<int64_t>(0)), max_rows);
-        const int64_t a1 = min(max(static_cast<int64_t>(offs[e + 1]), a0), max_rows);
-        o0 = static_cast<int>(a0);
-        me = static_cast<int>(a1 - a0);
-      }
-      const int tiles = (me + BM - 1) / BM;
-      const int incl = wave_incl_scan(tiles) + carry;
-      const int excl = incl - tiles;
-      const uint64_t hit = __ballot(e < E && mt >= excl && mt < incl);
-      if (hit) {
-        if (l == __ffsll(static_cast<unsigned long long>(hit)) - 1) {
-          const int lt = mt - excl;
-          info[0] = e;
-          info[1] = o0 + lt * BM;
-          info[2] = min(BM, me - lt * BM);
-        }
-        found = true;
-        break;
-      }
-      carry = __shfl(incl, kWave - 1, kWave);
-    }
-    if (!found && l == 0) info[0] = -1;
+__device__ __forceinline__ bool map_tile(const int32_t *__restrict__ offs, int E, int64_t max_rows, int n_tiles,
+                                         int *e_out, int *row0_out, int *rows_out, int *nt_out) {
+  const int l = lane_id();
+  // pass 1: real row tiles over all experts
+  int m_tiles = 0;
+  for (int e0 = 0; e0 < E; e0 += kWave) {
+    int o0 = 0, me = 0;
+    if (e0 + l < E) expert_rows(offs, e0 + l, max_rows, &o0, &me);
+    int t = (me + BM - 1) / BM;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
+    m_tiles += t;
   }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void tile_coords(const GemmParams &p, int *mt, int *nt) {
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = kGroupM * p.n_tiles;
-  const int group = bid / per_group;
+  const int total = m_tiles * n_tiles;
+  const int bid = blockIdx.x;
+  if (bid >= total) return false;
+  // XCD-contiguous remap of [0, total)
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int q = xcd * per + min(xcd, rem) + slot;
+  // grouped order: kGroupM row tiles share each column tile
+  const int per_group = kGroupM * n_tiles;
+  const int group = q / per_group;
   const int first_m = group * kGroupM;
-  const int gsz = min(p.m_tiles - first_m, kGroupM);
-  const int in_g = bid - group * per_group;
-  *mt = first_m + in_g % gsz;
-  *nt = in_g / gsz;
+  const int gsz = min(m_tiles - first_m, kGroupM);
+  const int in_g = q - group * per_group;
+  const int mt = first_m + in_g % gsz;
+  *nt_out = in_g / gsz;
+  // pass 2: the expert holding row tile mt
+  int carry = 0, fe = -1, frow = 0, frows = 0;
+  for (int e0 = 0; e0 < E; e0 += kWave) {
+    const int e = e0 + l;
+    int o0 = 0, me = 0;
+    if (e < E) expert_rows(offs, e, max_rows, &o0, &me);
+    const int tiles = (me + BM - 1) / BM;
+    const int incl = wave_incl_scan(tiles) + carry;
+    const int excl = incl - tiles;
+    const uint64_t hit = __ballot(e < E && mt >= excl && mt < incl);
+    if (hit) {
+      const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      const int lt = mt - excl;
+      fe = __shfl(e, src, kWave);
+      frow = __shfl(o0 + lt * BM, src, kWave);
+      frows = __shfl(min(BM, me - lt * BM), src, kWave);
+      break;
+    }
+    carry = __shfl(incl, kWave - 1, kWave);
+  }
+  *e_out = __builtin_amdgcn_readfirstlane(fe);
+  *row0_out = __builtin_amdgcn_readfirstlane(frow);
+  *rows_out = __builtin_amdgcn_readfirstlane(frows);
+  return fe >= 0;
 }
 
 template <int BM, int ACT>
@@ -122,14 +141,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
   constexpr int B_CH = BN * 8 / kThreads;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
-  __shared__ int info[3];
 
-  int mt, nt;
-  tile_coords(p, &mt, &nt);
-  find_tile<BM>(p.offs, p.E, p.max_rows, mt, info);
-  const int e = info[0];
-  if (e < 0) return;
-  const int row0 = info[1], rows = info[2];
+  int e, row0, rows, nt;
+  if (!map_tile<BM>(p.offs, p.E, p.max_rows, p.n_tiles, &e, &row0, &rows, &nt)) return;
 
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
   const int wm = w >> 1, wn = w & 1;
@@ -247,6 +261,295 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Main bf16 kernel (K a multiple of 32): 256 x 256 tile, 32-wide K stages in a
+// 5-deep LDS ring (5 x 32 KB = the whole 160 KB LDS) filled by
+// global_load_lds_dwordx4 (gfx950 direct-to-LDS loads: no VGPR staging, each
+// wave instruction writes 1 KB of LDS).  Stage kt+4 is requested right after
+// the barrier that opens stage kt, so each load has four stages of MFMA work
+// (about 1.7 us at full rate) to land.  The ring slots are distinct LDS arrays
+// and the K loop is unrolled by five, so every slot index is static.
+// LDS rows are 64 B (four 16-B chunks); chunk c of row r is stored at
+// c ^ ((r >> 1) & 3), which spreads the 16 rows of a fragment read over all
+// banks.
+constexpr int DK = 32;   // K per stage
+constexpr int NST = 5;   // stages in the LDS ring
+constexpr int DBM = 256; // tile rows
+constexpr int DSTAGE = DBM * DK;  // elements per operand per stage
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds_addr + 16 * lane.  Written as inline asm so the compiler's wait-count
+// pass does not see it: that pass cannot always tell which ring slot an LDS
+// read touches and would then drain every load in flight before the read.
+// The kernel orders these loads itself (explicit vmcnt waits + barriers).
+// The instruction has no register result; M0 carries the LDS address and
+// needs one wait state after it is written.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
+  // the LDS address is wave-uniform; readfirstlane puts it in an SGPR for M0
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v)
+               : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)p));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int S>
+struct Slot {
+  static constexpr int value = S;
+};
+
+// An empty asm "use" at the end of an iteration keeps that iteration's
+// fragment set live until then, so the register allocator cannot hand its
+// registers to the next stage's LDS reads while queued MFMAs still have to
+// read them (the hardware would hold the LDS read until they did).
+template <int SET, int MI, int NJ>
+__device__ __forceinline__ void keep_live(bf16x8 (&fa)[2][2][MI], bf16x8 (&fb)[2][2][NJ]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) asm volatile("" ::"v"(fa[SET][ks][i]));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) asm volatile("" ::"v"(fb[SET][ks][j]));
+  }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
+  // v_mfma_f32_32x32x16_bf16: one wave per SIMD keeps the matrix core full with
+  // it (the 16x16x32 form does not).  Each wave owns 128 x 128 = 4 x 4 tiles of
+  // 32 x 32; per 16-wide K step it reads 4 A and 4 B fragments (16 B per lane:
+  // row l%32, K chunk l/32) and issues 16 MFMAs.
+  constexpr int MI = 4, NJ = 4;
+  // one array per ring slot: A stage at [0, DSTAGE), B stage at [DSTAGE, 2*DSTAGE)
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * DSTAGE], s1[2 * DSTAGE], s2[2 * DSTAGE],
+      s3[2 * DSTAGE], s4[2 * DSTAGE];
+
+  int e, row0, rows, nt;
+  if (!map_tile<DBM>(p.offs, p.E, p.max_rows, p.n_tiles, &e, &row0, &rows, &nt)) return;
+  const int l = lane_id(), w = wave_id();
+  const int wm = w >> 1, wn = w & 1;
+  const uint16_t *A = static_cast<const uint16_t *>(p.A);
+  const uint16_t *B = static_cast<const uint16_t *>(p.B) + static_cast<int64_t>(e) * p.b_stride;
+
+  auto slot = [&](auto S) -> uint16_t * {
+    constexpr int s = decltype(S)::value;
+    if constexpr (s == 0) return s0;
+    else if constexpr (s == 1) return s1;
+    else if constexpr (s == 2) return s2;
+    else if constexpr (s == 3) return s3;
+    else return s4;
+  };
+
+  // DMA sources: wave w, instruction i fills LDS chunks [(4i+w)*64, +64), i.e.
+  // rows (4i+w)*16 .. +16; lane l -> row r = q/4, stored chunk q%4, which holds
+  // logical chunk (q%4) ^ ((r>>1)&3).
+  const uint16_t *a_src[4];
+  const uint16_t *b_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (4 * i + w) * 64 + l;
+    const int r = q >> 2;
+    const int c = (q & 3) ^ ((r >> 1) & 3);
+    a_src[i] = A + (row0 + min(r, rows - 1)) * p.lda + c * 8;
+    int br;
+    if (ACT == ACT_SWIGLU) {
+      const int col = nt * (BN / 2) + (r & (BN / 2 - 1));
+      br = (col < p.n_out ? col : 0) + (r >= BN / 2 ? p.up_off : 0);
+    } else {
+      const int col = nt * BN + r;
+      br = col < p.n_out ? col : 0;
+    }
+    b_src[i] = B + static_cast<int64_t>(br) * p.ldb + c * 8;
+  }
+  auto issue = [&](auto S, int k0) {
+    const uint32_t base = lds_addr_of(slot(S));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dma16(a_src[i] + k0, base + (4 * i + w) * 64 * 16);
+      dma16(b_src[i] + k0, base + DSTAGE * 2 + (4 * i + w) * 64 * 16);
+    }
+  };
+
+  // fragment offsets inside a stage (elements), for the two 16-wide K steps
+  const int frow = l & 31;
+  const int fsw = (frow >> 1) & 3;
+  const int fch0 = ((l >> 5) ^ fsw) * 8;        // K step 0: chunks 0,1
+  const int fch1 = (((l >> 5) + 2) ^ fsw) * 8;  // K step 1: chunks 2,3
+  const int a_row = (wm * 128 + frow) * DK;     // + i*32*DK
+  int b_row[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    int br;
+    if (ACT == ACT_SWIGLU) br = (j < NJ / 2) ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - NJ / 2) * 32;
+    else br = wn * 128 + j * 32;
+    b_row[j] = DSTAGE + (br + frow) * DK;
+  }
+
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // Fragments are double-buffered in registers: the reads of stage kt+1 go to
+  // the set the MFMAs of stage kt do not use, and they are issued half-way
+  // through stage kt's MFMAs (after the barrier that publishes stage kt+1), so
+  // the matrix core never waits for an LDS read or for a register a queued
+  // MFMA has yet to consume.
+  bf16x8 fa[2][2][MI], fb[2][2][NJ];  // [set][16-wide K step][tile]
+  auto read_frags = [&](auto SET, auto S) {
+    constexpr int set = decltype(SET)::value;
+    const uint16_t *ls = slot(S);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = ks ? fch1 : fch0;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        fa[set][ks][i] = *reinterpret_cast<const bf16x8 *>(ls + a_row + i * 32 * DK + ch);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) fb[set][ks][j] = *reinterpret_cast<const bf16x8 *>(ls + b_row[j] + ch);
+    }
+  };
+  auto mma = [&](auto SET, int ks) {
+    constexpr int set = decltype(SET)::value;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ks][i], fb[set][ks][j], acc[i][j], 0, 0, 0);
+  };
+  // wait until stage `st` has landed given the stages issued so far, then a
+  // plain barrier (this wave's LDS reads have returned; no fence, which would
+  // also wait for the DMA still in flight)
+  auto wait_stage = [&](int st, int issued_last) {
+    const int ahead = issued_last - st;
+    if (ahead >= 4) wait_vm<32>();
+    else if (ahead == 3) wait_vm<24>();
+    else if (ahead == 2) wait_vm<16>();
+    else if (ahead == 1) wait_vm<8>();
+    else wait_vm<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  const int nk = p.K / DK;
+  // prologue: stages 0..4 in flight, stage 0's fragments in set 0
+  if (0 < nk) issue(Slot<0>{}, 0);
+  if (1 < nk) issue(Slot<1>{}, DK);
+  if (2 < nk) issue(Slot<2>{}, 2 * DK);
+  if (3 < nk) issue(Slot<3>{}, 3 * DK);
+  if (4 < nk) issue(Slot<4>{}, 4 * DK);
+  wait_stage(0, min(nk - 1, 4));
+  read_frags(Slot<0>{}, Slot<0>{});
+
+  // iteration kt: stage kt sits in slot kt%5 and fragment set kt%2.
+  // After the barrier that publishes stage kt+1, each of stage kt's 32 MFMAs
+  // is followed by one of the 16 fragment reads of stage kt+1 (into the other
+  // register set) or one of the 8 DMA instructions that refill stage kt's slot
+  // with stage kt+5; sched_barrier pins this order, so the LDS reads and the
+  // loads issue in the shadow of the matrix core instead of between MFMAs.
+  auto iter = [&](auto S, auto SET, int kt) {
+    constexpr int s = decltype(S)::value;
+    constexpr int set = decltype(SET)::value;
+    const bool more = kt + 1 < nk;
+    const bool refill = kt + 5 < nk;
+    if (more) wait_stage(kt + 1, min(nk - 1, kt + 4));
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t *ls = slot(Slot<(s + 1) % NST>{});
+    const uint32_t dbase = lds_addr_of(slot(S));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ks][i], fb[set][ks][j], acc[i][j], 0, 0, 0);
+          const int t = ks * 16 + i * 4 + j;
+          if (t < 16) {
+            if (more) {  // read t: K step t/8, A tiles 0-3 then B tiles 0-3
+              const int rks = t >> 3, r = t & 7;
+              const int ch = rks ? fch1 : fch0;
+              if (r < MI) fa[set ^ 1][rks][r] = *reinterpret_cast<const bf16x8 *>(ls + a_row + r * 32 * DK + ch);
+              else fb[set ^ 1][rks][r - MI] = *reinterpret_cast<const bf16x8 *>(ls + b_row[r - MI] + ch);
+            }
+          } else if (t < 24) {
+            if (refill) {
+              const int d = t - 16, ii = d >> 1;
+              if ((d & 1) == 0) dma16(a_src[ii] + (kt + 5) * DK, dbase + (4 * ii + w) * 64 * 16);
+              else dma16(b_src[ii] + (kt + 5) * DK, dbase + DSTAGE * 2 + (4 * ii + w) * 64 * 16);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    keep_live<set>(fa, fb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kt = 0;
+  for (; kt + 9 < nk; kt += 10) {
+    iter(Slot<0>{}, Slot<0>{}, kt);
+    iter(Slot<1>{}, Slot<1>{}, kt + 1);
+    iter(Slot<2>{}, Slot<0>{}, kt + 2);
+    iter(Slot<3>{}, Slot<1>{}, kt + 3);
+    iter(Slot<4>{}, Slot<0>{}, kt + 4);
+    iter(Slot<0>{}, Slot<1>{}, kt + 5);
+    iter(Slot<1>{}, Slot<0>{}, kt + 6);
+    iter(Slot<2>{}, Slot<1>{}, kt + 7);
+    iter(Slot<3>{}, Slot<0>{}, kt + 8);
+    iter(Slot<4>{}, Slot<1>{}, kt + 9);
+  }
+  if (kt < nk) iter(Slot<0>{}, Slot<0>{}, kt);
+  if (kt + 1 < nk) iter(Slot<1>{}, Slot<1>{}, kt + 1);
+  if (kt + 2 < nk) iter(Slot<2>{}, Slot<0>{}, kt + 2);
+  if (kt + 3 < nk) iter(Slot<3>{}, Slot<1>{}, kt + 3);
+  if (kt + 4 < nk) iter(Slot<4>{}, Slot<0>{}, kt + 4);
+  if (kt + 5 < nk) iter(Slot<0>{}, Slot<1>{}, kt + 5);
+  if (kt + 6 < nk) iter(Slot<1>{}, Slot<0>{}, kt + 6);
+  if (kt + 7 < nk) iter(Slot<2>{}, Slot<1>{}, kt + 7);
+  if (kt + 8 < nk) iter(Slot<3>{}, Slot<0>{}, kt + 8);
+
+  // 32x32 accumulator layout: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
+  // column l%32 of its tile.
+  uint16_t *C = static_cast<uint16_t *>(p.C);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int lr = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+      if (lr >= rows) continue;
+      uint16_t *crow = C + static_cast<int64_t>(row0 + lr) * p.ldc;
+      if (ACT == ACT_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < NJ / 2; ++j) {
+          const int col = nt * (BN / 2) + wn * 64 + j * 32 + (l & 31);
+          if (col < p.n_out) crow[col] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + NJ / 2][v]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int col = nt * BN + wn * 128 + j * 32 + (l & 31);
+          if (col < p.n_out) {
+            const float x = acc[i][j][v];
+            crow[col] = f32_to_bf16(ACT == ACT_GELU ? gelu_erf(x) : x);
+          }
+        }
+      }
+    }
+  }
+}
+
 // fp32 path: plain FMA tiles (64 rows x 64 B rows x 16), 4x4 per thread.
 constexpr int F_BM = 64, F_BN = 64, F_BK = 16;
 
@@ -254,13 +557,8 @@ template <int ACT>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
   __shared__ float sA[F_BK][F_BM + 4];
   __shared__ float sB[F_BK][F_BN + 4];
-  __shared__ int info[3];
-  int mt, nt;
-  tile_coords(p, &mt, &nt);
-  find_tile<F_BM>(p.offs, p.E, p.max_rows, mt, info);
-  const int e = info[0];
-  if (e < 0) return;
-  const int row0 = info[1], rows = info[2];
+  int e, row0, rows, nt;
+  if (!map_tile<F_BM>(p.offs, p.E, p.max_rows, p.n_tiles, &e, &row0, &rows, &nt)) return;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const float *A = static_cast<const float *>(p.A);
   const float *B = static_cast<const float *>(p.B) + static_cast<int64_t>(e) * p.b_stride;
@@ -354,8 +652,21 @@ hipError_t run_f32(GemmParams p, int act, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t run_bf16_dma(GemmParams p, int act, hipStream_t st) {
+  p.m_tiles = static_cast<int>(mtile_bound(p.max_rows, p.E, DBM));
+  const int bn_out = act == ACT_SWIGLU ? BN / 2 : BN;
+  p.n_tiles = (p.n_out + bn_out - 1) / bn_out;
+  const int64_t blocks = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
+  if (blocks <= 0) return hipSuccess;
+  if (act == ACT_SWIGLU) gemm_bf16_dma_kernel<ACT_SWIGLU><<<blocks, kThreads, 0, st>>>(p);
+  else if (act == ACT_GELU) gemm_bf16_dma_kernel<ACT_GELU><<<blocks, kThreads, 0, st>>>(p);
+  else gemm_bf16_dma_kernel<ACT_NONE><<<blocks, kThreads, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 hipError_t run_gemm(int dtype, int bm, const GemmParams &p, int act, hipStream_t st) {
   if (dtype == 0) return run_f32(p, act, st);
+  if (bm == 256 && p.K % DK == 0) return run_bf16_dma(p, act, st);
   return bm == 256 ? run_bf16<256>(p, act, st) : run_bf16<128>(p, act, st);
 }
 
