@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-sample", type=int, default=48, help="tokens the oracle computes for cpu_baseline")
+    ap.add_argument("--cpu-sample", type=int, default=768, help="tokens the oracle computes for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (calibrates HBM byte counters)")
@@ -66,6 +66,23 @@ def algorithmic(w, n_rows: int, n_active: int):
         out["shared_ffn"] = ("flops", T * 2 * n_mat * d * w.d_ff_shared)
     out["unpermute"] = ("bytes", n_rows * d * s + T * d * s + (T * d * s if w.d_ff_shared else 0) + A * 8)
     return out
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per expert-FFN launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (scaled by a plain-copy calibration), or None when no such
+    measurement exists or the GEMM source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_ffn_traffic.json")
+    src = os.path.join(ROOT, "mixture_experts_layer_topkrouter_amd", "csrc", "gemm.hip")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("gemm_source_sha256"):
+            return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def main():
@@ -203,8 +220,8 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == W.BF16 else PEAK_F32_TFLOPS
     achieved = ffn_flops / ffn_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
-                "kernel": "grouped expert FFN: gemm_bf16_kernel GEMM1 (SwiGLU) + GEMM2, one moe_expert_ffn call",
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
+                "kernel": "grouped expert FFN: gemm_bf16_dma_kernel GEMM1 (SwiGLU) + GEMM2, one moe_expert_ffn call",
                 "avg_ms": round(stage_ms["expert_ffn"], 4), "flops_per_launch": int(ffn_flops)}
 
     cpu = None

@@ -19,8 +19,9 @@
 //   so each lane's MFMA fragment is one 16-byte LDS read.
 // * operands are staged global -> registers -> LDS, double-buffered: the
 //   next K slice is in flight while the current one feeds the MFMAs.  LDS
-//   rows are 128 B; the 16-B chunk c of row r is stored at chunk c ^ (r & 7),
-//   so the 16 rows a fragment read touches hit distinct banks.
+//   rows are 128 B; the 16-B chunk c of row r is stored at chunk
+//   c ^ ((r >> 1) & 7), so the 16 rows one 16-lane group of a fragment read
+//   touches hit distinct 16-B slots of the 64 banks.
 // * SwiGLU: the B tile holds 128 gate rows and the 128 matching up rows, and
 //   every wave computes the same output columns for both, so the epilogue
 //   silu(gate) * up is lane-local.  GELU is applied in the epilogue as well:
@@ -193,12 +194,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int r = rbase + 32 * i;
-      *reinterpret_cast<u32x4 *>(&sA[buf][r * BK + ((cc ^ (r & 7)) * 8)]) = ra[i];
+      *reinterpret_cast<u32x4 *>(&sA[buf][r * BK + ((cc ^ ((r >> 1) & 7)) * 8)]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const int r = rbase + 32 * i;
-      *reinterpret_cast<u32x4 *>(&sB[buf][r * BK + ((cc ^ (r & 7)) * 8)]) = rb[i];
+      *reinterpret_cast<u32x4 *>(&sB[buf][r * BK + ((cc ^ ((r >> 1) & 7)) * 8)]) = rb[i];
     }
   };
 
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
     if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int chunk = ((ks * 4 + (l >> 4)) ^ (l & 7)) * 8;
+      const int chunk = ((ks * 4 + (l >> 4)) ^ ((l >> 1) & 7)) * 8;
       bf16x8 a[MI], b[NJ];
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -270,8 +271,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
 // (about 1.7 us at full rate) to land.  The ring slots are distinct LDS arrays
 // and the K loop is unrolled by five, so every slot index is static.
 // LDS rows are 64 B (four 16-B chunks); chunk c of row r is stored at
-// c ^ ((r >> 1) & 3), which spreads the 16 rows of a fragment read over all
-// banks.
+// c ^ ((r >> 2) & 3).  gfx950 serves a 16-byte-per-lane LDS read 16 lanes at a
+// time over 64 banks (256 B); the 16 rows one such group reads then land on 16
+// distinct 16-B bank slots, so fragment reads are conflict-free.
 constexpr int DK = 32;   // K per stage
 constexpr int NST = 5;   // stages in the LDS ring
 constexpr int DBM = 256; // tile rows
@@ -352,14 +354,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
 
   // DMA sources: wave w, instruction i fills LDS chunks [(4i+w)*64, +64), i.e.
   // rows (4i+w)*16 .. +16; lane l -> row r = q/4, stored chunk q%4, which holds
-  // logical chunk (q%4) ^ ((r>>1)&3).
+  // logical chunk (q%4) ^ ((r>>2)&3).
   const uint16_t *a_src[4];
   const uint16_t *b_src[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = (4 * i + w) * 64 + l;
     const int r = q >> 2;
-    const int c = (q & 3) ^ ((r >> 1) & 3);
+    const int c = (q & 3) ^ ((r >> 2) & 3);
     a_src[i] = A + (row0 + min(r, rows - 1)) * p.lda + c * 8;
     int br;
     if (ACT == ACT_SWIGLU) {
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
 
   // fragment offsets inside a stage (elements), for the two 16-wide K steps
   const int frow = l & 31;
-  const int fsw = (frow >> 1) & 3;
+  const int fsw = (frow >> 2) & 3;
   const int fch0 = ((l >> 5) ^ fsw) * 8;        // K step 0: chunks 0,1
   const int fch1 = (((l >> 5) + 2) ^ fsw) * 8;  // K step 1: chunks 2,3
   const int a_row = (wm * 128 + frow) * DK;     // + i*32*DK
@@ -454,11 +456,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   read_frags(Slot<0>{}, Slot<0>{});
 
   // iteration kt: stage kt sits in slot kt%5 and fragment set kt%2.
-  // After the barrier that publishes stage kt+1, each of stage kt's 32 MFMAs
-  // is followed by one of the 16 fragment reads of stage kt+1 (into the other
-  // register set) or one of the 8 DMA instructions that refill stage kt's slot
-  // with stage kt+5; sched_barrier pins this order, so the LDS reads and the
-  // loads issue in the shadow of the matrix core instead of between MFMAs.
+  // After the barrier that publishes stage kt+1, stage kt's 32 MFMAs are
+  // interleaved with the 16 fragment reads of stage kt+1 (into the other
+  // register set) and the 8 DMA instructions that refill stage kt's slot with
+  // stage kt+5; sched_barrier pins this order, so the LDS reads and the loads
+  // issue in the shadow of the matrix core.
   auto iter = [&](auto S, auto SET, int kt) {
     constexpr int s = decltype(S)::value;
     constexpr int set = decltype(SET)::value;
@@ -475,18 +477,21 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ks][i], fb[set][ks][j], acc[i][j], 0, 0, 0);
+          // every 4 MFMAs: two fragment reads (t%4 == 0, 2) and one load
+          // (t%4 == 1), spread out so the per-CU load path drains between
+          // load issues instead of stalling the wave that issues them
           const int t = ks * 16 + i * 4 + j;
-          if (t < 16) {
-            if (more) {  // read t: K step t/8, A tiles 0-3 then B tiles 0-3
-              const int rks = t >> 3, r = t & 7;
+          if ((t & 1) == 0) {
+            if (more) {  // read t/2: K step (t/2)/8, A tiles 0-3 then B tiles 0-3
+              const int rd = t >> 1, rks = rd >> 3, r = rd & 7;
               const int ch = rks ? fch1 : fch0;
               if (r < MI) fa[set ^ 1][rks][r] = *reinterpret_cast<const bf16x8 *>(ls + a_row + r * 32 * DK + ch);
               else fb[set ^ 1][rks][r - MI] = *reinterpret_cast<const bf16x8 *>(ls + b_row[r - MI] + ch);
             }
-          } else if (t < 24) {
+          } else if ((t & 3) == 1) {
             if (refill) {
-              const int d = t - 16, ii = d >> 1;
-              if ((d & 1) == 0) dma16(a_src[ii] + (kt + 5) * DK, dbase + (4 * ii + w) * 64 * 16);
+              const int dd = t >> 2, ii = dd >> 1;
+              if ((dd & 1) == 0) dma16(a_src[ii] + (kt + 5) * DK, dbase + (4 * ii + w) * 64 * 16);
               else dma16(b_src[ii] + (kt + 5) * DK, dbase + DSTAGE * 2 + (4 * ii + w) * 64 * 16);
             }
           }
@@ -520,33 +525,55 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   if (kt + 7 < nk) iter(Slot<2>{}, Slot<1>{}, kt + 7);
   if (kt + 8 < nk) iter(Slot<3>{}, Slot<0>{}, kt + 8);
 
-  // 32x32 accumulator layout: value v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
-  // column l%32 of its tile.
-  uint16_t *C = static_cast<uint16_t *>(p.C);
+  // Epilogue through LDS.  The 32x32 accumulator layout puts value v of lane l
+  // at row 8*(v/4) + 4*(l/32) + v%4, column l%32 of its tile, so a lane holds a
+  // column slice; each wave writes its activated bf16 sub-tile into LDS (row
+  // pitch padded by 16 B so the two half-waves, four rows apart, hit different
+  // banks), then the block stores whole rows with 16-byte coalesced writes.
+  constexpr int OUT_COLS = (ACT == ACT_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
+  constexpr int PITCH = OUT_COLS * 2 + 16;                      // bytes per LDS row
+  static_assert(DBM * PITCH <= NST * 2 * DSTAGE * 2, "epilogue tile must fit in the ring");
+  // The five slot arrays fill the 160 KB exactly, so they are contiguous; the
+  // epilogue tile starts at whichever of them has the lowest LDS address.
+  uint16_t *lo = s0;
+  if (lds_addr_of(s1) < lds_addr_of(lo)) lo = s1;
+  if (lds_addr_of(s2) < lds_addr_of(lo)) lo = s2;
+  if (lds_addr_of(s3) < lds_addr_of(lo)) lo = s3;
+  if (lds_addr_of(s4) < lds_addr_of(lo)) lo = s4;
+  uint8_t *ep = reinterpret_cast<uint8_t *>(lo);
+  __syncthreads();  // every wave is done with the ring
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int lr = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-      if (lr >= rows) continue;
-      uint16_t *crow = C + static_cast<int64_t>(row0 + lr) * p.ldc;
       if (ACT == ACT_SWIGLU) {
 #pragma unroll
         for (int j = 0; j < NJ / 2; ++j) {
-          const int col = nt * (BN / 2) + wn * 64 + j * 32 + (l & 31);
-          if (col < p.n_out) crow[col] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + NJ / 2][v]);
+          const int lc = wn * 64 + j * 32 + (l & 31);
+          *reinterpret_cast<uint16_t *>(ep + lr * PITCH + lc * 2) =
+              f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + NJ / 2][v]);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int col = nt * BN + wn * 128 + j * 32 + (l & 31);
-          if (col < p.n_out) {
-            const float x = acc[i][j][v];
-            crow[col] = f32_to_bf16(ACT == ACT_GELU ? gelu_erf(x) : x);
-          }
+          const int lc = wn * 128 + j * 32 + (l & 31);
+          const float x = acc[i][j][v];
+          *reinterpret_cast<uint16_t *>(ep + lr * PITCH + lc * 2) = f32_to_bf16(ACT == ACT_GELU ? gelu_erf(x) : x);
         }
       }
     }
+  }
+  __syncthreads();
+  constexpr int CHUNKS = OUT_COLS / 8;  // 16-byte chunks per row
+  const int tid = threadIdx.x;
+  const int col0 = nt * OUT_COLS;
+  uint8_t *C = static_cast<uint8_t *>(p.C);
+  for (int q = tid; q < DBM * CHUNKS; q += kThreads) {
+    const int r = q / CHUNKS, c = q - (q / CHUNKS) * CHUNKS;
+    if (r >= rows || col0 + c * 8 >= p.n_out) continue;
+    const u32x4 val = *reinterpret_cast<const u32x4 *>(ep + r * PITCH + c * 16);
+    st16(C + (static_cast<int64_t>(row0 + r) * p.ldc + col0 + c * 8) * 2, val);
   }
 }
 
