@@ -115,6 +115,7 @@ def main():
     h, y_perm = V("h"), V("y_perm")
     L = layer.layout
     scratch = layer.workspace[L["scratch"]:L["scratch"] + max(L["scratch_bytes"], 1)]
+    ffn_ws = layer.workspace[L["ffn_scratch"]:L["ffn_scratch"] + L["ffn_scratch_bytes"]] if L["ffn_scratch_bytes"] else None
     if ec:
         scores, ec_token, ec_w = V("scores"), V("ec_token"), V("ec_w")
         slot_w, tok_ptr = V("slot_w"), V("tok_ptr")
@@ -144,13 +145,13 @@ def main():
             moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off, topk_idx=topk_idx, scratch=scratch)
         if ev is not None:
             ev[2].record(stream)
-        moe.expert_ffn(cfg, x_perm, off, dev.w1, dev.w2, h, y_perm)
+        moe.expert_ffn(cfg, x_perm, off, dev.w1, dev.w2, h, y_perm, ffn_ws)
         i = 3
         if ev is not None:
             ev[i].record(stream)
         y_sh = None
         if w.d_ff_shared:
-            moe.expert_ffn(scfg, dev.x, soff, dev.ws1, dev.ws2, hs, ys)
+            moe.expert_ffn(scfg, dev.x, soff, dev.ws1, dev.ws2, hs, ys, ffn_ws)
             y_sh = ys
             i += 1
             if ev is not None:

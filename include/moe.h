@@ -144,6 +144,14 @@ moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk
                        int32_t *expert_count, int32_t *expert_load, int32_t *expert_offset,
                        void *scratch, size_t scratch_bytes, void *stream);
 
+/* Bytes of device workspace moe_expert_ffn needs for this configuration.
+ * A bf16 GEMM with at least 384 rows per expert on average and a reduction
+ * length (d_model for the up projection, d_ff for the down projection) of at
+ * least 8192 cuts the tiles of its last, partial round of workgroups along K
+ * and keeps their fp32 partial tiles here: at most 256 tiles of 256 KiB
+ * (64 MiB).  0 for every other configuration. */
+moe_status moe_expert_ffn_workspace_bytes(const moe_config *cfg, size_t *bytes);
+
 /* --------------------------------------------------------------------------
  * moe_expert_ffn -- [P1] "Core MoE Layer Architecture" (MoELayer step 2: the
  * local experts process their dispatched tokens).  For every expert e, rows
@@ -155,12 +163,18 @@ moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk
  *   x_perm [rows,d], w1 [E, n_up*d_ff, d] (n_up = 2 for SwiGLU), w2 [E, d, d_ff],
  *   expert_offset [E+1] int32 (device), h [rows,d_ff] (workspace the caller
  *   owns), y_perm [rows,d].  rows = moe_max_rows(cfg).
+ *   workspace: moe_expert_ffn_workspace_bytes() bytes of device memory,
+ *   256-B aligned (NULL when that is 0); MOE_ERR_WORKSPACE when too small.
+ *   Its contents need no initialisation and are scratch afterwards; two
+ *   calls in flight at once need two workspaces.
+ * Results are deterministic: a K-split tile adds its pieces in K order.
  * The shared expert ([P3] "Key Parameters", top_k paragraph: a shared expert
  * every token uses) is this call with num_experts = 1, top_k = 1, dropless,
  * d_ff = d_ff_shared, expert_offset = {0, T} and x_perm = x.
  * ------------------------------------------------------------------------ */
 moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
-                          const void *w1, const void *w2, void *h, void *y_perm, void *stream);
+                          const void *w1, const void *w2, void *h, void *y_perm, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
  * moe_unpermute -- [P1] "Token Dispatching and Communication"
@@ -186,6 +200,7 @@ typedef struct {
   size_t x_perm, row_token, slot_row, slot_w, tok_ptr;
   size_t expert_count, expert_load, expert_offset, shared_offset;
   size_t h, y_perm, shared_h, shared_y, scratch, scratch_bytes;
+  size_t ffn_scratch, ffn_scratch_bytes; /* moe_expert_ffn workspace */
   size_t total; /* bytes the workspace must hold */
 } moe_workspace_layout;
 

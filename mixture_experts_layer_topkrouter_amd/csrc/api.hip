@@ -156,14 +156,22 @@ moe_status permute_impl(const moe_config *cfg, const void *x, const int32_t *top
   return hip_status(moe::launch_permute_topk(a, st));
 }
 
+size_t ffn_scratch_of(const moe_config *c) {
+  return moe::ffn_scratch_bytes(c->dtype, c->num_experts, c->d_model, c->d_ff, max_rows_of(c));
+}
+
 moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset, const void *w1,
-                    const void *w2, void *h, void *y_perm, void *stream) {
+                    const void *w2, void *h, void *y_perm, void *workspace, size_t workspace_bytes,
+                    void *stream) {
   if (max_rows_of(cfg) == 0) return MOE_OK;  // no rows: nothing to compute, empty buffers may be NULL
   if (!x_perm || !expert_offset || !w1 || !w2 || !h || !y_perm) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) || !aligned16(y_perm))
     return MOE_ERR_INVALID_ARG;
   const int64_t rows = max_rows_of(cfg);
   if (!gemm_fits(cfg, rows, cfg->d_ff)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = ffn_scratch_of(cfg);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_ERR_INVALID_ARG;
   moe::FfnArgs a{};
   a.dtype = cfg->dtype;
   a.act = cfg->act;
@@ -177,6 +185,8 @@ moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *ex
   a.w2 = w2;
   a.h = h;
   a.y_perm = y_perm;
+  a.scratch = workspace;
+  a.scratch_bytes = workspace_bytes;
   return hip_status(moe::launch_expert_ffn(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -252,6 +262,16 @@ void make_layout(const moe_config *c, moe_workspace_layout *L) {
   L->shared_y = take(c->d_ff_shared ? T * d * s : 0);
   L->scratch_bytes = ec ? 0 : moe::permute_scratch_bytes(c->num_tokens, c->top_k, c->num_experts);
   L->scratch = take(L->scratch_bytes);
+  // the routed and the shared expert FFN run one after the other on the
+  // stream, so they share one scratch region
+  size_t ffn = ffn_scratch_of(c);
+  if (c->d_ff_shared) {
+    const moe_config sc = shared_config(c);
+    const size_t sh = ffn_scratch_of(&sc);
+    if (sh > ffn) ffn = sh;
+  }
+  L->ffn_scratch_bytes = ffn;
+  L->ffn_scratch = take(ffn);
   L->total = off;
 }
 
@@ -259,7 +279,7 @@ void make_layout(const moe_config *c, moe_workspace_layout *L) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 const char *moe_status_string(moe_status s) {
   switch (s) {
@@ -311,11 +331,20 @@ moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk
                       expert_count, expert_load, expert_offset, scratch, scratch_bytes, stream);
 }
 
-moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
-                          const void *w1, const void *w2, void *h, void *y_perm, void *stream) {
+moe_status moe_expert_ffn_workspace_bytes(const moe_config *cfg, size_t *bytes) {
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
-  return ffn_impl(cfg, x_perm, expert_offset, w1, w2, h, y_perm, stream);
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = ffn_scratch_of(cfg);
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
+                          const void *w1, const void *w2, void *h, void *y_perm, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  return ffn_impl(cfg, x_perm, expert_offset, w1, w2, h, y_perm, workspace, workspace_bytes, stream);
 }
 
 moe_status moe_unpermute(const moe_config *cfg, const void *y_perm, const int32_t *tok_ptr,
@@ -376,14 +405,16 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
                    static_cast<float *>(P(L.slot_w)), tok_ptr, static_cast<int32_t *>(P(L.expert_count)),
                    static_cast<int32_t *>(P(L.expert_load)), expert_offset, P(L.scratch), L.scratch_bytes, stream);
   if (s != MOE_OK) return s;
-  s = ffn_impl(cfg, P(L.x_perm), expert_offset, w1, w2, P(L.h), P(L.y_perm), stream);
+  s = ffn_impl(cfg, P(L.x_perm), expert_offset, w1, w2, P(L.h), P(L.y_perm), P(L.ffn_scratch),
+               L.ffn_scratch_bytes, stream);
   if (s != MOE_OK) return s;
   const void *y_shared = nullptr;
   if (cfg->d_ff_shared > 0) {
     int32_t *so = static_cast<int32_t *>(P(L.shared_offset));
     if (moe::launch_fill_offsets(so, cfg->num_tokens, static_cast<hipStream_t>(stream)) != hipSuccess)
       return MOE_ERR_HIP;
-    s = ffn_impl(&sc, x, so, ws1, ws2, P(L.shared_h), P(L.shared_y), stream);
+    s = ffn_impl(&sc, x, so, ws1, ws2, P(L.shared_h), P(L.shared_y), P(L.ffn_scratch), L.ffn_scratch_bytes,
+                 stream);
     if (s != MOE_OK) return s;
     y_shared = P(L.shared_y);
   }

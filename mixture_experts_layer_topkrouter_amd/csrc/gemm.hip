@@ -9,26 +9,35 @@
 //
 // gfx950 design (bf16):
 // * one launch per GEMM covers every expert: the grid is an upper bound on
-//   the number of (expert, 256- or 128-row) tiles times the column tiles, and
-//   each workgroup finds its expert from the device-side expert offsets (a
-//   64-lane prefix sum over per-expert tile counts), so the host never reads
-//   how many rows each expert received.  Surplus workgroups exit at once.
-// * tile BM x 256 x 64 with 4 waves in a 2 x 2 grid; each wave owns a
-//   BM/2 x 128 sub-tile of v_mfma_f32_16x16x32_bf16 results (fp32 accumulators).
-//   Both operands are K-contiguous ([rows, K] activations, [out, in] weights),
-//   so each lane's MFMA fragment is one 16-byte LDS read.
-// * operands are staged global -> registers -> LDS, double-buffered: the
-//   next K slice is in flight while the current one feeds the MFMAs.  LDS
-//   rows are 128 B; the 16-B chunk c of row r is stored at chunk
-//   c ^ ((r >> 1) & 7), so the 16 rows one 16-lane group of a fragment read
-//   touches hit distinct 16-B slots of the 64 banks.
+//   the number of (expert, row tile, column tile) tiles, and each workgroup
+//   finds its tile from the device-side expert offsets (a 64-lane prefix sum
+//   over per-expert tile counts), so the host never reads how many rows each
+//   expert received.  Surplus workgroups exit at once.
+// * tiles are ordered expert by expert, and inside an expert its row tiles
+//   form groups of at most 8 that walk the column tiles together; workgroup
+//   ids are remapped so each of the 8 XCDs takes a contiguous run of that
+//   order.  Tiles running together on one XCD then share weight tiles or
+//   rows in its L2, and no group mixes two experts' weights.
+// * main kernel (gemm_bf16_dma_kernel, K a multiple of 32, >= 384 rows per
+//   expert on average): 256 x 256 tiles, 4 waves of 128 x 128
+//   v_mfma_f32_32x32x16_bf16 results, operands loaded straight into a 5-deep
+//   LDS ring by direct-to-LDS loads (its own comment has the details).  The
+//   tiles left over after the last whole round of one workgroup per CU are
+//   cut along K when K >= 8192; split_reduce_kernel adds the pieces.
+// * small-expert kernel (gemm_bf16_kernel, BM = 128 or 256): tile BM x 256
+//   x 64 with 4 waves in a 2 x 2 grid of v_mfma_f32_16x16x32_bf16 results,
+//   operands staged global -> registers -> LDS, double-buffered; LDS rows are
+//   128 B with the 16-B chunk c of row r stored at chunk c ^ ((r >> 1) & 7),
+//   so a 16-lane fragment read hits distinct 16-B slots of the 64 banks.
+// * both operands are K-contiguous ([rows, K] activations, [out, in]
+//   weights), so each lane's MFMA fragment is one 16-byte LDS read.
 // * SwiGLU: the B tile holds 128 gate rows and the 128 matching up rows, and
 //   every wave computes the same output columns for both, so the epilogue
 //   silu(gate) * up is lane-local.  GELU is applied in the epilogue as well:
 //   the hidden activation is written once, in bf16.
-// * workgroup ids are remapped so the 8 XCDs each take a contiguous range of
-//   tiles, walked in groups of 4 row tiles, so tiles that share weights or
-//   rows run together on one XCD and hit its L2.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -42,7 +51,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int BK = 64;
 constexpr int BN = 256;  // B rows per tile
-constexpr int kGroupM = 4;
+constexpr int kGroupM = 8;  // most row tiles per group (see find_tile)
 
 enum { ACT_NONE = 0, ACT_GELU = 1, ACT_SWIGLU = 2 };
 
@@ -57,17 +66,20 @@ struct GemmParams {
   int E, K, n_out, up_off;
   int64_t max_rows;
   int m_tiles, n_tiles;
+  // bf16 256 x 256 kernel: `units` workgroups make one round (one per CU);
+  // K-split of the last, partial round needs max_split > 1 and room for the
+  // fp32 256 x 256 partial tiles of every piece (`slots` of them at part).
+  float *part;
+  int units, slots, max_split;
 };
 
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
-// Block -> tile for the grouped GEMMs, done by every wave on its own (no LDS).
-// The grid is an upper bound on the tile count; the real count follows from
-// the device-side expert offsets.  Only block ids below the real count get a
-// tile, and those ids are spread over the 8 XCDs (ids are dispatched to XCDs
-// round-robin) before being remapped so that each XCD walks a contiguous run
-// of tiles, in groups of kGroupM row tiles.  Returns false for surplus blocks.
+// Block -> tile for the grouped GEMMs is done by every wave on its own (no
+// LDS): the grid is an upper bound on the tile count and the real count
+// follows from the device-side expert offsets.
+//
 // Rows of expert e, clamped to the buffer so a bad offset cannot address
 // outside it.
 __device__ __forceinline__ void expert_rows(const int32_t *__restrict__ offs, int e, int64_t max_rows, int *o0,
@@ -78,11 +90,10 @@ __device__ __forceinline__ void expert_rows(const int32_t *__restrict__ offs, in
   *me = static_cast<int>(a1 - a0);
 }
 
+// Real row tiles over all experts (every lane gets the same count).
 template <int BM>
-__device__ __forceinline__ bool map_tile(const int32_t *__restrict__ offs, int E, int64_t max_rows, int n_tiles,
-                                         int *e_out, int *row0_out, int *rows_out, int *nt_out) {
+__device__ __forceinline__ int count_mtiles(const int32_t *__restrict__ offs, int E, int64_t max_rows) {
   const int l = lane_id();
-  // pass 1: real row tiles over all experts
   int m_tiles = 0;
   for (int e0 = 0; e0 < E; e0 += kWave) {
     int o0 = 0, me = 0;
@@ -92,23 +103,30 @@ __device__ __forceinline__ bool map_tile(const int32_t *__restrict__ offs, int E
     for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
     m_tiles += t;
   }
-  const int total = m_tiles * n_tiles;
-  const int bid = blockIdx.x;
-  if (bid >= total) return false;
-  // XCD-contiguous remap of [0, total)
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = total >> 3, rem = total & 7;
-  const int q = xcd * per + min(xcd, rem) + slot;
-  // grouped order: kGroupM row tiles share each column tile
-  const int per_group = kGroupM * n_tiles;
-  const int group = q / per_group;
-  const int first_m = group * kGroupM;
-  const int gsz = min(m_tiles - first_m, kGroupM);
-  const int in_g = q - group * per_group;
-  const int mt = first_m + in_g % gsz;
-  *nt_out = in_g / gsz;
-  // pass 2: the expert holding row tile mt
-  int carry = 0, fe = -1, frow = 0, frows = 0;
+  // the same in every lane; readfirstlane lets the compiler treat everything
+  // derived from it (and the branches on it) as wave-uniform
+  return __builtin_amdgcn_readfirstlane(m_tiles);
+}
+
+// Block ids are dispatched to the 8 XCDs round-robin; this remaps id b of
+// [0, n) so that each XCD walks a contiguous run of tile indices.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return xcd * per + min(xcd, rem) + slot;
+}
+
+// Tile index q -> (expert, rows, column tile).  Tiles are ordered expert by
+// expert; inside an expert its row tiles form groups of at most kGroupM (as
+// even as possible) and a group walks all column tiles with its row tiles
+// innermost, so neighbouring tiles share either their weight tile (same
+// expert, same column tile) or their rows.  Groups never straddle two
+// experts, whose weights differ.
+template <int BM>
+__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offs, int E, int64_t max_rows, int n_tiles,
+                                          int q, int *e_out, int *row0_out, int *rows_out, int *nt_out) {
+  const int l = lane_id();
+  int carry = 0, fe = -1, fo0 = 0, fme = 0, fexcl = 0, ftiles = 0;
   for (int e0 = 0; e0 < E; e0 += kWave) {
     const int e = e0 + l;
     int o0 = 0, me = 0;
@@ -116,21 +134,58 @@ __device__ __forceinline__ bool map_tile(const int32_t *__restrict__ offs, int E
     const int tiles = (me + BM - 1) / BM;
     const int incl = wave_incl_scan(tiles) + carry;
     const int excl = incl - tiles;
-    const uint64_t hit = __ballot(e < E && mt >= excl && mt < incl);
+    const uint64_t hit = __ballot(e < E && q >= excl * n_tiles && q < incl * n_tiles);
     if (hit) {
       const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-      const int lt = mt - excl;
       fe = __shfl(e, src, kWave);
-      frow = __shfl(o0 + lt * BM, src, kWave);
-      frows = __shfl(min(BM, me - lt * BM), src, kWave);
+      fo0 = __shfl(o0, src, kWave);
+      fme = __shfl(me, src, kWave);
+      fexcl = __shfl(excl, src, kWave);
+      ftiles = __shfl(tiles, src, kWave);
       break;
     }
     carry = __shfl(incl, kWave - 1, kWave);
   }
-  *e_out = __builtin_amdgcn_readfirstlane(fe);
-  *row0_out = __builtin_amdgcn_readfirstlane(frow);
-  *rows_out = __builtin_amdgcn_readfirstlane(frows);
-  return fe >= 0;
+  fe = __builtin_amdgcn_readfirstlane(fe);
+  if (fe < 0) return false;
+  fo0 = __builtin_amdgcn_readfirstlane(fo0);
+  fme = __builtin_amdgcn_readfirstlane(fme);
+  fexcl = __builtin_amdgcn_readfirstlane(fexcl);
+  ftiles = __builtin_amdgcn_readfirstlane(ftiles);
+  // ng groups: the first `big` hold base+1 row tiles, the others base
+  const int ql = q - fexcl * n_tiles;
+  const int ng = (ftiles + kGroupM - 1) / kGroupM;
+  const int base = ftiles / ng, big = ftiles - base * ng;
+  const int span_big = big * (base + 1) * n_tiles;
+  int m0, gsz, in_g;
+  if (ql < span_big) {
+    const int g = ql / ((base + 1) * n_tiles);
+    gsz = base + 1;
+    m0 = g * gsz;
+    in_g = ql - g * gsz * n_tiles;
+  } else {
+    const int g = (ql - span_big) / (base * n_tiles);
+    gsz = base;
+    m0 = big * (base + 1) + g * base;
+    in_g = ql - span_big - g * base * n_tiles;
+  }
+  const int lmt = m0 + in_g % gsz;
+  *nt_out = in_g / gsz;
+  *e_out = fe;
+  *row0_out = fo0 + lmt * BM;
+  *rows_out = min(BM, fme - lmt * BM);
+  return true;
+}
+
+// Block -> tile: one block per real tile, ids past the real count exit.
+template <int BM>
+__device__ __forceinline__ bool map_tile(const int32_t *__restrict__ offs, int E, int64_t max_rows, int n_tiles,
+                                         int *e_out, int *row0_out, int *rows_out, int *nt_out) {
+  const int m_tiles = count_mtiles<BM>(offs, E, max_rows);
+  const int total = m_tiles * n_tiles;
+  const int bid = blockIdx.x;
+  if (bid >= total) return false;
+  return find_tile<BM>(offs, E, max_rows, n_tiles, xcd_remap(bid, total), e_out, row0_out, rows_out, nt_out);
 }
 
 template <int BM, int ACT>
@@ -279,6 +334,79 @@ constexpr int NST = 5;   // stages in the LDS ring
 constexpr int DBM = 256; // tile rows
 constexpr int DSTAGE = DBM * DK;  // elements per operand per stage
 
+// K-split of the last round: only GEMMs with at least kSplitMinStages K
+// stages split (measured on gfx950: with K = 14336 the split saves a sixth of
+// the down projection, with K = 4096 it saves nothing: a short tail tile
+// costs less than the pieces' prologues and the extra reduction pass); a
+// piece keeps at least kPieceMinStages stages, and a tile splits into at
+// most kMaxSplit pieces.
+constexpr int kSplitMinStages = 256;
+constexpr int kPieceMinStages = 32;
+constexpr int kMaxSplit = 16;
+
+// One workgroup's share of a 256 x 256 grouped GEMM.  The tiles that fill
+// whole rounds of `units` workgroups run one per workgroup (XCD-remapped as in
+// map_tile).  The remaining tiles, fewer than one round, would leave most of
+// the chip idle during the last round; when the GEMM may split (max_split >
+// 1), each of them is cut along K into
+// nseg = min(units / remaining, stages / kPieceMinStages, max_split) pieces,
+// so the last round takes about 1/nseg of a tile's time.  A piece stores its fp32 partial tile;
+// split_reduce_kernel then adds the pieces in K order (so the result does not
+// depend on which piece finished first) and applies the epilogue.
+struct Split {
+  int m_tiles, total, full, rest, nseg;
+};
+
+__device__ __forceinline__ Split split_plan(const GemmParams &p, int nk) {
+  Split sp;
+  sp.m_tiles = count_mtiles<DBM>(p.offs, p.E, p.max_rows);
+  sp.total = sp.m_tiles * p.n_tiles;
+  sp.full = sp.total / p.units * p.units;
+  sp.rest = sp.total - sp.full;
+  sp.nseg = 1;
+  if (sp.rest > 0)
+    sp.nseg = max(1, min(min(min(p.units, p.slots) / sp.rest, nk / kPieceMinStages), p.max_split));
+  return sp;
+}
+
+struct Job {
+  int e, row0, rows, nt;
+  int kb, ke;           // K stages [kb, ke) of this piece
+  int tail, seg, nseg;  // split tile index (-1 if whole), piece, pieces
+};
+
+__device__ __forceinline__ bool map_job(const GemmParams &p, int nk, Job *j) {
+  const Split sp = split_plan(p, nk);
+  const int bid = blockIdx.x;
+  int q;
+  j->kb = 0;
+  j->ke = nk;
+  j->tail = -1;
+  j->seg = 0;
+  j->nseg = 1;
+  if (bid < sp.full) {
+    q = xcd_remap(bid, sp.full);
+  } else {
+    const int n = sp.rest * sp.nseg;
+    if (bid - sp.full >= n) return false;
+    // pieces walk piece-major (all tiles' first K piece, then the second,
+    // ...) in XCD-contiguous runs, so the pieces one XCD runs together read
+    // the same K slice of neighbouring tiles and share it in its L2
+    const int u = xcd_remap(bid - sp.full, n);
+    const int seg = u / sp.rest, t = u - seg * sp.rest;
+    q = sp.full + t;
+    if (sp.nseg > 1) {
+      // wave-uniform: keep them in scalar registers across the K loop
+      j->kb = __builtin_amdgcn_readfirstlane(seg * nk / sp.nseg);
+      j->ke = __builtin_amdgcn_readfirstlane((seg + 1) * nk / sp.nseg);
+      j->tail = __builtin_amdgcn_readfirstlane(t);
+      j->seg = __builtin_amdgcn_readfirstlane(seg);
+      j->nseg = __builtin_amdgcn_readfirstlane(sp.nseg);
+    }
+  }
+  return find_tile<DBM>(p.offs, p.E, p.max_rows, p.n_tiles, q, &j->e, &j->row0, &j->rows, &j->nt);
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // 16 bytes per lane from global memory straight into LDS at
@@ -287,11 +415,13 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // read touches and would then drain every load in flight before the read.
 // The kernel orders these loads itself (explicit vmcnt waits + barriers).
 // The instruction has no register result; M0 carries the LDS address and
-// needs one wait state after it is written.
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
+// needs one wait state after it is written.  The global address is a
+// wave-uniform base in SGPRs plus a 32-bit per-lane byte offset, so advancing
+// a stage is scalar arithmetic and each lane keeps one VGPR per load stream.
+__device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t lds_addr) {
   // the LDS address is wave-uniform; readfirstlane puts it in an SGPR for M0
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0v)
                : "memory", "m0");
 }
 
@@ -336,12 +466,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * DSTAGE], s1[2 * DSTAGE], s2[2 * DSTAGE],
       s3[2 * DSTAGE], s4[2 * DSTAGE];
 
-  int e, row0, rows, nt;
-  if (!map_tile<DBM>(p.offs, p.E, p.max_rows, p.n_tiles, &e, &row0, &rows, &nt)) return;
-  const int l = lane_id(), w = wave_id();
+  Job job;
+  if (!map_job(p, p.K / DK, &job)) return;
+  const int e = job.e, row0 = job.row0, rows = job.rows, nt = job.nt;
+  const int l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const int wm = w >> 1, wn = w & 1;
-  const uint16_t *A = static_cast<const uint16_t *>(p.A);
-  const uint16_t *B = static_cast<const uint16_t *>(p.B) + static_cast<int64_t>(e) * p.b_stride;
+  // wave-uniform bases of this piece's K range: A at the tile's first row, B
+  // at the expert's weights
+  const char *A = static_cast<const char *>(p.A) + (static_cast<int64_t>(row0) * p.lda + job.kb * DK) * 2;
+  const char *B = static_cast<const char *>(p.B) + (static_cast<int64_t>(e) * p.b_stride + job.kb * DK) * 2;
 
   auto slot = [&](auto S) -> uint16_t * {
     constexpr int s = decltype(S)::value;
@@ -354,15 +487,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
 
   // DMA sources: wave w, instruction i fills LDS chunks [(4i+w)*64, +64), i.e.
   // rows (4i+w)*16 .. +16; lane l -> row r = q/4, stored chunk q%4, which holds
-  // logical chunk (q%4) ^ ((r>>2)&3).
-  const uint16_t *a_src[4];
-  const uint16_t *b_src[4];
+  // logical chunk (q%4) ^ ((r>>2)&3).  Per-lane byte offsets from A / B (they
+  // fit 32 bits: the host limits every operand to 2^31 elements).
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = (4 * i + w) * 64 + l;
     const int r = q >> 2;
     const int c = (q & 3) ^ ((r >> 2) & 3);
-    a_src[i] = A + (row0 + min(r, rows - 1)) * p.lda + c * 8;
+    a_off[i] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
     int br;
     if (ACT == ACT_SWIGLU) {
       const int col = nt * (BN / 2) + (r & (BN / 2 - 1));
@@ -371,14 +504,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
       const int col = nt * BN + r;
       br = col < p.n_out ? col : 0;
     }
-    b_src[i] = B + static_cast<int64_t>(br) * p.ldb + c * 8;
+    b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(br) * p.ldb + c * 8) * 2);
   }
-  auto issue = [&](auto S, int k0) {
+  // stage st of this piece: K elements [st*DK, st*DK + DK) past A / B
+  auto issue = [&](auto S, int st) {
     const uint32_t base = lds_addr_of(slot(S));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dma16(a_src[i] + k0, base + (4 * i + w) * 64 * 16);
-      dma16(b_src[i] + k0, base + DSTAGE * 2 + (4 * i + w) * 64 * 16);
+      dma16(a_off[i], A + st * DK * 2, base + (4 * i + w) * 64 * 16);
+      dma16(b_off[i], B + st * DK * 2, base + DSTAGE * 2 + (4 * i + w) * 64 * 16);
     }
   };
 
@@ -445,13 +579,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  const int nk = p.K / DK;
+  const int nk = job.ke - job.kb;  // stages of this piece (A / B start at its first)
   // prologue: stages 0..4 in flight, stage 0's fragments in set 0
   if (0 < nk) issue(Slot<0>{}, 0);
-  if (1 < nk) issue(Slot<1>{}, DK);
-  if (2 < nk) issue(Slot<2>{}, 2 * DK);
-  if (3 < nk) issue(Slot<3>{}, 3 * DK);
-  if (4 < nk) issue(Slot<4>{}, 4 * DK);
+  if (1 < nk) issue(Slot<1>{}, 1);
+  if (2 < nk) issue(Slot<2>{}, 2);
+  if (3 < nk) issue(Slot<3>{}, 3);
+  if (4 < nk) issue(Slot<4>{}, 4);
   wait_stage(0, min(nk - 1, 4));
   read_frags(Slot<0>{}, Slot<0>{});
 
@@ -491,8 +625,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
           } else if ((t & 3) == 1) {
             if (refill) {
               const int dd = t >> 2, ii = dd >> 1;
-              if ((dd & 1) == 0) dma16(a_src[ii] + (kt + 5) * DK, dbase + (4 * ii + w) * 64 * 16);
-              else dma16(b_src[ii] + (kt + 5) * DK, dbase + DSTAGE * 2 + (4 * ii + w) * 64 * 16);
+              if ((dd & 1) == 0) dma16(a_off[ii], A + (kt + 5) * DK * 2, dbase + (4 * ii + w) * 64 * 16);
+              else dma16(b_off[ii], B + (kt + 5) * DK * 2, dbase + DSTAGE * 2 + (4 * ii + w) * 64 * 16);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -525,6 +659,50 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   if (kt + 7 < nk) iter(Slot<2>{}, Slot<1>{}, kt + 7);
   if (kt + 8 < nk) iter(Slot<3>{}, Slot<0>{}, kt + 8);
 
+  if (job.nseg > 1) {
+    // K-split piece: store the fp32 partial in accumulator order (lane l of
+    // wave w, tile (i, j), values 4*v4..4*v4+3 at float4 index
+    // ((w*MI + i)*NJ + j)*4*64 + v4*64 + l), so every store is a coalesced
+    // 1 KB wave store; split_reduce_kernel finishes the tile.  The stores
+    // take the accumulators straight from the AGPRs (inline asm with an
+    // SGPR base and immediate offsets): through VGPRs, this path and the
+    // epilogue together overflow the register file.  The compiler cannot see
+    // inside the asm, so each block first waits out the MFMA / AGPR-write
+    // read hazard itself (21 wait states).
+    constexpr int kTileF = DBM * BN;
+    const char *mine = reinterpret_cast<const char *>(p.part) +
+                       (static_cast<int64_t>(job.tail * job.nseg + job.seg) * kTileF + w * (MI * NJ * 4 * kWave * 4)) * 4;
+    const uint32_t voff = l * 16;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const char *sb = mine + (i * NJ + j) * 4 * kWave * 16;
+        const f32x4 v0 = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        const f32x4 v1 = {acc[i][j][4], acc[i][j][5], acc[i][j][6], acc[i][j][7]};
+        const f32x4 v2 = {acc[i][j][8], acc[i][j][9], acc[i][j][10], acc[i][j][11]};
+        const f32x4 v3 = {acc[i][j][12], acc[i][j][13], acc[i][j][14], acc[i][j][15]};
+        asm volatile(
+            "s_nop 7\n\ts_nop 7\n\ts_nop 4\n\t"
+            "global_store_dwordx4 %0, %1, %5\n\t"
+            "global_store_dwordx4 %0, %2, %5 offset:1024\n\t"
+            "global_store_dwordx4 %0, %3, %5 offset:2048\n\t"
+            "global_store_dwordx4 %0, %4, %5 offset:3072" ::"v"(voff),
+            "a"(v0), "a"(v1), "a"(v2), "a"(v3), "s"(sb)
+            : "memory");
+      }
+    }
+    return;
+  }
+
+  // The five slot arrays fill the 160 KB exactly, so they are contiguous; the
+  // epilogue tile starts at whichever of them has the lowest LDS address.
+  uint16_t *lo = s0;
+  if (lds_addr_of(s1) < lds_addr_of(lo)) lo = s1;
+  if (lds_addr_of(s2) < lds_addr_of(lo)) lo = s2;
+  if (lds_addr_of(s3) < lds_addr_of(lo)) lo = s3;
+  if (lds_addr_of(s4) < lds_addr_of(lo)) lo = s4;
+
   // Epilogue through LDS.  The 32x32 accumulator layout puts value v of lane l
   // at row 8*(v/4) + 4*(l/32) + v%4, column l%32 of its tile, so a lane holds a
   // column slice; each wave writes its activated bf16 sub-tile into LDS (row
@@ -533,13 +711,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   constexpr int OUT_COLS = (ACT == ACT_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
   constexpr int PITCH = OUT_COLS * 2 + 16;                      // bytes per LDS row
   static_assert(DBM * PITCH <= NST * 2 * DSTAGE * 2, "epilogue tile must fit in the ring");
-  // The five slot arrays fill the 160 KB exactly, so they are contiguous; the
-  // epilogue tile starts at whichever of them has the lowest LDS address.
-  uint16_t *lo = s0;
-  if (lds_addr_of(s1) < lds_addr_of(lo)) lo = s1;
-  if (lds_addr_of(s2) < lds_addr_of(lo)) lo = s2;
-  if (lds_addr_of(s3) < lds_addr_of(lo)) lo = s3;
-  if (lds_addr_of(s4) < lds_addr_of(lo)) lo = s4;
   uint8_t *ep = reinterpret_cast<uint8_t *>(lo);
   __syncthreads();  // every wave is done with the ring
 #pragma unroll
@@ -574,6 +745,60 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
     if (r >= rows || col0 + c * 8 >= p.n_out) continue;
     const u32x4 val = *reinterpret_cast<const u32x4 *>(ep + r * PITCH + c * 16);
     st16(C + (static_cast<int64_t>(row0 + r) * p.ldc + col0 + c * 8) * 2, val);
+  }
+}
+
+// Finishes the K-split tiles of gemm_bf16_dma_kernel: for each split tile,
+// adds its pieces' fp32 partials in K order and applies the epilogue.  One
+// thread per float4 of the accumulator layout (SwiGLU: per gate float4, which
+// also reads its up partner, two column tiles further), grid-stride over
+// (tile, block-of-work) pairs.
+template <int ACT>
+__global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
+  constexpr int MI = 4, NJ = 4;
+  constexpr int kTileF = DBM * BN;
+  constexpr int kGroups = (ACT == ACT_SWIGLU ? kTileF / 2 : kTileF) / 4;  // float4 groups per tile
+  constexpr int kWork = kGroups / kThreads;                               // blocks of work per tile
+  const Split sp = split_plan(p, p.K / DK);
+  if (sp.nseg <= 1) return;
+  uint16_t *C = static_cast<uint16_t *>(p.C);
+  for (int b = blockIdx.x; b < sp.rest * kWork; b += gridDim.x) {
+    const int t = b / kWork;
+    int e, row0, rows, nt;
+    if (!find_tile<DBM>(p.offs, p.E, p.max_rows, p.n_tiles, sp.full + t, &e, &row0, &rows, &nt)) continue;
+    const int gi = (b - t * kWork) * kThreads + threadIdx.x;
+    int lane, v4, i, j, w;
+    if (ACT == ACT_SWIGLU) {  // gate tiles j = 0, 1 only
+      lane = gi & 63;
+      v4 = (gi >> 6) & 3;
+      j = (gi >> 8) & 1;
+      i = (gi >> 9) & 3;
+      w = gi >> 11;
+    } else {
+      lane = gi & 63;
+      v4 = (gi >> 6) & 3;
+      j = (gi >> 8) & 3;
+      i = (gi >> 10) & 3;
+      w = gi >> 12;
+    }
+    const int64_t off = static_cast<int64_t>((((w * MI + i) * NJ + j) * 4 + v4) * kWave + lane);
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(p.part + static_cast<int64_t>(t) * sp.nseg * kTileF) + off;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < sp.nseg; ++g) {
+      a += src[static_cast<int64_t>(g) * (kTileF / 4)];
+      if (ACT == ACT_SWIGLU) u += src[static_cast<int64_t>(g) * (kTileF / 4) + (NJ / 2) * 4 * kWave];
+    }
+    const int wm = w >> 1, wn = w & 1;
+    const int r0 = wm * 128 + i * 32 + 8 * v4 + 4 * (lane >> 5);
+    const int col = ACT == ACT_SWIGLU ? nt * (BN / 2) + wn * 64 + j * 32 + (lane & 31)
+                                      : nt * BN + wn * 128 + j * 32 + (lane & 31);
+    if (col >= p.n_out) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r0 + r >= rows) continue;
+      const float v = ACT == ACT_SWIGLU ? silu(a[r]) * u[r] : (ACT == ACT_GELU ? gelu_erf(a[r]) : a[r]);
+      C[static_cast<int64_t>(row0 + r0 + r) * p.ldc + col] = f32_to_bf16(v);
+    }
   }
 }
 
@@ -683,27 +908,92 @@ hipError_t run_bf16_dma(GemmParams p, int act, hipStream_t st) {
   p.m_tiles = static_cast<int>(mtile_bound(p.max_rows, p.E, DBM));
   const int bn_out = act == ACT_SWIGLU ? BN / 2 : BN;
   p.n_tiles = (p.n_out + bn_out - 1) / bn_out;
-  const int64_t blocks = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
-  if (blocks <= 0) return hipSuccess;
-  if (act == ACT_SWIGLU) gemm_bf16_dma_kernel<ACT_SWIGLU><<<blocks, kThreads, 0, st>>>(p);
-  else if (act == ACT_GELU) gemm_bf16_dma_kernel<ACT_GELU><<<blocks, kThreads, 0, st>>>(p);
-  else gemm_bf16_dma_kernel<ACT_NONE><<<blocks, kThreads, 0, st>>>(p);
+  const int64_t tiles = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
+  if (tiles <= 0) return hipSuccess;
+  // whole-round tiles + at most one round of K-split pieces, then (when this
+  // GEMM may split) the reduction of the split tiles, whose workgroups exit
+  // at once when the device-side counts left nothing to split
+  const int64_t blocks = tiles + p.units;
+  const int rblocks = 1024;
+  const bool reduce = p.max_split > 1 && p.slots > 1;
+  if (act == ACT_SWIGLU) {
+    gemm_bf16_dma_kernel<ACT_SWIGLU><<<blocks, kThreads, 0, st>>>(p);
+    if (reduce) split_reduce_kernel<ACT_SWIGLU><<<rblocks, kThreads, 0, st>>>(p);
+  } else if (act == ACT_GELU) {
+    gemm_bf16_dma_kernel<ACT_GELU><<<blocks, kThreads, 0, st>>>(p);
+    if (reduce) split_reduce_kernel<ACT_GELU><<<rblocks, kThreads, 0, st>>>(p);
+  } else {
+    gemm_bf16_dma_kernel<ACT_NONE><<<blocks, kThreads, 0, st>>>(p);
+    if (reduce) split_reduce_kernel<ACT_NONE><<<rblocks, kThreads, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 
-hipError_t run_gemm(int dtype, int bm, const GemmParams &p, int act, hipStream_t st) {
-  if (dtype == 0) return run_f32(p, act, st);
-  if (bm == 256 && p.K % DK == 0) return run_bf16_dma(p, act, st);
-  return bm == 256 ? run_bf16<256>(p, act, st) : run_bf16<128>(p, act, st);
+// Which kernel each GEMM of the FFN runs (the host never sees the per-expert
+// row counts, so the choice follows the average rows per expert), and which
+// of them may split their last round along K.
+struct FfnPlan {
+  int bm;
+  bool dma1, dma2;      // GEMM1 / GEMM2 on the 256 x 256 direct-to-LDS kernel
+  bool split1, split2;  // ... with enough K stages to split
+};
+
+FfnPlan plan_ffn(int dtype, int E, int d, int d_ff, int64_t max_rows) {
+  FfnPlan f{};
+  const int64_t avg_rows = max_rows / E;
+  f.bm = avg_rows >= 384 ? 256 : 128;
+  f.dma1 = dtype == 1 && f.bm == 256 && d % DK == 0;
+  f.dma2 = dtype == 1 && f.bm == 256 && d_ff % DK == 0;
+  f.split1 = f.dma1 && d / DK >= kSplitMinStages;
+  f.split2 = f.dma2 && d_ff / DK >= kSplitMinStages;
+  return f;
 }
 
+// Scratch: the fp32 partial tiles of the K-split pieces (the two GEMMs run
+// one after the other and share it).
+constexpr size_t kPartTileBytes = static_cast<size_t>(DBM) * BN * sizeof(float);
+
+// Workgroups in one round: one per CU (the kernel's 160 KB of LDS allows one
+// per CU), at most kSplitUnits.
+int round_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = kSplitUnits;
+  n = std::max(8, std::min(n, kSplitUnits));
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+
 }  // namespace
+
+size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows) {
+  if (max_rows == 0) return 0;
+  const FfnPlan f = plan_ffn(dtype, E, d, d_ff, max_rows);
+  if (!f.split1 && !f.split2) return 0;
+  // the pieces of one round: at most kSplitUnits, and at most kMaxSplit per
+  // tile of the larger GEMM
+  const int64_t mt = mtile_bound(max_rows, E, DBM);
+  const int64_t nt = std::max<int64_t>((d_ff + BN / 2 - 1) / (BN / 2), (d + BN - 1) / BN);
+  const int64_t pieces = std::min<int64_t>(kSplitUnits, mt * nt * kMaxSplit);
+  return static_cast<size_t>(pieces) * kPartTileBytes;
+}
 
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   if (a.max_rows == 0) return hipSuccess;
   const int n_up = a.act == 1 ? 2 : 1;
-  const int64_t avg_rows = a.max_rows / a.E;
-  const int bm = avg_rows >= 384 ? 256 : 128;
+  const FfnPlan f = plan_ffn(a.dtype, a.E, a.d, a.d_ff, a.max_rows);
+  const size_t need = ffn_scratch_bytes(a.dtype, a.E, a.d, a.d_ff, a.max_rows);
+  if (a.scratch_bytes < need || (need > 0 && a.scratch == nullptr)) return hipErrorInvalidValue;
+  float *part = static_cast<float *>(a.scratch);
+  const int units = round_units();
+  const int slots = static_cast<int>(std::min<size_t>(kSplitUnits, need / kPartTileBytes));
   GemmParams g1{};
   g1.A = a.x_perm;
   g1.lda = a.d;
@@ -718,7 +1008,15 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   g1.n_out = a.d_ff;
   g1.up_off = a.d_ff;
   g1.max_rows = a.max_rows;
-  hipError_t err = run_gemm(a.dtype, bm, g1, a.act == 1 ? ACT_SWIGLU : ACT_GELU, st);
+  g1.part = part;
+  g1.units = units;
+  g1.slots = slots;
+  g1.max_split = f.split1 ? kMaxSplit : 1;
+  const int act1 = a.act == 1 ? ACT_SWIGLU : ACT_GELU;
+  hipError_t err = a.dtype == 0  ? run_f32(g1, act1, st)
+                   : f.dma1      ? run_bf16_dma(g1, act1, st)
+                   : f.bm == 256 ? run_bf16<256>(g1, act1, st)
+                                 : run_bf16<128>(g1, act1, st);
   if (err != hipSuccess) return err;
   GemmParams g2{};
   g2.A = a.h;
@@ -734,7 +1032,14 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   g2.n_out = a.d;
   g2.up_off = 0;
   g2.max_rows = a.max_rows;
-  return run_gemm(a.dtype, bm, g2, ACT_NONE, st);
+  g2.part = part;
+  g2.units = units;
+  g2.slots = slots;
+  g2.max_split = f.split2 ? kMaxSplit : 1;
+  return a.dtype == 0   ? run_f32(g2, ACT_NONE, st)
+         : f.dma2      ? run_bf16_dma(g2, ACT_NONE, st)
+         : f.bm == 256 ? run_bf16<256>(g2, ACT_NONE, st)
+                       : run_bf16<128>(g2, ACT_NONE, st);
 }
 
 __global__ void fill_offsets_kernel(int32_t *dst, int32_t t) {

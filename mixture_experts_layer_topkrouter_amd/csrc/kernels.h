@@ -9,6 +9,7 @@
 namespace moe {
 
 constexpr int kEcMaxTokens = 16384;      // ExpertChoice: score column held in LDS
+constexpr int kSplitUnits = 256;        // grouped GEMM: most workgroups in one round (one per CU)
 constexpr int kPermuteBlock = 1024;      // assignments per counting block
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
@@ -62,7 +63,10 @@ struct FfnArgs {
   const int32_t *expert_offset;
   const void *w1, *w2;
   void *h, *y_perm;
+  void *scratch;  // ffn_scratch_bytes() bytes, 256-B aligned
+  size_t scratch_bytes;
 };
+size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows);
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st);
 
 struct CombineArgs {

@@ -54,7 +54,8 @@ class MoeConfig(ctypes.Structure):
 
 _LAYOUT_FIELDS = ["logits", "topk_idx", "topk_w", "scores", "ec_token", "ec_w", "x_perm", "row_token",
                   "slot_row", "slot_w", "tok_ptr", "expert_count", "expert_load", "expert_offset",
-                  "shared_offset", "h", "y_perm", "shared_h", "shared_y", "scratch", "scratch_bytes", "total"]
+                  "shared_offset", "h", "y_perm", "shared_h", "shared_y", "scratch", "scratch_bytes",
+                  "ffn_scratch", "ffn_scratch_bytes", "total"]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -85,7 +86,8 @@ def load_library() -> ctypes.CDLL:
         "moe_route": ([CP, P, P, P, i64, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_permute_scratch_bytes": ([CP, ctypes.POINTER(sz)], ctypes.c_int),
         "moe_permute": ([CP, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
-        "moe_expert_ffn": ([CP, P, P, P, P, P, P, P], ctypes.c_int),
+        "moe_expert_ffn_workspace_bytes": ([CP, ctypes.POINTER(sz)], ctypes.c_int),
+        "moe_expert_ffn": ([CP, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_unpermute": ([CP, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_layer_workspace": ([CP, ctypes.POINTER(WorkspaceLayout)], ctypes.c_int),
         "moe_layer_fwd": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
@@ -163,9 +165,25 @@ def permute(cfg: MoeConfig, x, x_perm, row_token, slot_row, expert_count, expert
            "moe_permute")
 
 
-def expert_ffn(cfg: MoeConfig, x_perm, expert_offset, w1, w2, h, y_perm, stream=None):
+def expert_ffn_workspace_bytes(cfg: MoeConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_expert_ffn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
+           "moe_expert_ffn_workspace_bytes")
+    return int(n.value)
+
+
+def alloc_ffn_workspace(cfg: MoeConfig, device="cuda") -> Optional[torch.Tensor]:
+    n = expert_ffn_workspace_bytes(cfg)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def expert_ffn(cfg: MoeConfig, x_perm, expert_offset, w1, w2, h, y_perm, workspace=None, stream=None):
+    """moe_expert_ffn.  `workspace` is a uint8 device tensor of
+    expert_ffn_workspace_bytes(cfg) bytes (see alloc_ffn_workspace); None
+    passes NULL, which the library rejects when the configuration needs one."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().moe_expert_ffn(ctypes.byref(cfg), _p(x_perm), _p(expert_offset), _p(w1), _p(w2), _p(h),
-                                         _p(y_perm), _stream(stream)), "moe_expert_ffn")
+                                         _p(y_perm), _p(workspace), nbytes, _stream(stream)), "moe_expert_ffn")
 
 
 def unpermute(cfg: MoeConfig, y_perm, slot_row, slot_w, y, *, tok_ptr=None, y_shared=None, stream=None):

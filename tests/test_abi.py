@@ -21,7 +21,7 @@ def test_library_exports_every_header_symbol():
 
 def test_status_strings_and_version():
     lib = moe.load_library()
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
 
@@ -40,8 +40,16 @@ def test_rows_capacity_and_workspace_sizes(name):
         assert moe.max_rows(cfg) == min(w.T * w.k, cap * w.E)
     L = moe.layer_workspace(cfg)
     assert L["total"] >= L["y_perm"] + moe.max_rows(cfg) * w.d * w.elem_bytes
-    offs = [L[n] for n in ("logits", "x_perm", "h", "y_perm", "total")]
+    offs = [L[n] for n in ("logits", "x_perm", "h", "y_perm", "ffn_scratch", "total")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    ffn = moe.expert_ffn_workspace_bytes(cfg)
+    assert L["ffn_scratch_bytes"] >= ffn and L["ffn_scratch"] + L["ffn_scratch_bytes"] <= L["total"]
+    # only bf16 256-row GEMMs (>= 384 rows per expert on average) with a
+    # reduction length >= 8192 split their last round of tiles along K
+    if w.dtype == W.F32 or moe.max_rows(cfg) // w.E < 384 or max(w.d, w.d_ff) < 8192:
+        assert ffn == 0
+    else:
+        assert ffn == 256 * 256 * 256 * 4
 
 
 def _cfg(**kw):
@@ -84,6 +92,17 @@ def test_unsupported_and_workspace_errors():
     # misaligned pointer -> invalid argument
     st = lib.moe_layer_fwd(ctypes.byref(cfg), ctypes.c_void_p(8), fake, None, 0, fake, fake, None, None, fake, fake,
                            1 << 30, None)
+    assert st == 1
+    # expert FFN without the workspace its configuration needs -> MOE_ERR_WORKSPACE
+    big = _cfg(num_tokens=4096, d_model=256, d_ff=8192)
+    need = moe.expert_ffn_workspace_bytes(big)
+    assert need > 0
+    st = lib.moe_expert_ffn(ctypes.byref(big), fake, fake, fake, fake, fake, fake, None, 0, None)
+    assert st == 3
+    st = lib.moe_expert_ffn(ctypes.byref(big), fake, fake, fake, fake, fake, fake, fake, need - 1, None)
+    assert st == 3
+    # misaligned workspace -> invalid argument
+    st = lib.moe_expert_ffn(ctypes.byref(big), fake, fake, fake, fake, fake, fake, ctypes.c_void_p(272), need, None)
     assert st == 1
     # null output -> invalid argument
     st = lib.moe_unpermute(ctypes.byref(cfg), fake, None, fake, fake, None, None, None)

@@ -29,6 +29,14 @@ SMALL = {
     "mixtral_small": W.small_variant(WL["mixtral_top2_bf16"], T=1600, d=384, d_ff=520),
     "finegrained_small": W.small_variant(WL["finegrained_shared_bf16"], T=700, d=256, E=12, d_ff=136,
                                          d_ff_shared=264, wr_std=1.0 / 16.0),
+    # >= 384 rows per expert and a reduction length of 8192: the bf16
+    # 256 x 256 GEMM cuts its last round of tiles along K (8 pieces each) and
+    # a second pass adds them: down projection (plain epilogue), up
+    # projection with SwiGLU (gate and up pieces paired), up projection with
+    # GELU
+    "ksplit_down_small": W.small_variant(WL["mixtral_top2_bf16"], T=400, d=256, E=2, d_ff=8192),
+    "ksplit_up_swiglu_small": W.small_variant(WL["mixtral_top2_bf16"], T=400, d=8192, E=2, d_ff=256),
+    "ksplit_up_gelu_small": W.small_variant(WL["switch_top1_bf16"], T=800, d=8192, E=2, d_ff=264, cf=0.0),
     "switch_small": W.small_variant(WL["switch_top1_bf16"], T=2000, d=192, E=16, d_ff=328),
     "correlated_small": W.small_variant(WL["correlated_top2_bf16"], T=1500, d=256, E=16, d_ff=200),
     "correlated_ec_small": W.small_variant(WL["correlated_ec_bf16"], T=1500, d=256, E=16, d_ff=200,
@@ -109,12 +117,12 @@ def test_entry_points_step_by_step_match_layer_fwd():
     moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off, topk_idx=idx, scratch=scratch)
     h = torch.empty((rows, w.d_ff), dtype=dt, device=dev_)
     y_perm = torch.empty((rows, d), dtype=dt, device=dev_)
-    moe.expert_ffn(cfg, x_perm, off, dev.w1, dev.w2, h, y_perm)
+    moe.expert_ffn(cfg, x_perm, off, dev.w1, dev.w2, h, y_perm, moe.alloc_ffn_workspace(cfg))
     scfg = moe.MoeConfig(T, d, 1, 1, w.d_ff_shared, 0, 0.0, 0, w.dtype, w.act, W.SOFTMAX_ALL)
     soff = torch.tensor([0, T], dtype=torch.int32, device=dev_)
     hs = torch.empty((T, w.d_ff_shared), dtype=dt, device=dev_)
     ys = torch.empty((T, d), dtype=dt, device=dev_)
-    moe.expert_ffn(scfg, dev.x, soff, dev.ws1, dev.ws2, hs, ys)
+    moe.expert_ffn(scfg, dev.x, soff, dev.ws1, dev.ws2, hs, ys, moe.alloc_ffn_workspace(scfg))
     y = torch.empty((T, d), dtype=dt, device=dev_)
     moe.unpermute(cfg, y_perm, slot_row, tw, y, y_shared=ys)
     torch.cuda.synchronize()
@@ -196,6 +204,23 @@ def test_deterministic_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), layer.y.view(torch.int16))
     assert torch.equal(xp1.view(torch.int16), layer.view("x_perm").view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_k_split_tiles_deterministic_bitwise():
+    """Tiles cut along K are summed in piece order by whichever piece
+    finishes last: repeated runs give identical bits."""
+    w = SMALL["ksplit_down_small"]
+    cfg = moe.make_config(w)
+    assert moe.expert_ffn_workspace_bytes(cfg) > 0
+    layer, _ = run_layer(w)
+    y1 = layer.y.clone()
+    h1 = layer.view("h").clone()
+    for _ in range(3):
+        layer.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(h1.view(torch.int16), layer.view("h").view(torch.int16))
+        assert torch.equal(y1.view(torch.int16), layer.y.view(torch.int16))
 
 
 @pytest.mark.gpu
