@@ -222,7 +222,7 @@ def main():
     achieved = ffn_flops / ffn_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
-                "kernel": "grouped expert FFN: gemm_bf16_dma_kernel GEMM1 (SwiGLU) + GEMM2, one moe_expert_ffn call",
+                "kernel": "grouped expert FFN: gemm_bf16_dma_kernel GEMM1 (SwiGLU) + GEMM2 + split_reduce_kernel, one moe_expert_ffn call",
                 "avg_ms": round(stage_ms["expert_ffn"], 4), "flops_per_launch": int(ffn_flops)}
 
     cpu = None
