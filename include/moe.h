@@ -145,7 +145,7 @@ moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk
                        void *scratch, size_t scratch_bytes, void *stream);
 
 /* Bytes of device workspace moe_expert_ffn needs for this configuration.
- * A bf16 GEMM with at least 384 rows per expert on average and a reduction
+ * A bf16 GEMM with at least 192 rows per expert on average and a reduction
  * length (d_model for the up projection, d_ff for the down projection) of at
  * least 8192 cuts the tiles of its last, partial round of workgroups along K
  * and keeps their fp32 partial tiles here: at most 256 tiles of 256 KiB

@@ -7,11 +7,15 @@
 // Communication" (token_unpermutation); "Expert Parallelism > Key
 // Parameters", capacity_factor paragraph (a dropped assignment adds nothing).
 //
-// gfx950 design: one wave per token; each lane owns 16-byte column chunks of
-// the output row, accumulates w * y_perm[row] in fp32 over the token's slots
-// in slot order (a fixed order, so the result is deterministic), adds the
-// shared expert's row and rounds once.  Every load and store is a 16-byte
-// vector access to a contiguous row, so the pass is a pure HBM stream.
+// gfx950 design: one wave per token; each lane owns CPL 16-byte column
+// chunks of the output row (one pass over the row when d fits) and
+// accumulates w * y_perm[row] in fp32 over the token's slots in slot order (a
+// fixed order, so the result is deterministic), adds the shared expert's row
+// and rounds once.  The slot rows and weights are wave-uniform scalars; for
+// each pair of slots every lane issues all of its chunk loads before the
+// first add, so a wave keeps 2 * CPL * 1 KB in flight instead of waiting on
+// one load per chunk.  Every load and store is a 16-byte vector access to a
+// contiguous row: a pure HBM stream.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,7 +25,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTokens = kThreads / kWave;
 
-template <bool BF16>
+template <bool BF16, int CPL>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restrict__ y_perm_,
                                                            const int32_t *__restrict__ tok_ptr,
                                                            const int32_t *__restrict__ slot_row,
@@ -34,61 +38,107 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
   if (t >= T) return;
   const int l = lane_id();
   // slot ranges and rows come from device memory: clamp them to the buffers
-  const int64_t s0 = tok_ptr ? min(max(static_cast<int64_t>(tok_ptr[t]), static_cast<int64_t>(0)), nslots)
-                             : static_cast<int64_t>(t) * k;
-  const int64_t s1 = tok_ptr ? min(max(static_cast<int64_t>(tok_ptr[t + 1]), s0), nslots)
-                             : static_cast<int64_t>(t) * k + k;
+  int64_t s0 = tok_ptr ? min(max(static_cast<int64_t>(tok_ptr[t]), static_cast<int64_t>(0)), nslots)
+                       : static_cast<int64_t>(t) * k;
+  int64_t s1 = tok_ptr ? min(max(static_cast<int64_t>(tok_ptr[t + 1]), s0), nslots) : static_cast<int64_t>(t) * k + k;
+  s0 = uniform64(s0);
+  s1 = uniform64(s1);
   const size_t row_bytes = static_cast<size_t>(d) * (BF16 ? 2 : 4);
   const uint8_t *y_perm = static_cast<const uint8_t *>(y_perm_);
   const uint8_t *y_shared = static_cast<const uint8_t *>(y_shared_);
   uint8_t *y = static_cast<uint8_t *>(y_);
   const int nchunk = d / kElems;
-  for (int c = l; c < nchunk; c += kWave) {
-    float acc[kElems];
+  auto add = [&](float (&acc)[CPL][kElems], const u32x4 (&v)[CPL], float w) {
 #pragma unroll
-    for (int i = 0; i < kElems; ++i) acc[i] = 0.f;
-    for (int64_t s = s0; s < s1; ++s) {
-      const int row = slot_row[s];
-      if (row < 0 || row >= rows) continue;
-      const float w = slot_w[s];
-      const u32x4 v = ld16(y_perm + static_cast<size_t>(row) * row_bytes + static_cast<size_t>(c) * 16);
+    for (int u = 0; u < CPL; ++u) {
       if (BF16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(w, __uint_as_float(v[i] << 16), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(w, __uint_as_float(v[i] & 0xffff0000u), acc[2 * i + 1]);
+          acc[u][2 * i] = fmaf(w, __uint_as_float(v[u][i] << 16), acc[u][2 * i]);
+          acc[u][2 * i + 1] = fmaf(w, __uint_as_float(v[u][i] & 0xffff0000u), acc[u][2 * i + 1]);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, __uint_as_float(v[i]), acc[i]);
+        for (int i = 0; i < 4; ++i) acc[u][i] = fmaf(w, __uint_as_float(v[u][i]), acc[u][i]);
       }
     }
-    const size_t off = static_cast<size_t>(t) * row_bytes + static_cast<size_t>(c) * 16;
-    if (y_shared) {
-      const u32x4 v = ld16(y_shared + off);
+  };
+  auto load = [&](u32x4 (&v)[CPL], int row, int c0) {
+    const uint8_t *src = y_perm + static_cast<size_t>(row) * row_bytes;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = c0 + u * kWave + l;
+      v[u] = c < nchunk ? ld16(src + static_cast<size_t>(c) * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  for (int c0 = 0; c0 < nchunk; c0 += CPL * kWave) {
+    float acc[CPL][kElems];
+#pragma unroll
+    for (int u = 0; u < CPL; ++u)
+#pragma unroll
+      for (int i = 0; i < kElems; ++i) acc[u][i] = 0.f;
+    for (int64_t s = s0; s < s1; s += 2) {
+      const bool two = s + 1 < s1;
+      const int ra = __builtin_amdgcn_readfirstlane(slot_row[s]);
+      const float wa = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(slot_w[s])));
+      const int rb = two ? __builtin_amdgcn_readfirstlane(slot_row[s + 1]) : -1;
+      const float wb = two ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(slot_w[s + 1]))) : 0.f;
+      const bool va = ra >= 0 && ra < rows, vb = rb >= 0 && rb < rows;
+      u32x4 xa[CPL], xb[CPL];
+      if (va) load(xa, ra, c0);
+      if (vb) load(xb, rb, c0);
+      if (va) add(acc, xa, wa);
+      if (vb) add(acc, xb, wb);
+    }
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = c0 + u * kWave + l;
+      if (c >= nchunk) continue;
+      const size_t off = static_cast<size_t>(t) * row_bytes + static_cast<size_t>(c) * 16;
+      if (y_shared) {
+        const u32x4 v = ld16(y_shared + off);
+        if (BF16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[u][2 * i] += __uint_as_float(v[i] << 16);
+            acc[u][2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[u][i] += __uint_as_float(v[i]);
+        }
+      }
+      u32x4 o;
       if (BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += __uint_as_float(v[i] << 16);
-          acc[2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
-        }
+        for (int i = 0; i < 4; ++i)
+          o[i] = static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i])) |
+                 (static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i + 1])) << 16);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(v[i]);
+        for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[u][i]);
       }
+      st16(y + off, o);
     }
-    u32x4 o;
-    if (BF16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
-               (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
-    }
-    st16(y + off, o);
   }
+}
+
+template <bool BF16>
+void launch(const CombineArgs &a, int blocks, hipStream_t st) {
+  const int nchunk = a.d / (BF16 ? 8 : 4);
+  const int per_lane = (nchunk + kWave - 1) / kWave;
+  if (per_lane <= 1)
+    combine_kernel<BF16, 1><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
+                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots);
+  else if (per_lane <= 2)
+    combine_kernel<BF16, 2><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
+                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots);
+  else if (per_lane <= 4)
+    combine_kernel<BF16, 4><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
+                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots);
+  else
+    combine_kernel<BF16, 8><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
+                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots);
 }
 
 }  // namespace
@@ -96,12 +146,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   const int blocks = (a.T + kTokens - 1) / kTokens;
-  if (a.dtype == 1)
-    combine_kernel<true><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                      a.y, a.T, a.d, a.k, a.rows, a.nslots);
-  else
-    combine_kernel<false><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                       a.y, a.T, a.d, a.k, a.rows, a.nslots);
+  if (a.dtype == 1) launch<true>(a, blocks, st);
+  else launch<false>(a, blocks, st);
   return hipGetLastError();
 }
 

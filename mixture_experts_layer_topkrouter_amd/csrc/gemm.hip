@@ -18,7 +18,7 @@
 //   ids are remapped so each of the 8 XCDs takes a contiguous run of that
 //   order.  Tiles running together on one XCD then share weight tiles or
 //   rows in its L2, and no group mixes two experts' weights.
-// * main kernel (gemm_bf16_dma_kernel, K a multiple of 32, >= 384 rows per
+// * main kernel (gemm_bf16_dma_kernel, K a multiple of 32, >= 192 rows per
 //   expert on average): 256 x 256 tiles, 4 waves of 128 x 128
 //   v_mfma_f32_32x32x16_bf16 results, operands loaded straight into a 5-deep
 //   LDS ring by direct-to-LDS loads (its own comment has the details).  The
@@ -332,6 +332,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
 constexpr int DK = 32;   // K per stage
 constexpr int NST = 5;   // stages in the LDS ring
 constexpr int DBM = 256; // tile rows
+constexpr int kDmaWaves = 4;  // waves per workgroup of gemm_bf16_dma_kernel (4 or 8)
+// The 256-row kernel runs when the experts average at least this many rows
+// (measured: with 256 rows per expert it is 25-28 % faster than the 128-row
+// kernel; with at most 128 it is slower, its tiles being mostly padding).
+constexpr int64_t kDmaMinAvgRows = 192;
 constexpr int DSTAGE = DBM * DK;  // elements per operand per stage
 
 // K-split of the last round: only GEMMs with at least kSplitMinStages K
@@ -455,13 +460,23 @@ __device__ __forceinline__ void keep_live(bf16x8 (&fa)[2][2][MI], bf16x8 (&fb)[2
   }
 }
 
-template <int ACT>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
-  // v_mfma_f32_32x32x16_bf16: one wave per SIMD keeps the matrix core full with
-  // it (the 16x16x32 form does not).  Each wave owns 128 x 128 = 4 x 4 tiles of
-  // 32 x 32; per 16-wide K step it reads 4 A and 4 B fragments (16 B per lane:
-  // row l%32, K chunk l/32) and issues 16 MFMAs.
-  constexpr int MI = 4, NJ = 4;
+template <int ACT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p) {
+  // v_mfma_f32_32x32x16_bf16 (the 16x16x32 form does not keep the matrix core
+  // full from one wave per SIMD).  WAVES = 4: one wave per SIMD, each owning
+  // 128 x 128 = 4 x 4 tiles of 32 x 32; WAVES = 8: two waves per SIMD, each
+  // owning 64 x 128 = 2 x 4 tiles, so one wave's memory instructions can wait
+  // while the other feeds the matrix core.  Per 16-wide K step a wave reads
+  // MI A and NJ B fragments (16 B per lane: row l%32, K chunk l/32) and issues
+  // MI * NJ MFMAs.
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
+  constexpr int NTH = WAVES * kWave;
+  constexpr int MI = WAVES == 4 ? 4 : 2, NJ = 4;
+  constexpr int RW = 32 * MI;           // rows per wave
+  constexpr int ND = 32 / WAVES;        // load instructions per wave per stage
+  constexpr int NR = 2 * (MI + NJ);     // fragment reads per wave per stage
+  constexpr int NM = 2 * MI * NJ;       // MFMAs per wave per stage
+  static_assert((WAVES == 4 ? NM / 2 : 3 * NM / 4) == NR && NM / 4 == ND, "interleave covers every read and load");
   // one array per ring slot: A stage at [0, DSTAGE), B stage at [DSTAGE, 2*DSTAGE)
   __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * DSTAGE], s1[2 * DSTAGE], s2[2 * DSTAGE],
       s3[2 * DSTAGE], s4[2 * DSTAGE];
@@ -485,14 +500,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
     else return s4;
   };
 
-  // DMA sources: wave w, instruction i fills LDS chunks [(4i+w)*64, +64), i.e.
-  // rows (4i+w)*16 .. +16; lane l -> row r = q/4, stored chunk q%4, which holds
-  // logical chunk (q%4) ^ ((r>>2)&3).  Per-lane byte offsets from A / B (they
-  // fit 32 bits: the host limits every operand to 2^31 elements).
-  uint32_t a_off[4], b_off[4];
+  // DMA sources: wave w, instruction i of an operand fills LDS chunks
+  // [(WAVES*i+w)*64, +64), i.e. rows (WAVES*i+w)*16 .. +16; lane l -> row
+  // r = q/4, stored chunk q%4, which holds logical chunk (q%4) ^ ((r>>2)&3).
+  // Per-lane byte offsets from A / B (they fit 32 bits: the host limits every
+  // operand to 2^31 elements).
+  uint32_t a_off[ND / 2], b_off[ND / 2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = (4 * i + w) * 64 + l;
+  for (int i = 0; i < ND / 2; ++i) {
+    const int q = (WAVES * i + w) * 64 + l;
     const int r = q >> 2;
     const int c = (q & 3) ^ ((r >> 2) & 3);
     a_off[i] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
@@ -510,9 +526,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   auto issue = [&](auto S, int st) {
     const uint32_t base = lds_addr_of(slot(S));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dma16(a_off[i], A + st * DK * 2, base + (4 * i + w) * 64 * 16);
-      dma16(b_off[i], B + st * DK * 2, base + DSTAGE * 2 + (4 * i + w) * 64 * 16);
+    for (int i = 0; i < ND / 2; ++i) {
+      dma16(a_off[i], A + st * DK * 2, base + (WAVES * i + w) * 64 * 16);
+      dma16(b_off[i], B + st * DK * 2, base + DSTAGE * 2 + (WAVES * i + w) * 64 * 16);
     }
   };
 
@@ -521,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   const int fsw = (frow >> 2) & 3;
   const int fch0 = ((l >> 5) ^ fsw) * 8;        // K step 0: chunks 0,1
   const int fch1 = (((l >> 5) + 2) ^ fsw) * 8;  // K step 1: chunks 2,3
-  const int a_row = (wm * 128 + frow) * DK;     // + i*32*DK
+  const int a_row = (wm * RW + frow) * DK;      // + i*32*DK
   int b_row[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -571,10 +587,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   // also wait for the DMA still in flight)
   auto wait_stage = [&](int st, int issued_last) {
     const int ahead = issued_last - st;
-    if (ahead >= 4) wait_vm<32>();
-    else if (ahead == 3) wait_vm<24>();
-    else if (ahead == 2) wait_vm<16>();
-    else if (ahead == 1) wait_vm<8>();
+    if (ahead >= 4) wait_vm<4 * ND>();
+    else if (ahead == 3) wait_vm<3 * ND>();
+    else if (ahead == 2) wait_vm<2 * ND>();
+    else if (ahead == 1) wait_vm<ND>();
     else wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
@@ -590,11 +606,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   read_frags(Slot<0>{}, Slot<0>{});
 
   // iteration kt: stage kt sits in slot kt%5 and fragment set kt%2.
-  // After the barrier that publishes stage kt+1, stage kt's 32 MFMAs are
-  // interleaved with the 16 fragment reads of stage kt+1 (into the other
-  // register set) and the 8 DMA instructions that refill stage kt's slot with
-  // stage kt+5; sched_barrier pins this order, so the LDS reads and the loads
-  // issue in the shadow of the matrix core.
+  // After the barrier that publishes stage kt+1, stage kt's NM MFMAs are
+  // interleaved with the NR fragment reads of stage kt+1 (into the other
+  // register set) and the ND DMA instructions that refill stage kt's slot
+  // with stage kt+5; sched_barrier pins this order, so the LDS reads and the
+  // loads issue in the shadow of the matrix core.
   auto iter = [&](auto S, auto SET, int kt) {
     constexpr int s = decltype(S)::value;
     constexpr int set = decltype(SET)::value;
@@ -611,22 +627,26 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][ks][i], fb[set][ks][j], acc[i][j], 0, 0, 0);
-          // every 4 MFMAs: two fragment reads (t%4 == 0, 2) and one load
-          // (t%4 == 1), spread out so the per-CU load path drains between
+          // every 4 MFMAs one load (t%4 == 1 for 4 waves, 3 for 8 waves) and
+          // the fragment reads in the other slots (4 waves: t even; 8 waves:
+          // t%4 != 3), spread out so the per-CU load path drains between
           // load issues instead of stalling the wave that issues them
-          const int t = ks * 16 + i * 4 + j;
-          if ((t & 1) == 0) {
-            if (more) {  // read t/2: K step (t/2)/8, A tiles 0-3 then B tiles 0-3
-              const int rd = t >> 1, rks = rd >> 3, r = rd & 7;
+          const int t = ks * (MI * NJ) + i * NJ + j;
+          constexpr int kLoadSlot = WAVES == 4 ? 1 : 3;
+          const bool is_read = WAVES == 4 ? (t & 1) == 0 : (t & 3) != 3;
+          if (is_read) {
+            if (more) {  // read rd: K step rd / (MI+NJ), A tiles then B tiles
+              const int rd = WAVES == 4 ? t >> 1 : (t >> 2) * 3 + (t & 3);
+              const int rks = rd / (MI + NJ), r = rd % (MI + NJ);
               const int ch = rks ? fch1 : fch0;
               if (r < MI) fa[set ^ 1][rks][r] = *reinterpret_cast<const bf16x8 *>(ls + a_row + r * 32 * DK + ch);
               else fb[set ^ 1][rks][r - MI] = *reinterpret_cast<const bf16x8 *>(ls + b_row[r - MI] + ch);
             }
-          } else if ((t & 3) == 1) {
+          } else if ((t & 3) == kLoadSlot) {
             if (refill) {
               const int dd = t >> 2, ii = dd >> 1;
-              if ((dd & 1) == 0) dma16(a_off[ii], A + (kt + 5) * DK * 2, dbase + (4 * ii + w) * 64 * 16);
-              else dma16(b_off[ii], B + (kt + 5) * DK * 2, dbase + DSTAGE * 2 + (4 * ii + w) * 64 * 16);
+              if ((dd & 1) == 0) dma16(a_off[ii], A + (kt + 5) * DK * 2, dbase + (WAVES * ii + w) * 64 * 16);
+              else dma16(b_off[ii], B + (kt + 5) * DK * 2, dbase + DSTAGE * 2 + (WAVES * ii + w) * 64 * 16);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -717,7 +737,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int lr = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+      const int lr = wm * RW + i * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
       if (ACT == ACT_SWIGLU) {
 #pragma unroll
         for (int j = 0; j < NJ / 2; ++j) {
@@ -740,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int col0 = nt * OUT_COLS;
   uint8_t *C = static_cast<uint8_t *>(p.C);
-  for (int q = tid; q < DBM * CHUNKS; q += kThreads) {
+  for (int q = tid; q < DBM * CHUNKS; q += NTH) {
     const int r = q / CHUNKS, c = q - (q / CHUNKS) * CHUNKS;
     if (r >= rows || col0 + c * 8 >= p.n_out) continue;
     const u32x4 val = *reinterpret_cast<const u32x4 *>(ep + r * PITCH + c * 16);
@@ -753,12 +773,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_dma_kernel(GemmParams p) {
 // thread per float4 of the accumulator layout (SwiGLU: per gate float4, which
 // also reads its up partner, two column tiles further), grid-stride over
 // (tile, block-of-work) pairs.
-template <int ACT>
+template <int ACT, int WAVES>
 __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
-  constexpr int MI = 4, NJ = 4;
+  constexpr int MI = WAVES == 4 ? 4 : 2, NJ = 4, RW = 32 * MI;  // as in gemm_bf16_dma_kernel
+  constexpr int NJE = ACT == ACT_SWIGLU ? NJ / 2 : NJ;         // tiles a thread starts from
   constexpr int kTileF = DBM * BN;
-  constexpr int kGroups = (ACT == ACT_SWIGLU ? kTileF / 2 : kTileF) / 4;  // float4 groups per tile
-  constexpr int kWork = kGroups / kThreads;                               // blocks of work per tile
+  constexpr int kGroups = WAVES * MI * NJE * 4 * kWave;          // float4 groups per tile
+  constexpr int kWork = kGroups / kThreads;                      // blocks of work per tile
+  static_assert(kGroups * 4 == (ACT == ACT_SWIGLU ? kTileF / 2 : kTileF), "one float4 per thread");
   const Split sp = split_plan(p, p.K / DK);
   if (sp.nseg <= 1) return;
   uint16_t *C = static_cast<uint16_t *>(p.C);
@@ -767,20 +789,10 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
     int e, row0, rows, nt;
     if (!find_tile<DBM>(p.offs, p.E, p.max_rows, p.n_tiles, sp.full + t, &e, &row0, &rows, &nt)) continue;
     const int gi = (b - t * kWork) * kThreads + threadIdx.x;
-    int lane, v4, i, j, w;
-    if (ACT == ACT_SWIGLU) {  // gate tiles j = 0, 1 only
-      lane = gi & 63;
-      v4 = (gi >> 6) & 3;
-      j = (gi >> 8) & 1;
-      i = (gi >> 9) & 3;
-      w = gi >> 11;
-    } else {
-      lane = gi & 63;
-      v4 = (gi >> 6) & 3;
-      j = (gi >> 8) & 3;
-      i = (gi >> 10) & 3;
-      w = gi >> 12;
-    }
+    // gi -> (wave, i, j, v4, lane); SwiGLU threads start from the gate tiles
+    const int lane = gi & 63, v4 = (gi >> 6) & 3;
+    const int rest = gi >> 8;
+    const int j = rest % NJE, i = (rest / NJE) % MI, w = rest / (NJE * MI);
     const int64_t off = static_cast<int64_t>((((w * MI + i) * NJ + j) * 4 + v4) * kWave + lane);
     const f32x4 *src = reinterpret_cast<const f32x4 *>(p.part + static_cast<int64_t>(t) * sp.nseg * kTileF) + off;
     f32x4 a = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
@@ -789,7 +801,7 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
       if (ACT == ACT_SWIGLU) u += src[static_cast<int64_t>(g) * (kTileF / 4) + (NJ / 2) * 4 * kWave];
     }
     const int wm = w >> 1, wn = w & 1;
-    const int r0 = wm * 128 + i * 32 + 8 * v4 + 4 * (lane >> 5);
+    const int r0 = wm * RW + i * 32 + 8 * v4 + 4 * (lane >> 5);
     const int col = ACT == ACT_SWIGLU ? nt * (BN / 2) + wn * 64 + j * 32 + (lane & 31)
                                       : nt * BN + wn * 128 + j * 32 + (lane & 31);
     if (col >= p.n_out) continue;
@@ -916,15 +928,16 @@ hipError_t run_bf16_dma(GemmParams p, int act, hipStream_t st) {
   const int64_t blocks = tiles + p.units;
   const int rblocks = 1024;
   const bool reduce = p.max_split > 1 && p.slots > 1;
+  constexpr int W = kDmaWaves;
   if (act == ACT_SWIGLU) {
-    gemm_bf16_dma_kernel<ACT_SWIGLU><<<blocks, kThreads, 0, st>>>(p);
-    if (reduce) split_reduce_kernel<ACT_SWIGLU><<<rblocks, kThreads, 0, st>>>(p);
+    gemm_bf16_dma_kernel<ACT_SWIGLU, W><<<blocks, W * kWave, 0, st>>>(p);
+    if (reduce) split_reduce_kernel<ACT_SWIGLU, W><<<rblocks, kThreads, 0, st>>>(p);
   } else if (act == ACT_GELU) {
-    gemm_bf16_dma_kernel<ACT_GELU><<<blocks, kThreads, 0, st>>>(p);
-    if (reduce) split_reduce_kernel<ACT_GELU><<<rblocks, kThreads, 0, st>>>(p);
+    gemm_bf16_dma_kernel<ACT_GELU, W><<<blocks, W * kWave, 0, st>>>(p);
+    if (reduce) split_reduce_kernel<ACT_GELU, W><<<rblocks, kThreads, 0, st>>>(p);
   } else {
-    gemm_bf16_dma_kernel<ACT_NONE><<<blocks, kThreads, 0, st>>>(p);
-    if (reduce) split_reduce_kernel<ACT_NONE><<<rblocks, kThreads, 0, st>>>(p);
+    gemm_bf16_dma_kernel<ACT_NONE, W><<<blocks, W * kWave, 0, st>>>(p);
+    if (reduce) split_reduce_kernel<ACT_NONE, W><<<rblocks, kThreads, 0, st>>>(p);
   }
   return hipGetLastError();
 }
@@ -941,7 +954,7 @@ struct FfnPlan {
 FfnPlan plan_ffn(int dtype, int E, int d, int d_ff, int64_t max_rows) {
   FfnPlan f{};
   const int64_t avg_rows = max_rows / E;
-  f.bm = avg_rows >= 384 ? 256 : 128;
+  f.bm = avg_rows >= kDmaMinAvgRows ? 256 : 128;
   f.dma1 = dtype == 1 && f.bm == 256 && d % DK == 0;
   f.dma2 = dtype == 1 && f.bm == 256 && d_ff % DK == 0;
   f.split1 = f.dma1 && d / DK >= kSplitMinStages;

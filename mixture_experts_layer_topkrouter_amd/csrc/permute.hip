@@ -7,20 +7,23 @@
 // paragraph (assignments beyond an expert's capacity are dropped and add
 // nothing to the output).
 //
-// gfx950 design (three launches, no floating point, no global atomics, so
-// the result is bit-reproducible):
+// gfx950 design (two or three launches, no floating point, no global
+// atomics, so the result is bit-reproducible):
 // 1. count: a block takes 1024 consecutive assignments (token-major order).
 //    Each wave labels 64 of them at a time: a lane finds the lanes holding the
 //    same expert with one ballot per bit of the expert id, so its rank inside
 //    the 64 is a popcount and the lowest such lane writes the group size to a
 //    private LDS slot.  A per-expert scan over the 16 groups gives block-local
 //    ranks and the block's histogram row.
-// 2. scan: one workgroup turns the [blocks x E] histogram into per-block
-//    bases (exclusive over blocks), the loads, the kept counts min(load, C)
-//    and the exclusive expert offsets.
+// 2. scan: the [blocks x E] histogram becomes per-block bases (exclusive
+//    over blocks), the loads, the kept counts min(load, C) and the exclusive
+//    expert offsets.
 // 3. scatter: one wave per token computes its k rows (or -1 when the rank is
 //    at or above the capacity), loads the token row once with 16-B loads and
 //    stores it to each kept row.
+// When the histogram table is small (the usual case) every scatter
+// workgroup does step 2 itself in LDS, which saves the single-workgroup
+// scan launch.
 #include "common.h"
 #include "kernels.h"
 
@@ -105,6 +108,35 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t *__restrict_
 
 constexpr int kScatterTokens = kThreads / kWave;  // one wave per token
 
+// Loads the token row (CPL 16-B chunks per lane per pass) and stores it to
+// each of the token's kept rows (row of slot j in lane j).
+template <int CPL>
+__device__ __forceinline__ void copy_row(const uint8_t *__restrict__ x, size_t row_bytes, int t, int k, int row,
+                                         uint8_t *__restrict__ x_perm) {
+  const int l = lane_id();
+  const int nchunk = static_cast<int>(row_bytes / 16);
+  const uint8_t *src = x + static_cast<size_t>(t) * row_bytes;
+  for (int c0 = 0; c0 < nchunk; c0 += CPL * kWave) {
+    u32x4 v[CPL];
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = c0 + u * kWave + l;
+      if (c < nchunk) v[u] = ld16(src + static_cast<size_t>(c) * 16);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int rj = __shfl(row, j, kWave);
+      if (rj < 0) continue;
+      uint8_t *dst = x_perm + static_cast<size_t>(rj) * row_bytes;
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int c = c0 + u * kWave + l;
+        if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
+      }
+    }
+  }
+}
+
+template <int CPL>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(
     const uint8_t *__restrict__ x, size_t row_bytes, const int32_t *__restrict__ idx, int T, int k, int E,
     int64_t cap, const int32_t *__restrict__ blk, const int32_t *__restrict__ rank,
@@ -124,26 +156,68 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
     }
     slot_row[a] = row;
   }
-  const int nchunk = static_cast<int>(row_bytes / 16);
-  const uint8_t *src = x + static_cast<size_t>(t) * row_bytes;
-  for (int c0 = 0; c0 < nchunk; c0 += 4 * kWave) {
-    u32x4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = c0 + u * kWave + l;
-      if (c < nchunk) v[u] = ld16(src + static_cast<size_t>(c) * 16);
+  copy_row<CPL>(x, row_bytes, t, k, row, x_perm);
+}
+
+// Scan and scatter in one launch, for histogram tables of at most
+// kFusedTable entries: every workgroup loads the [blocks x E] histogram into
+// LDS and computes the per-block bases (exclusive over blocks), the loads,
+// the kept counts and the expert offsets itself (workgroup 0 also stores
+// them), then copies its 16 tokens' rows.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedTokens = kFusedThreads / kWave;
+constexpr int kFusedTable = 8192;
+
+template <int CPL>
+__global__ __launch_bounds__(kFusedThreads) void scan_scatter_kernel(
+    const uint8_t *__restrict__ x, size_t row_bytes, const int32_t *__restrict__ idx, int T, int k, int E,
+    int64_t cap, const int32_t *__restrict__ blk, int nblk, const int32_t *__restrict__ rank,
+    int32_t *__restrict__ expert_count, int32_t *__restrict__ expert_load, int32_t *__restrict__ expert_offset,
+    uint8_t *__restrict__ x_perm, int32_t *__restrict__ row_token, int32_t *__restrict__ slot_row) {
+  __shared__ int tab[kFusedTable];
+  __shared__ int offs[kMaxExperts + 1];
+  __shared__ int tmp[kFusedThreads / kWave + 1];
+  const int tid = threadIdx.x;
+  const int n = nblk * E;
+  for (int i = tid; i < n; i += kFusedThreads) tab[i] = blk[i];
+  __syncthreads();
+  int cnt = 0, load = 0;
+  if (tid < E) {
+    for (int b = 0; b < nblk; ++b) {
+      const int c = tab[b * E + tid];
+      tab[b * E + tid] = load;
+      load += c;
     }
-    for (int j = 0; j < k; ++j) {
-      const int rj = __shfl(row, j, kWave);
-      if (rj < 0) continue;
-      uint8_t *dst = x_perm + static_cast<size_t>(rj) * row_bytes;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + u * kWave + l;
-        if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
-      }
-    }
+    cnt = (cap >= 0 && load > cap) ? static_cast<int>(cap) : load;
   }
+  int total;
+  const int off = block_excl_scan(cnt, tmp, &total);
+  if (tid < E) offs[tid] = off;
+  if (tid == 0) offs[E] = total;
+  if (blockIdx.x == 0) {
+    if (tid < E) {
+      expert_load[tid] = load;
+      expert_count[tid] = cnt;
+      expert_offset[tid] = off;
+    }
+    if (tid == 0) expert_offset[E] = total;
+  }
+  __syncthreads();
+  const int t = blockIdx.x * kFusedTokens + wave_id();
+  if (t >= T) return;
+  const int l = lane_id();
+  int row = -1;
+  if (l < k) {
+    const int64_t a = static_cast<int64_t>(t) * k + l;
+    const int e = idx[a];
+    const int r = (e >= 0 && e < E) ? tab[static_cast<int>(a / kPermuteBlock) * E + e] + rank[a] : -1;
+    if (r >= 0 && (cap < 0 || r < cap)) {
+      row = offs[e] + r;
+      row_token[row] = t;
+    }
+    slot_row[a] = row;
+  }
+  copy_row<CPL>(x, row_bytes, t, k, row, x_perm);
 }
 
 // ---------------------------------------------------------------- ExpertChoice
@@ -259,12 +333,34 @@ hipError_t launch_permute_topk(const PermuteArgs &a, hipStream_t st) {
   int ebits = 0;
   while ((1 << ebits) <= a.E) ++ebits;  // ids 0..E (E marks an empty lane)
   if (nblk > 0) count_kernel<<<nblk, kThreads, 0, st>>>(a.topk_idx, A, a.E, ebits, a.blk, a.rank);
+  const int per_lane = static_cast<int>((a.row_bytes / 16 + kWave - 1) / kWave);  // 16-B chunks per lane
+  const uint8_t *x = static_cast<const uint8_t *>(a.x);
+  uint8_t *xp = static_cast<uint8_t *>(a.x_perm);
+  if (a.T > 0 && static_cast<int64_t>(nblk) * a.E <= kFusedTable) {
+    const int blocks = (a.T + kFusedTokens - 1) / kFusedTokens;
+#define MOE_SCAN_SCATTER(CPL)                                                                                  \
+  scan_scatter_kernel<CPL><<<blocks, kFusedThreads, 0, st>>>(x, a.row_bytes, a.topk_idx, a.T, a.k, a.E, a.cap, \
+                                                             a.blk, nblk, a.rank, a.expert_count,              \
+                                                             a.expert_load, a.expert_offset, xp, a.row_token,  \
+                                                             a.slot_row)
+    if (per_lane <= 2) MOE_SCAN_SCATTER(2);
+    else if (per_lane <= 4) MOE_SCAN_SCATTER(4);
+    else MOE_SCAN_SCATTER(8);
+#undef MOE_SCAN_SCATTER
+    return hipGetLastError();
+  }
   scan_kernel<<<1, kScanThreads, 0, st>>>(a.blk, nblk, a.E, a.cap, a.expert_count, a.expert_load,
                                           a.expert_offset);
-  if (a.T > 0)
-    scatter_kernel<<<(a.T + kScatterTokens - 1) / kScatterTokens, kThreads, 0, st>>>(
-        static_cast<const uint8_t *>(a.x), a.row_bytes, a.topk_idx, a.T, a.k, a.E, a.cap, a.blk, a.rank,
-        a.expert_offset, static_cast<uint8_t *>(a.x_perm), a.row_token, a.slot_row);
+  if (a.T > 0) {
+    const int blocks = (a.T + kScatterTokens - 1) / kScatterTokens;
+#define MOE_SCATTER(CPL)                                                                                      \
+  scatter_kernel<CPL><<<blocks, kThreads, 0, st>>>(x, a.row_bytes, a.topk_idx, a.T, a.k, a.E, a.cap, a.blk,   \
+                                                   a.rank, a.expert_offset, xp, a.row_token, a.slot_row)
+    if (per_lane <= 2) MOE_SCATTER(2);
+    else if (per_lane <= 4) MOE_SCATTER(4);
+    else MOE_SCATTER(8);
+#undef MOE_SCATTER
+  }
   return hipGetLastError();
 }
 

@@ -44,9 +44,9 @@ def test_rows_capacity_and_workspace_sizes(name):
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     ffn = moe.expert_ffn_workspace_bytes(cfg)
     assert L["ffn_scratch_bytes"] >= ffn and L["ffn_scratch"] + L["ffn_scratch_bytes"] <= L["total"]
-    # only bf16 256-row GEMMs (>= 384 rows per expert on average) with a
+    # only bf16 256-row GEMMs (>= 192 rows per expert on average) with a
     # reduction length >= 8192 split their last round of tiles along K
-    if w.dtype == W.F32 or moe.max_rows(cfg) // w.E < 384 or max(w.d, w.d_ff) < 8192:
+    if w.dtype == W.F32 or moe.max_rows(cfg) // w.E < 192 or max(w.d, w.d_ff) < 8192:
         assert ffn == 0
     else:
         assert ffn == 256 * 256 * 256 * 4

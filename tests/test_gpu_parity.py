@@ -29,7 +29,7 @@ SMALL = {
     "mixtral_small": W.small_variant(WL["mixtral_top2_bf16"], T=1600, d=384, d_ff=520),
     "finegrained_small": W.small_variant(WL["finegrained_shared_bf16"], T=700, d=256, E=12, d_ff=136,
                                          d_ff_shared=264, wr_std=1.0 / 16.0),
-    # >= 384 rows per expert and a reduction length of 8192: the bf16
+    # >= 192 rows per expert and a reduction length of 8192: the bf16
     # 256 x 256 GEMM cuts its last round of tiles along K (8 pieces each) and
     # a second pass adds them: down projection (plain epilogue), up
     # projection with SwiGLU (gate and up pieces paired), up projection with
