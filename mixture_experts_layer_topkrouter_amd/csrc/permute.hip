@@ -277,19 +277,26 @@ __global__ __launch_bounds__(kThreads) void ec_count_kernel(const int32_t *__res
 
 constexpr int kPtrThreads = 1024;
 
-// In-place inclusive scan of tok_ptr[1..T] (single workgroup).
+// In-place inclusive scan of tok_ptr[1..T] (single workgroup).  The counts
+// pass through LDS so that global loads and stores are coalesced; each
+// thread scans a contiguous run there.
 __global__ __launch_bounds__(kPtrThreads) void ec_ptr_scan_kernel(int32_t *__restrict__ tok_ptr, int T) {
   __shared__ int tmp[kPtrThreads / kWave + 1];
+  __shared__ int vals[kEcMaxTokens];
+  for (int i = threadIdx.x; i < T; i += kPtrThreads) vals[i] = tok_ptr[i + 1];
+  __syncthreads();
   const int per = (T + kPtrThreads - 1) / kPtrThreads;
   const int b0 = min(T, static_cast<int>(threadIdx.x) * per), b1 = min(T, b0 + per);
   int s = 0;
-  for (int i = b0; i < b1; ++i) s += tok_ptr[i + 1];
+  for (int i = b0; i < b1; ++i) s += vals[i];
   int tot;
   int run = block_excl_scan(s, tmp, &tot);
   for (int i = b0; i < b1; ++i) {
-    run += tok_ptr[i + 1];
-    tok_ptr[i + 1] = run;
+    run += vals[i];
+    vals[i] = run;
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T; i += kPtrThreads) tok_ptr[i + 1] = vals[i];
 }
 
 // Per token: its rows and weights in ascending expert order.

@@ -9,9 +9,10 @@
 //
 // gfx950 design:
 // * logits: bf16 MFMA 16x16x32 with fp32 accumulation.  A block owns 16*MT
-//   tokens and all E (padded to 16*NT) experts; its four waves split the
-//   contraction over d by interleaved 32-wide steps and their partial tiles
-//   are summed in LDS in a fixed wave order, so results are deterministic.
+//   tokens and all E (padded to 16*NT) experts; its eight waves split the
+//   contraction over d by interleaved 32-wide steps, each with several steps
+//   of loads in flight, and their partial tiles are summed in LDS in a fixed
+//   wave order, so results are deterministic.
 //   The router weight is tiny and stays in L2; x is streamed once from HBM.
 // * the gate runs on the logits tile while it is still in LDS: one wave per
 //   token, lane l holds experts l, l+64, l+128, l+192; each of the k picks is a
@@ -141,14 +142,32 @@ __device__ void finish_logits(float *tile, int ld, int rows, int t0, int T, int 
   __syncthreads();
 }
 
+// Logits: 8 waves per block split the contraction over d by interleaved
+// 32-wide steps (wave w takes steps w, w+8, ...).  Each wave keeps D steps of
+// operand fragments in flight in a register ring (load step j+D, then
+// multiply step j), so a CU holds tens of KB of x loads in flight: enough to
+// stream x at HBM speed instead of waiting on one step at a time.
+constexpr int kRouteBf16Threads = 512;
+
 template <int MT, int NT>
-__global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
+__global__ __launch_bounds__(kRouteBf16Threads) void route_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, const float *__restrict__ bias,
     int64_t bias_stride, int T, int d, int E, int k, int routing, float *__restrict__ logits,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ scores) {
   constexpr int BT = 16 * MT, EP = 16 * NT;
-  __shared__ float tile[BT * EP];
-  const int l = lane_id(), w = wave_id();
+  constexpr int NW = kRouteBf16Threads / kWave;
+  // logits tile row pitch: 4 rows apart (the row groups of a 16x16 MFMA
+  // result) land 16 banks apart, so the tile write is conflict-free
+  constexpr int LD = EP + 4;
+  constexpr int RED = (NW / 2) * MT * NT * kWave;  // float4s of the reduction buffer
+  static_assert(BT * LD <= RED * 4 || RED == 0, "logits tile fits in the reduction buffer");
+  // steps in flight per wave: as many as fit next to the accumulators in
+  // about 192 registers (4 per fragment), at most 8
+  constexpr int D_FIT = (192 - 4 * MT * NT) / (4 * (MT + NT));
+  constexpr int D = D_FIT < 1 ? 1 : (D_FIT > 8 ? 8 : D_FIT);
+  __shared__ f32x4 red[RED];  // partial tiles, then the logits tile
+  float *tile = reinterpret_cast<float *>(red);
+  const int l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const int t0 = blockIdx.x * BT;
   f32x4 acc[MT][NT];
 #pragma unroll
@@ -157,45 +176,71 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
     for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ksteps = (d + 31) / 32;
+  const int nsteps = ksteps > w ? (ksteps - w + NW - 1) / NW : 0;  // this wave's steps
   const bf16x8 zero = {};
-#pragma unroll 2
-  for (int s = w; s < ksteps; s += 4) {
-    const int kk = s * 32 + (l >> 4) * 8;
-    const bool kin = kk < d;
-    bf16x8 a[MT], b[NT];
+  bf16x8 a[D][MT], b[D][NT];
+  // fragments of this wave's step j (zero past the end of d or of the rows)
+  auto load = [&](bf16x8 (&fa)[MT], bf16x8 (&fb)[NT], int j) {
+    const int kk = (w + j * NW) * 32 + (l >> 4) * 8;
+    const bool kin = j < nsteps && kk < d;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int row = t0 + m * 16 + (l & 15);
-      a[m] = (kin && row < T) ? *reinterpret_cast<const bf16x8 *>(x + (int64_t)row * d + kk) : zero;
+      fa[m] = (kin && row < T) ? *reinterpret_cast<const bf16x8 *>(x + (int64_t)row * d + kk) : zero;
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int e = n * 16 + (l & 15);
-      b[n] = (kin && e < E) ? *reinterpret_cast<const bf16x8 *>(wr + (int64_t)e * d + kk) : zero;
+      fb[n] = (kin && e < E) ? *reinterpret_cast<const bf16x8 *>(wr + (int64_t)e * d + kk) : zero;
     }
+  };
+#pragma unroll
+  for (int i = 0; i < D; ++i) load(a[i], b[i], i);
+  for (int j0 = 0; j0 < nsteps; j0 += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (j0 + i < nsteps) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][m], b[i][n], acc[m][n], 0, 0, 0);
+        load(a[i], b[i], j0 + i + D);
+      }
+    }
+  }
+  // Sum of the waves' partial tiles by a fixed tree (waves h..2h-1 hand
+  // theirs to waves 0..h-1, h = 4, 2, 1), so the result is deterministic.
+  // Partials travel in accumulator order: each lane moves whole float4s to
+  // consecutive addresses.
+#pragma unroll
+  for (int h = NW / 2; h >= 1; h >>= 1) {
+    if (w >= h && w < 2 * h) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) red[((w - h) * MT * NT + m * NT + n) * kWave + l] = acc[m][n];
+    }
+    __syncthreads();
+    if (w < h) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[m][n] += red[(w * MT * NT + m * NT + n) * kWave + l];
+    }
+    __syncthreads();
+  }
+  if (w == 0) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int n = 0; n < NT; ++n)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tile[(m * 16 + (l >> 4) * 4 + r) * LD + n * 16 + (l & 15)] = acc[m][n][r];
   }
-  // fixed-order sum of the four waves' partial tiles
-  for (int ww = 0; ww < kRouteThreads / kWave; ++ww) {
-    if (w == ww) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int id = (m * 16 + (l >> 4) * 4 + r) * EP + n * 16 + (l & 15);
-            tile[id] = (ww == 0 ? 0.f : tile[id]) + acc[m][n][r];
-          }
-    }
-    __syncthreads();
-  }
-  finish_logits(tile, EP, BT, t0, T, E, bias, bias_stride, logits);
-  gate_rows(tile, EP, BT, t0, T, E, k, routing, topk_idx, topk_w, scores);
+  __syncthreads();
+  finish_logits(tile, LD, BT, t0, T, E, bias, bias_stride, logits);
+  gate_rows(tile, LD, BT, t0, T, E, k, routing, topk_idx, topk_w, scores);
 }
 
 constexpr int kF32Rows = 16;
@@ -252,19 +297,50 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
     __syncthreads();
-    for (int t = threadIdx.x; t < T; t += blockDim.x) {
-      const uint32_t kv = key[t];
-      if ((kv & pmask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1);
+    // Softmax scores of one expert share their top bits, so most lanes hit
+    // the same bin: the lanes of a wave with equal bins are found with one
+    // ballot per bin bit and only the lowest of them adds the group's count.
+    for (int t0 = 0; t0 < T; t0 += blockDim.x) {
+      const int t = t0 + threadIdx.x;
+      const uint32_t kv = t < T ? key[t] : 0u;
+      const bool match = t < T && (kv & pmask) == prefix;
+      const uint32_t bin = (kv >> shift) & 255u;
+      uint64_t peers = __ballot(match);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const bool bit = (bin >> b) & 1u;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      if (match && (peers & lanemask_lt()) == 0) atomicAdd(&hist[bin], __popcll(peers));
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int cum = 0, b = 255;
-      for (; b > 0; --b) {
-        if (cum + hist[b] >= need) break;
-        cum += hist[b];
+    if (wave_id() == 0) {
+      // bins from the top: lane l holds bins 255-4l .. 252-4l; a suffix
+      // count over them finds the bin that holds the need-th largest key
+      const int l = lane_id();
+      int h[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = hist[255 - (4 * l + q)];
+        sum += h[q];
       }
-      sel_state[0] = static_cast<uint32_t>(b);
-      sel_state[1] = static_cast<uint32_t>(need - cum);
+      const int incl = wave_incl_scan(sum);
+      const int excl = incl - sum;
+      const uint64_t hit = __ballot(excl < need && need <= incl);
+      // every key matching the prefix is in some bin and at least `need` of
+      // them do, so one lane is hit; without a hit bin 0 is taken, as the
+      // sequential search did
+      const int src = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave - 1;
+      if (l == src) {
+        int cum = excl, q = 0;
+        for (; q < 3; ++q) {
+          if (cum + h[q] >= need) break;
+          cum += h[q];
+        }
+        sel_state[0] = static_cast<uint32_t>(255 - (4 * l + q));
+        sel_state[1] = static_cast<uint32_t>(need - cum);
+      }
     }
     __syncthreads();
     prefix |= sel_state[0] << shift;
@@ -322,6 +398,8 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
   } else {
     int nt = 1;
     while (nt * 16 < a.E) nt <<= 1;
+    // 16*mt tokens per block: larger token tiles re-read the router weight
+    // (all E rows, from L2) fewer times, as long as 256 blocks remain
     int mt = 1;
     if ((a.T + 63) / 64 >= 256 && nt <= 8) mt = 4;
     else if ((a.T + 31) / 32 >= 256 && nt <= 16) mt = 2;
@@ -330,7 +408,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
     const uint16_t *wr = static_cast<const uint16_t *>(a.wr);
 #define MOE_ROUTE_CASE(MT_, NT_)                                                                     \
   if (mt == MT_ && nt == NT_) {                                                                      \
-    route_bf16_kernel<MT_, NT_><<<blocks, kRouteThreads, 0, st>>>(x, wr, a.bias, a.bias_stride, a.T, \
+    route_bf16_kernel<MT_, NT_><<<blocks, kRouteBf16Threads, 0, st>>>(x, wr, a.bias, a.bias_stride, a.T, \
                                                                   a.d, a.E, a.k, a.routing,          \
                                                                   a.logits, a.topk_idx, a.topk_w,    \
                                                                   a.scores);                         \
