@@ -9,7 +9,10 @@ same order, as moe_layer_fwd) and records a HIP event between the stages, so
 each stage's average duration comes from the timed region itself.
 
 Prints one JSON line.  ``roofline`` reports the grouped expert FFN (the
-dominant stage: its two GEMM launches) against the bf16 MFMA peak;
+dominant stage: the kernels of one moe_expert_ffn call) against the bf16
+MFMA peak, or against HBM bandwidth when its flops per byte of expert
+weights and activations fall below the ridge (decode batches, few rows per
+expert);
 ``stages`` gives every stage's time and its algorithmic HBM rate or FLOP rate;
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
@@ -214,16 +217,29 @@ def main():
             ent["flops"] = int(work[n][1])
             if len(work[n]) > 2:
                 ent["min_bytes"] = int(work[n][2])
+                ent["GB/s"] = round(work[n][2] / sec / 1e9, 1)
+                ent["hbm_frac"] = round(work[n][2] / sec / 1e9 / PEAK_HBM_GBS, 4)
         stages[n] = ent
 
-    ffn_flops = work["expert_ffn"][1]
+    # The dominant kernel is the grouped expert FFN (every kernel of one
+    # moe_expert_ffn call).  Its bound follows from its arithmetic intensity:
+    # at or above the ridge (peak flops / peak bytes) the matrix core, below
+    # it the stream of expert weights from HBM.
+    ffn_flops, ffn_bytes = work["expert_ffn"][1], work["expert_ffn"][2]
     ffn_s = stage_ms["expert_ffn"] / 1e3
     peak = PEAK_BF16_TFLOPS if w.dtype == W.BF16 else PEAK_F32_TFLOPS
-    achieved = ffn_flops / ffn_s / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
-                "kernel": "grouped expert FFN: gemm_bf16_dma_kernel GEMM1 (SwiGLU) + GEMM2 + split_reduce_kernel, one moe_expert_ffn call",
-                "avg_ms": round(stage_ms["expert_ffn"], 4), "flops_per_launch": int(ffn_flops)}
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    common = {"traffic": measured_traffic(w.name), "kernel": "grouped expert FFN: every kernel of one moe_expert_ffn call",
+              "avg_ms": round(stage_ms["expert_ffn"], 4), "flops_per_launch": int(ffn_flops),
+              "bytes_per_launch": int(ffn_bytes), "intensity_flop_per_byte": round(ffn_flops / ffn_bytes, 1)}
+    if ffn_flops / ffn_bytes >= ridge:
+        achieved = ffn_flops / ffn_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), **common}
+    else:
+        achieved = ffn_bytes / ffn_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), **common}
 
     cpu = None
     parity = None

@@ -144,12 +144,15 @@ moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk
                        int32_t *expert_count, int32_t *expert_load, int32_t *expert_offset,
                        void *scratch, size_t scratch_bytes, void *stream);
 
-/* Bytes of device workspace moe_expert_ffn needs for this configuration.
- * A bf16 GEMM with at least 192 rows per expert on average and a reduction
- * length (d_model for the up projection, d_ff for the down projection) of at
- * least 8192 cuts the tiles of its last, partial round of workgroups along K
- * and keeps their fp32 partial tiles here: at most 256 tiles of 256 KiB
- * (64 MiB).  0 for every other configuration. */
+/* Bytes of device workspace moe_expert_ffn needs for this configuration:
+ * room for the fp32 partial tiles of GEMM tiles cut along K.
+ *   bf16, >= 192 rows per expert on average, and a reduction length (d_model
+ *   for the up projection, d_ff for the down projection) >= 8192: the tiles
+ *   of the last, partial round of workgroups are cut; 256 tiles of 256 KiB.
+ *   bf16, <= 128 rows per expert on average, K a multiple of 64: the
+ *   weight-streaming kernel cuts its tiles when there are too few to fill
+ *   the GPU; 512 tiles of 64 x 256 fp32: 32 MiB.
+ * The larger of the two applies; 0 for every other configuration. */
 moe_status moe_expert_ffn_workspace_bytes(const moe_config *cfg, size_t *bytes);
 
 /* --------------------------------------------------------------------------

@@ -38,155 +38,10 @@
 #include <algorithm>
 #include <atomic>
 
-#include "common.h"
-#include "kernels.h"
-
-// the direct-to-LDS loads name M0, which the compiler reserves (it uses M0
-// nowhere else in these kernels)
-#pragma clang diagnostic ignored "-Winline-asm"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int BK = 64;
-constexpr int BN = 256;  // B rows per tile
-constexpr int kGroupM = 8;  // most row tiles per group (see find_tile)
-
-enum { ACT_NONE = 0, ACT_GELU = 1, ACT_SWIGLU = 2 };
-
-struct GemmParams {
-  const void *A;
-  int64_t lda;  // A: [rows, K]
-  const void *B;
-  int64_t ldb, b_stride;  // B: per expert [Nb, K]
-  void *C;
-  int64_t ldc;  // C: [rows, n_out]
-  const int32_t *offs;
-  int E, K, n_out, up_off;
-  int64_t max_rows;
-  int m_tiles, n_tiles;
-  // bf16 256 x 256 kernel: `units` workgroups make one round (one per CU);
-  // K-split of the last, partial round needs max_split > 1 and room for the
-  // fp32 256 x 256 partial tiles of every piece (`slots` of them at part).
-  float *part;
-  int units, slots, max_split;
-};
-
-__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
-__device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
-
-// Block -> tile for the grouped GEMMs is done by every wave on its own (no
-// LDS): the grid is an upper bound on the tile count and the real count
-// follows from the device-side expert offsets.
-//
-// Rows of expert e, clamped to the buffer so a bad offset cannot address
-// outside it.
-__device__ __forceinline__ void expert_rows(const int32_t *__restrict__ offs, int e, int64_t max_rows, int *o0,
-                                            int *me) {
-  const int64_t a0 = min(max(static_cast<int64_t>(offs[e]), static_cast<int64_t>(0)), max_rows);
-  const int64_t a1 = min(max(static_cast<int64_t>(offs[e + 1]), a0), max_rows);
-  *o0 = static_cast<int>(a0);
-  *me = static_cast<int>(a1 - a0);
-}
-
-// Real row tiles over all experts (every lane gets the same count).
-template <int BM>
-__device__ __forceinline__ int count_mtiles(const int32_t *__restrict__ offs, int E, int64_t max_rows) {
-  const int l = lane_id();
-  int m_tiles = 0;
-  for (int e0 = 0; e0 < E; e0 += kWave) {
-    int o0 = 0, me = 0;
-    if (e0 + l < E) expert_rows(offs, e0 + l, max_rows, &o0, &me);
-    int t = (me + BM - 1) / BM;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
-    m_tiles += t;
-  }
-  // the same in every lane; readfirstlane lets the compiler treat everything
-  // derived from it (and the branches on it) as wave-uniform
-  return __builtin_amdgcn_readfirstlane(m_tiles);
-}
-
-// Block ids are dispatched to the 8 XCDs round-robin; this remaps id b of
-// [0, n) so that each XCD walks a contiguous run of tile indices.
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-  const int xcd = b & 7, slot = b >> 3;
-  const int per = n >> 3, rem = n & 7;
-  return xcd * per + min(xcd, rem) + slot;
-}
-
-// Tile index q -> (expert, rows, column tile).  Tiles are ordered expert by
-// expert; inside an expert its row tiles form groups of at most kGroupM (as
-// even as possible) and a group walks all column tiles with its row tiles
-// innermost, so neighbouring tiles share either their weight tile (same
-// expert, same column tile) or their rows.  Groups never straddle two
-// experts, whose weights differ.
-template <int BM>
-__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offs, int E, int64_t max_rows, int n_tiles,
-                                          int q, int *e_out, int *row0_out, int *rows_out, int *nt_out) {
-  const int l = lane_id();
-  int carry = 0, fe = -1, fo0 = 0, fme = 0, fexcl = 0, ftiles = 0;
-  for (int e0 = 0; e0 < E; e0 += kWave) {
-    const int e = e0 + l;
-    int o0 = 0, me = 0;
-    if (e < E) expert_rows(offs, e, max_rows, &o0, &me);
-    const int tiles = (me + BM - 1) / BM;
-    const int incl = wave_incl_scan(tiles) + carry;
-    const int excl = incl - tiles;
-    const uint64_t hit = __ballot(e < E && q >= excl * n_tiles && q < incl * n_tiles);
-    if (hit) {
-      const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-      fe = __shfl(e, src, kWave);
-      fo0 = __shfl(o0, src, kWave);
-      fme = __shfl(me, src, kWave);
-      fexcl = __shfl(excl, src, kWave);
-      ftiles = __shfl(tiles, src, kWave);
-      break;
-    }
-    carry = __shfl(incl, kWave - 1, kWave);
-  }
-  fe = __builtin_amdgcn_readfirstlane(fe);
-  if (fe < 0) return false;
-  fo0 = __builtin_amdgcn_readfirstlane(fo0);
-  fme = __builtin_amdgcn_readfirstlane(fme);
-  fexcl = __builtin_amdgcn_readfirstlane(fexcl);
-  ftiles = __builtin_amdgcn_readfirstlane(ftiles);
-  // ng groups: the first `big` hold base+1 row tiles, the others base
-  const int ql = q - fexcl * n_tiles;
-  const int ng = (ftiles + kGroupM - 1) / kGroupM;
-  const int base = ftiles / ng, big = ftiles - base * ng;
-  const int span_big = big * (base + 1) * n_tiles;
-  int m0, gsz, in_g;
-  if (ql < span_big) {
-    const int g = ql / ((base + 1) * n_tiles);
-    gsz = base + 1;
-    m0 = g * gsz;
-    in_g = ql - g * gsz * n_tiles;
-  } else {
-    const int g = (ql - span_big) / (base * n_tiles);
-    gsz = base;
-    m0 = big * (base + 1) + g * base;
-    in_g = ql - span_big - g * base * n_tiles;
-  }
-  const int lmt = m0 + in_g % gsz;
-  *nt_out = in_g / gsz;
-  *e_out = fe;
-  *row0_out = fo0 + lmt * BM;
-  *rows_out = min(BM, fme - lmt * BM);
-  return true;
-}
-
-// Block -> tile: one block per real tile, ids past the real count exit.
-template <int BM>
-__device__ __forceinline__ bool map_tile(const int32_t *__restrict__ offs, int E, int64_t max_rows, int n_tiles,
-                                         int *e_out, int *row0_out, int *rows_out, int *nt_out) {
-  const int m_tiles = count_mtiles<BM>(offs, E, max_rows);
-  const int total = m_tiles * n_tiles;
-  const int bid = blockIdx.x;
-  if (bid >= total) return false;
-  return find_tile<BM>(offs, E, max_rows, n_tiles, xcd_remap(bid, total), e_out, row0_out, rows_out, nt_out);
-}
 
 template <int BM, int ACT>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
@@ -411,39 +266,6 @@ __device__ __forceinline__ bool map_job(const GemmParams &p, int nk, Job *j) {
   }
   return find_tile<DBM>(p.offs, p.E, p.max_rows, p.n_tiles, q, &j->e, &j->row0, &j->rows, &j->nt);
 }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// 16 bytes per lane from global memory straight into LDS at
-// lds_addr + 16 * lane.  Written as inline asm so the compiler's wait-count
-// pass does not see it: that pass cannot always tell which ring slot an LDS
-// read touches and would then drain every load in flight before the read.
-// The kernel orders these loads itself (explicit vmcnt waits + barriers).
-// The instruction has no register result; M0 carries the LDS address and
-// needs one wait state after it is written.  The global address is a
-// wave-uniform base in SGPRs plus a 32-bit per-lane byte offset, so advancing
-// a stage is scalar arithmetic and each lane keeps one VGPR per load stream.
-__device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t lds_addr) {
-  // the LDS address is wave-uniform; readfirstlane puts it in an SGPR for M0
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0v)
-               : "memory", "m0");
-}
-
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)p));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-template <int S>
-struct Slot {
-  static constexpr int value = S;
-};
 
 // An empty asm "use" at the end of an iteration keeps that iteration's
 // fragment set live until then, so the register allocator cannot hand its
@@ -949,7 +771,12 @@ struct FfnPlan {
   int bm;
   bool dma1, dma2;      // GEMM1 / GEMM2 on the 256 x 256 direct-to-LDS kernel
   bool split1, split2;  // ... with enough K stages to split
+  int sk1, sk2;         // GEMM1 / GEMM2 on the skinny kernel with this tile height (0: not)
 };
+
+// Experts averaging at most this many rows run the skinny (weight-streaming)
+// kernel when K is a multiple of 64.
+constexpr int64_t kSkinnyMaxAvgRows = 128;
 
 FfnPlan plan_ffn(int dtype, int E, int d, int d_ff, int64_t max_rows) {
   FfnPlan f{};
@@ -959,6 +786,9 @@ FfnPlan plan_ffn(int dtype, int E, int d, int d_ff, int64_t max_rows) {
   f.dma2 = dtype == 1 && f.bm == 256 && d_ff % DK == 0;
   f.split1 = f.dma1 && d / DK >= kSplitMinStages;
   f.split2 = f.dma2 && d_ff / DK >= kSplitMinStages;
+  const int sk = 64;  // tile height (measured: 64 beats 32 even for decode batches)
+  f.sk1 = dtype == 1 && avg_rows <= kSkinnyMaxAvgRows && d % 64 == 0 ? sk : 0;
+  f.sk2 = dtype == 1 && avg_rows <= kSkinnyMaxAvgRows && d_ff % 64 == 0 ? sk : 0;
   return f;
 }
 
@@ -989,13 +819,18 @@ int round_units() {
 size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows) {
   if (max_rows == 0) return 0;
   const FfnPlan f = plan_ffn(dtype, E, d, d_ff, max_rows);
-  if (!f.split1 && !f.split2) return 0;
-  // the pieces of one round: at most kSplitUnits, and at most kMaxSplit per
-  // tile of the larger GEMM
-  const int64_t mt = mtile_bound(max_rows, E, DBM);
-  const int64_t nt = std::max<int64_t>((d_ff + BN / 2 - 1) / (BN / 2), (d + BN - 1) / BN);
-  const int64_t pieces = std::min<int64_t>(kSplitUnits, mt * nt * kMaxSplit);
-  return static_cast<size_t>(pieces) * kPartTileBytes;
+  size_t need = 0;
+  if (f.split1 || f.split2) {
+    // the pieces of one round: at most kSplitUnits, and at most kMaxSplit per
+    // tile of the larger GEMM
+    const int64_t mt = mtile_bound(max_rows, E, DBM);
+    const int64_t nt = std::max<int64_t>((d_ff + BN / 2 - 1) / (BN / 2), (d + BN - 1) / BN);
+    const int64_t pieces = std::min<int64_t>(kSplitUnits, mt * nt * kMaxSplit);
+    need = static_cast<size_t>(pieces) * kPartTileBytes;
+  }
+  const int sk = std::max(f.sk1, f.sk2);
+  if (sk) need = std::max(need, static_cast<size_t>(kSkinnyMaxPieces) * skinny_part_tile_bytes(sk));
+  return need;
 }
 
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
@@ -1007,6 +842,10 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   float *part = static_cast<float *>(a.scratch);
   const int units = round_units();
   const int slots = static_cast<int>(std::min<size_t>(kSplitUnits, need / kPartTileBytes));
+  const int sk_slots = std::max(f.sk1, f.sk2)
+                           ? static_cast<int>(std::min<size_t>(kSkinnyMaxPieces,
+                                                               need / skinny_part_tile_bytes(std::max(f.sk1, f.sk2))))
+                           : 0;
   GemmParams g1{};
   g1.A = a.x_perm;
   g1.lda = a.d;
@@ -1026,10 +865,18 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   g1.slots = slots;
   g1.max_split = f.split1 ? kMaxSplit : 1;
   const int act1 = a.act == 1 ? ACT_SWIGLU : ACT_GELU;
-  hipError_t err = a.dtype == 0  ? run_f32(g1, act1, st)
-                   : f.dma1      ? run_bf16_dma(g1, act1, st)
-                   : f.bm == 256 ? run_bf16<256>(g1, act1, st)
-                                 : run_bf16<128>(g1, act1, st);
+  hipError_t err;
+  if (a.dtype == 0) {
+    err = run_f32(g1, act1, st);
+  } else if (f.dma1) {
+    err = run_bf16_dma(g1, act1, st);
+  } else if (f.sk1) {
+    g1.slots = sk_slots;
+    g1.max_split = sk_slots > 0 ? kSkinnyMaxSplit : 1;
+    err = run_bf16_skinny(g1, act1, f.sk1, st);
+  } else {
+    err = f.bm == 256 ? run_bf16<256>(g1, act1, st) : run_bf16<128>(g1, act1, st);
+  }
   if (err != hipSuccess) return err;
   GemmParams g2{};
   g2.A = a.h;
@@ -1049,10 +896,14 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   g2.units = units;
   g2.slots = slots;
   g2.max_split = f.split2 ? kMaxSplit : 1;
-  return a.dtype == 0   ? run_f32(g2, ACT_NONE, st)
-         : f.dma2      ? run_bf16_dma(g2, ACT_NONE, st)
-         : f.bm == 256 ? run_bf16<256>(g2, ACT_NONE, st)
-                       : run_bf16<128>(g2, ACT_NONE, st);
+  if (a.dtype == 0) return run_f32(g2, ACT_NONE, st);
+  if (f.dma2) return run_bf16_dma(g2, ACT_NONE, st);
+  if (f.sk2) {
+    g2.slots = sk_slots;
+    g2.max_split = sk_slots > 0 ? kSkinnyMaxSplit : 1;
+    return run_bf16_skinny(g2, ACT_NONE, f.sk2, st);
+  }
+  return f.bm == 256 ? run_bf16<256>(g2, ACT_NONE, st) : run_bf16<128>(g2, ACT_NONE, st);
 }
 
 __global__ void fill_offsets_kernel(int32_t *dst, int32_t t) {

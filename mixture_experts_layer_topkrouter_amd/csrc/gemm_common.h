@@ -1,0 +1,203 @@
+// Internal to the grouped expert GEMM kernels (gemm.hip, gemm_skinny.hip):
+// their parameter block, activations, the device-side block -> tile mapping
+// and the direct-to-LDS load helpers.  Not part of the C ABI.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+// the direct-to-LDS loads name M0, which the compiler reserves (it uses M0
+// nowhere else in these kernels)
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace moe {
+
+constexpr int kThreads = 256;
+constexpr int BK = 64;
+constexpr int BN = 256;  // B rows per tile
+constexpr int kGroupM = 8;  // most row tiles per group (see find_tile)
+
+enum { ACT_NONE = 0, ACT_GELU = 1, ACT_SWIGLU = 2 };
+
+struct GemmParams {
+  const void *A;
+  int64_t lda;  // A: [rows, K]
+  const void *B;
+  int64_t ldb, b_stride;  // B: per expert [Nb, K]
+  void *C;
+  int64_t ldc;  // C: [rows, n_out]
+  const int32_t *offs;
+  int E, K, n_out, up_off;
+  int64_t max_rows;
+  int m_tiles, n_tiles;
+  // bf16 kernels: `units` workgroups make one round (one per CU); a K split
+  // needs max_split > 1 and room for the fp32 partial tiles of every piece
+  // (`slots` of them at part: 256 x 256 for the main kernel, bm x 256 for
+  // the skinny one).
+  float *part;
+  int units, slots, max_split;
+};
+
+namespace {
+
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
+
+// Block -> tile for the grouped GEMMs is done by every wave on its own (no
+// LDS): the grid is an upper bound on the tile count and the real count
+// follows from the device-side expert offsets.
+//
+// Rows of expert e, clamped to the buffer so a bad offset cannot address
+// outside it.
+__device__ __forceinline__ void expert_rows(const int32_t *__restrict__ offs, int e, int64_t max_rows, int *o0,
+                                            int *me) {
+  const int64_t a0 = min(max(static_cast<int64_t>(offs[e]), static_cast<int64_t>(0)), max_rows);
+  const int64_t a1 = min(max(static_cast<int64_t>(offs[e + 1]), a0), max_rows);
+  *o0 = static_cast<int>(a0);
+  *me = static_cast<int>(a1 - a0);
+}
+
+// Real row tiles over all experts (every lane gets the same count).
+template <int BM>
+__device__ __forceinline__ int count_mtiles(const int32_t *__restrict__ offs, int E, int64_t max_rows) {
+  const int l = lane_id();
+  int m_tiles = 0;
+  for (int e0 = 0; e0 < E; e0 += kWave) {
+    int o0 = 0, me = 0;
+    if (e0 + l < E) expert_rows(offs, e0 + l, max_rows, &o0, &me);
+    int t = (me + BM - 1) / BM;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
+    m_tiles += t;
+  }
+  // the same in every lane; readfirstlane lets the compiler treat everything
+  // derived from it (and the branches on it) as wave-uniform
+  return __builtin_amdgcn_readfirstlane(m_tiles);
+}
+
+// Block ids are dispatched to the 8 XCDs round-robin; this remaps id b of
+// [0, n) so that each XCD walks a contiguous run of tile indices.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return xcd * per + min(xcd, rem) + slot;
+}
+
+// Tile index q -> (expert, rows, column tile).  Tiles are ordered expert by
+// expert; inside an expert its row tiles form groups of at most kGroupM (as
+// even as possible) and a group walks all column tiles with its row tiles
+// innermost, so neighbouring tiles share either their weight tile (same
+// expert, same column tile) or their rows.  Groups never straddle two
+// experts, whose weights differ.
+template <int BM>
+__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offs, int E, int64_t max_rows, int n_tiles,
+                                          int q, int *e_out, int *row0_out, int *rows_out, int *nt_out) {
+  const int l = lane_id();
+  int carry = 0, fe = -1, fo0 = 0, fme = 0, fexcl = 0, ftiles = 0;
+  for (int e0 = 0; e0 < E; e0 += kWave) {
+    const int e = e0 + l;
+    int o0 = 0, me = 0;
+    if (e < E) expert_rows(offs, e, max_rows, &o0, &me);
+    const int tiles = (me + BM - 1) / BM;
+    const int incl = wave_incl_scan(tiles) + carry;
+    const int excl = incl - tiles;
+    const uint64_t hit = __ballot(e < E && q >= excl * n_tiles && q < incl * n_tiles);
+    if (hit) {
+      const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      fe = __shfl(e, src, kWave);
+      fo0 = __shfl(o0, src, kWave);
+      fme = __shfl(me, src, kWave);
+      fexcl = __shfl(excl, src, kWave);
+      ftiles = __shfl(tiles, src, kWave);
+      break;
+    }
+    carry = __shfl(incl, kWave - 1, kWave);
+  }
+  fe = __builtin_amdgcn_readfirstlane(fe);
+  if (fe < 0) return false;
+  fo0 = __builtin_amdgcn_readfirstlane(fo0);
+  fme = __builtin_amdgcn_readfirstlane(fme);
+  fexcl = __builtin_amdgcn_readfirstlane(fexcl);
+  ftiles = __builtin_amdgcn_readfirstlane(ftiles);
+  // ng groups: the first `big` hold base+1 row tiles, the others base
+  const int ql = q - fexcl * n_tiles;
+  const int ng = (ftiles + kGroupM - 1) / kGroupM;
+  const int base = ftiles / ng, big = ftiles - base * ng;
+  const int span_big = big * (base + 1) * n_tiles;
+  int m0, gsz, in_g;
+  if (ql < span_big) {
+    const int g = ql / ((base + 1) * n_tiles);
+    gsz = base + 1;
+    m0 = g * gsz;
+    in_g = ql - g * gsz * n_tiles;
+  } else {
+    const int g = (ql - span_big) / (base * n_tiles);
+    gsz = base;
+    m0 = big * (base + 1) + g * base;
+    in_g = ql - span_big - g * base * n_tiles;
+  }
+  const int lmt = m0 + in_g % gsz;
+  *nt_out = in_g / gsz;
+  *e_out = fe;
+  *row0_out = fo0 + lmt * BM;
+  *rows_out = min(BM, fme - lmt * BM);
+  return true;
+}
+
+// Block -> tile: one block per real tile, ids past the real count exit.
+template <int BM>
+__device__ __forceinline__ bool map_tile(const int32_t *__restrict__ offs, int E, int64_t max_rows, int n_tiles,
+                                         int *e_out, int *row0_out, int *rows_out, int *nt_out) {
+  const int m_tiles = count_mtiles<BM>(offs, E, max_rows);
+  const int total = m_tiles * n_tiles;
+  const int bid = blockIdx.x;
+  if (bid >= total) return false;
+  return find_tile<BM>(offs, E, max_rows, n_tiles, xcd_remap(bid, total), e_out, row0_out, rows_out, nt_out);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds_addr + 16 * lane.  Written as inline asm so the compiler's wait-count
+// pass does not see it: that pass cannot always tell which ring slot an LDS
+// read touches and would then drain every load in flight before the read.
+// The kernel orders these loads itself (explicit vmcnt waits + barriers).
+// The instruction has no register result; M0 carries the LDS address and
+// needs one wait state after it is written.  The global address is a
+// wave-uniform base in SGPRs plus a 32-bit per-lane byte offset, so advancing
+// a stage is scalar arithmetic and each lane keeps one VGPR per load stream.
+__device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  // the LDS address is wave-uniform; readfirstlane puts it in an SGPR for M0
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0v)
+               : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)p));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int S>
+struct Slot {
+  static constexpr int value = S;
+};
+
+}  // namespace
+
+// Small-row-count expert GEMMs (gemm_skinny.hip): bm = 64 rows per tile, K
+// a multiple of 64; p.part / p.slots / p.max_split as for the
+// 256-row kernel (slots counted in bm x 256 fp32 partial tiles).
+hipError_t run_bf16_skinny(GemmParams p, int act, int bm, hipStream_t st);
+// fp32 partial-tile bytes of one K piece of a bm-row skinny tile, and the
+// pieces a skinny GEMM splits into at most
+size_t skinny_part_tile_bytes(int bm);
+constexpr int kSkinnyMaxPieces = 512;
+constexpr int kSkinnyMaxSplit = 8;  // pieces per tile at most
+
+}  // namespace moe

@@ -10,7 +10,9 @@ structure of the five workloads:
 
 * tiny top-2 MoE, fp32: T=256, d=128, E=8, k=2, GELU d_ff=256, capacity 1.25
 * Mixtral-style slice, bf16: T=4096, d=4096, E=8, k=2, SwiGLU d_ff=14336,
-  dropless, softmax over the two chosen logits
+  dropless, softmax over the two chosen logits; and the same layer on a
+  decode batch of T=128 tokens (about 32 rows per expert: the expert
+  weights are streamed from HBM once per step)
 * fine-grained + shared expert, bf16: T=8192, d=2048, E=64, k=6, SwiGLU
   d_ff=1408, shared SwiGLU d_ff=2816, dropless; router std 1/sqrt(d) so the
   logits are about N(0,1)
@@ -91,6 +93,8 @@ WORKLOADS: Dict[str, Workload] = {
                                dtype=F32, routing=SOFTMAX_ALL, cf=1.25),
     "mixtral_top2_bf16": Workload("mixtral_top2_bf16", T=4096, d=4096, E=8, k=2, d_ff=14336,
                                   act=SWIGLU, dtype=BF16, routing=SOFTMAX_TOPK),
+    "mixtral_decode_bf16": Workload("mixtral_decode_bf16", T=128, d=4096, E=8, k=2, d_ff=14336,
+                                    act=SWIGLU, dtype=BF16, routing=SOFTMAX_TOPK),
     "finegrained_shared_bf16": Workload("finegrained_shared_bf16", T=8192, d=2048, E=64, k=6,
                                         d_ff=1408, act=SWIGLU, dtype=BF16, routing=SOFTMAX_ALL,
                                         d_ff_shared=2816, wr_std=1.0 / np.sqrt(2048.0)),

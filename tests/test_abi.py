@@ -44,12 +44,29 @@ def test_rows_capacity_and_workspace_sizes(name):
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     ffn = moe.expert_ffn_workspace_bytes(cfg)
     assert L["ffn_scratch_bytes"] >= ffn and L["ffn_scratch"] + L["ffn_scratch_bytes"] <= L["total"]
-    # only bf16 256-row GEMMs (>= 192 rows per expert on average) with a
-    # reduction length >= 8192 split their last round of tiles along K
-    if w.dtype == W.F32 or moe.max_rows(cfg) // w.E < 192 or max(w.d, w.d_ff) < 8192:
-        assert ffn == 0
-    else:
-        assert ffn == 256 * 256 * 256 * 4
+    assert ffn == expected_ffn_workspace(w.dtype, moe.max_rows(cfg) // w.E, w.d, w.d_ff)
+
+
+def expected_ffn_workspace(dtype, avg_rows, d, d_ff):
+    """K-split partial tiles: 256 of 256 x 256 fp32 for the 256-row kernel
+    (>= 192 rows per expert on average, a reduction length >= 8192); 512 of
+    64 x 256 fp32 for the weight-streaming kernel (<= 128 rows per expert on
+    average, K a multiple of 64)."""
+    if dtype == W.F32:
+        return 0
+    need = 0
+    if avg_rows >= 192 and max(d, d_ff) >= 8192:
+        need = 256 * 256 * 256 * 4
+    if avg_rows <= 128 and (d % 64 == 0 or d_ff % 64 == 0):
+        need = max(need, 512 * 64 * 256 * 4)
+    return need
+
+
+@pytest.mark.parametrize("T,d,E,k,d_ff", [(64, 512, 8, 2, 1024), (1200, 256, 16, 1, 512), (4096, 256, 8, 2, 8192),
+                                          (700, 264, 4, 2, 264), (16, 64, 4, 1, 64)])
+def test_ffn_workspace_rule(T, d, E, k, d_ff):
+    cfg = _cfg(num_tokens=T, d_model=d, num_experts=E, top_k=k, d_ff=d_ff)
+    assert moe.expert_ffn_workspace_bytes(cfg) == expected_ffn_workspace(W.BF16, T * k // E, d, d_ff)
 
 
 def _cfg(**kw):

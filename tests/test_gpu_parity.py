@@ -37,6 +37,12 @@ SMALL = {
     "ksplit_down_small": W.small_variant(WL["mixtral_top2_bf16"], T=400, d=256, E=2, d_ff=8192),
     "ksplit_up_swiglu_small": W.small_variant(WL["mixtral_top2_bf16"], T=400, d=8192, E=2, d_ff=256),
     "ksplit_up_gelu_small": W.small_variant(WL["switch_top1_bf16"], T=800, d=8192, E=2, d_ff=264, cf=0.0),
+    # few rows per expert (the weight-streaming kernel, 64-row tiles): GELU;
+    # decode-sized SwiGLU batches whose K is cut into pieces (2-4 and up to 8
+    # per tile) that a second pass adds
+    "skinny_gelu_small": W.small_variant(WL["switch_top1_bf16"], T=1200, d=256, E=16, d_ff=512, cf=0.0),
+    "skinny_decode_small": W.small_variant(WL["mixtral_top2_bf16"], T=64, d=512, E=8, d_ff=1024),
+    "skinny_decode_longk_small": W.small_variant(WL["mixtral_top2_bf16"], T=32, d=256, E=4, d_ff=4096),
     "switch_small": W.small_variant(WL["switch_top1_bf16"], T=2000, d=192, E=16, d_ff=328),
     "correlated_small": W.small_variant(WL["correlated_top2_bf16"], T=1500, d=256, E=16, d_ff=200),
     "correlated_ec_small": W.small_variant(WL["correlated_ec_bf16"], T=1500, d=256, E=16, d_ff=200,
@@ -61,8 +67,8 @@ def test_layer_parity_small(name):
         check_output_topk(w, layer, inp, lg, toks)
 
 
-FULL = ["tiny_top2_fp32", "mixtral_top2_bf16", "finegrained_shared_bf16", "switch_top1_bf16",
-        "correlated_top2_bf16", "correlated_ec_bf16"]
+FULL = ["tiny_top2_fp32", "mixtral_top2_bf16", "mixtral_decode_bf16", "finegrained_shared_bf16",
+        "switch_top1_bf16", "correlated_top2_bf16", "correlated_ec_bf16"]
 
 
 @pytest.mark.gpu
@@ -220,6 +226,19 @@ def test_k_split_tiles_deterministic_bitwise():
         layer.forward()
         torch.cuda.synchronize()
         assert torch.equal(h1.view(torch.int16), layer.view("h").view(torch.int16))
+        assert torch.equal(y1.view(torch.int16), layer.y.view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_skinny_split_deterministic_bitwise():
+    """The weight-streaming kernel's K pieces are added in piece order:
+    repeated runs give identical bits."""
+    w = SMALL["skinny_decode_longk_small"]
+    layer, _ = run_layer(w)
+    y1 = layer.y.clone()
+    for _ in range(3):
+        layer.forward()
+        torch.cuda.synchronize()
         assert torch.equal(y1.view(torch.int16), layer.y.view(torch.int16))
 
 
