@@ -203,7 +203,8 @@ typedef struct {
   size_t x_perm, row_token, slot_row, slot_w, tok_ptr;
   size_t expert_count, expert_load, expert_offset, shared_offset;
   size_t h, y_perm, shared_h, shared_y, scratch, scratch_bytes;
-  size_t ffn_scratch, ffn_scratch_bytes; /* moe_expert_ffn workspace */
+  size_t ffn_scratch, ffn_scratch_bytes;               /* moe_expert_ffn workspace */
+  size_t shared_ffn_scratch, shared_ffn_scratch_bytes; /* ... of the shared expert */
   size_t total; /* bytes the workspace must hold */
 } moe_workspace_layout;
 
@@ -212,8 +213,12 @@ moe_status moe_layer_workspace(const moe_config *cfg, moe_workspace_layout *layo
 /* --------------------------------------------------------------------------
  * moe_layer_fwd -- the whole MoE block forward ([P1] "Core MoE Layer
  * Architecture": MoELayer / MoELayerExpertChoice): route, permute, routed
- * experts, shared expert (when d_ff_shared > 0, weight 1), unpermute; one
- * stream, no host synchronisation.
+ * experts, shared expert (when d_ff_shared > 0, weight 1), unpermute; no
+ * host synchronisation.  The shared expert reads only x, so it runs on a
+ * side stream beside the rest (forked from `stream` at the start, joined
+ * back before the combine; P1's shared-expert overlap): the call is
+ * asynchronous on `stream` as a whole.  The side stream and its two events
+ * are created once per device and host thread and kept.
  *   x [T,d], w_router [E,d], logit_bias as in moe_route, w1/w2 as in
  *   moe_expert_ffn, ws1 [n_up*d_ff_shared, d] / ws2 [d, d_ff_shared] (NULL
  *   when d_ff_shared == 0), y [T,d] output.

@@ -1,6 +1,8 @@
 // C ABI entry points (include/moe.h): host-side validation, workspace
 // layout and the enqueue sequence of the forward pass.  Every check runs
-// before anything is enqueued; nothing here allocates, frees or waits.
+// before anything is enqueued; nothing here allocates device memory, frees
+// or waits on the host (moe_layer_fwd with a shared expert creates one side
+// stream and two events per device and host thread, once).
 #include <math.h>
 #include <string.h>
 
@@ -214,6 +216,29 @@ moe_status unpermute_impl(const moe_config *cfg, const void *y_perm, const int32
   return hip_status(moe::launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 
+// One side stream (default priority) and its fork / join events per device
+// and host thread, created on first use and kept for the life of the
+// process.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+SideStream *side_stream() {
+  constexpr int kMaxDevices = 64;
+  thread_local SideStream per_device[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream &s = per_device[dev];
+  if (!s.stream) {
+    if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+  }
+  return &s;
+}
+
 moe_config shared_config(const moe_config *cfg) {
   moe_config s = *cfg;
   s.num_experts = 1;
@@ -262,16 +287,15 @@ void make_layout(const moe_config *c, moe_workspace_layout *L) {
   L->shared_y = take(c->d_ff_shared ? T * d * s : 0);
   L->scratch_bytes = ec ? 0 : moe::permute_scratch_bytes(c->num_tokens, c->top_k, c->num_experts);
   L->scratch = take(L->scratch_bytes);
-  // the routed and the shared expert FFN run one after the other on the
-  // stream, so they share one scratch region
-  size_t ffn = ffn_scratch_of(c);
+  // the shared expert FFN runs beside the routed one (side stream), so each
+  // has its own scratch region
+  L->ffn_scratch_bytes = ffn_scratch_of(c);
+  L->ffn_scratch = take(L->ffn_scratch_bytes);
   if (c->d_ff_shared) {
     const moe_config sc = shared_config(c);
-    const size_t sh = ffn_scratch_of(&sc);
-    if (sh > ffn) ffn = sh;
+    L->shared_ffn_scratch_bytes = ffn_scratch_of(&sc);
   }
-  L->ffn_scratch_bytes = ffn;
-  L->ffn_scratch = take(ffn);
+  L->shared_ffn_scratch = take(L->shared_ffn_scratch_bytes);
   L->total = off;
 }
 
@@ -279,7 +303,7 @@ void make_layout(const moe_config *c, moe_workspace_layout *L) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 const char *moe_status_string(moe_status s) {
   switch (s) {
@@ -398,6 +422,28 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
   int32_t *tok_ptr = static_cast<int32_t *>(P(L.tok_ptr));
   int32_t *expert_offset = static_cast<int32_t *>(P(L.expert_offset));
 
+  // Shared expert ([P3] top_k paragraph; overlapped as P1's shared-expert
+  // overlap): it reads only x, so it is forked onto a side stream right away
+  // and runs beside routing, permutation and the routed experts; the main
+  // stream waits for it just before the combine.
+  hipStream_t main_st = static_cast<hipStream_t>(stream);
+  const void *y_shared = nullptr;
+  hipEvent_t join = nullptr;
+  if (cfg->d_ff_shared > 0) {
+    SideStream *side = side_stream();
+    if (!side) return MOE_ERR_HIP;
+    if (hipEventRecord(side->fork, main_st) != hipSuccess ||
+        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+      return MOE_ERR_HIP;
+    int32_t *so = static_cast<int32_t *>(P(L.shared_offset));
+    if (moe::launch_fill_offsets(so, cfg->num_tokens, side->stream) != hipSuccess) return MOE_ERR_HIP;
+    s = ffn_impl(&sc, x, so, ws1, ws2, P(L.shared_h), P(L.shared_y), P(L.shared_ffn_scratch),
+                 L.shared_ffn_scratch_bytes, side->stream);
+    if (s != MOE_OK) return s;
+    if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_ERR_HIP;
+    join = side->join;
+    y_shared = P(L.shared_y);
+  }
   s = route_impl(cfg, x, w_router, logit_bias, bias_row_stride, logits, topk_idx, topk_w, scores, ec_token, ec_w,
                  stream);
   if (s != MOE_OK) return s;
@@ -408,16 +454,7 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
   s = ffn_impl(cfg, P(L.x_perm), expert_offset, w1, w2, P(L.h), P(L.y_perm), P(L.ffn_scratch),
                L.ffn_scratch_bytes, stream);
   if (s != MOE_OK) return s;
-  const void *y_shared = nullptr;
-  if (cfg->d_ff_shared > 0) {
-    int32_t *so = static_cast<int32_t *>(P(L.shared_offset));
-    if (moe::launch_fill_offsets(so, cfg->num_tokens, static_cast<hipStream_t>(stream)) != hipSuccess)
-      return MOE_ERR_HIP;
-    s = ffn_impl(&sc, x, so, ws1, ws2, P(L.shared_h), P(L.shared_y), P(L.ffn_scratch), L.ffn_scratch_bytes,
-                 stream);
-    if (s != MOE_OK) return s;
-    y_shared = P(L.shared_y);
-  }
+  if (join && hipStreamWaitEvent(main_st, join, 0) != hipSuccess) return MOE_ERR_HIP;
   return unpermute_impl(cfg, P(L.y_perm), tok_ptr, slot_row, slot_w, y_shared, y, stream);
 }
 

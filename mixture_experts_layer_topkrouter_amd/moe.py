@@ -55,7 +55,7 @@ class MoeConfig(ctypes.Structure):
 _LAYOUT_FIELDS = ["logits", "topk_idx", "topk_w", "scores", "ec_token", "ec_w", "x_perm", "row_token",
                   "slot_row", "slot_w", "tok_ptr", "expert_count", "expert_load", "expert_offset",
                   "shared_offset", "h", "y_perm", "shared_h", "shared_y", "scratch", "scratch_bytes",
-                  "ffn_scratch", "ffn_scratch_bytes", "total"]
+                  "ffn_scratch", "ffn_scratch_bytes", "shared_ffn_scratch", "shared_ffn_scratch_bytes", "total"]
 
 
 class WorkspaceLayout(ctypes.Structure):

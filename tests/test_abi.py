@@ -21,7 +21,7 @@ def test_library_exports_every_header_symbol():
 
 def test_status_strings_and_version():
     lib = moe.load_library()
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
 
