@@ -75,18 +75,28 @@ def algorithmic(w, n_rows: int, n_active: int):
 def measured_traffic(workload: str):
     """HBM bytes per expert-FFN launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs (scaled by a plain-copy calibration), or None when no such
-    measurement exists or the GEMM source has changed since it was taken."""
-    import hashlib
+    measurement exists or the GEMM sources have changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_ffn_traffic.json")
-    src = os.path.join(ROOT, "mixture_experts_layer_topkrouter_amd", "csrc", "gemm.hip")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec.get("gemm_source_sha256"):
-            return None
+    if gemm_sources_sha256() != rec.get("gemm_source_sha256"):
+        return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+GEMM_SOURCES = ("gemm_common.h", "gemm.hip", "gemm_skinny.hip")
+
+
+def gemm_sources_sha256() -> str:
+    """One hash over the grouped-GEMM sources, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_topkrouter_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def main():
