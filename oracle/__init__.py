@@ -1,4 +1,5 @@
-"""Python handle on the fp64 CPU oracle (``oracle/moe_oracle.c``).
+"""Python handle on the fp64 CPU oracle (``oracle/moe_oracle.c``): forward and
+backward pass.
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the tests, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py`` may import this package.  It never
@@ -66,6 +67,14 @@ def _load():
     lib.orc_ffn_row.argtypes = [i32, i32, i32, i32, P, i64, P, i64, P, i64, P]
     lib.orc_moe_rows_topk.argtypes = [i32] * 7 + [P] * 8 + [i32, P, P]
     lib.orc_moe_rows_ec.argtypes = [i32] * 8 + [P] * 7 + [i32, P, P]
+    lib.orc_ffn_row_bwd.argtypes = [i32, i32, i32, i32, P, i64, P, i64, P, i64, P, P, P, P, P]
+    lib.orc_gate_bwd_topk.argtypes = [i32, i32, i32, i32, P, P, P, P]
+    lib.orc_gate_bwd_ec.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.orc_moe_bwd_topk.argtypes = [i32] * 9 + [P] * 18
+    lib.orc_moe_bwd_ec.argtypes = [i32] * 8 + [P] * 17
+    lib.orc_moe_bwd_tokens_topk.argtypes = [i32] * 8 + [P] * 10 + [i32] + [P] * 4
+    lib.orc_moe_bwd_tokens_ec.argtypes = [i32] * 7 + [P] * 9 + [i32] + [P] * 4
+    lib.orc_ffn_dw_elems.argtypes = [i32] * 4 + [P] * 4 + [i32, P, P, i32, i32, P, P, P]
     _lib = lib
     return lib
 
@@ -263,3 +272,140 @@ def layer(x, wr, w1, w2, *, k: int, routing: int, act: int, cf: float = 0.0, ec_
     res.dispatch = dispatch_topk(res.idx, E, capacity(cf, T, k, E))
     res.y = moe_rows_topk(x, res.idx, res.w, res.dispatch.slot_row, w1, w2, act, res.toks, ws1, ws2)
     return res
+
+
+# ---------------------------------------------------------------------------
+# Backward pass ("Activation Checkpointing and Constraints": the layer is
+# trained and its forward is re-run inside the backward).  The choice of
+# experts is held fixed; gradients flow through the gate weights, the expert
+# FFNs and the router's linear layer.
+# ---------------------------------------------------------------------------
+
+def ffn_row_bwd(x_row, w1_e, w2_e, act: int, g):
+    """Backward of one expert FFN on one row: (dW1, dW2, dx, out)."""
+    x_row, w1_e, w2_e = _c(x_row), _c(w1_e), _c(w2_e)
+    g = _c(g, np.float64)
+    d = x_row.shape[-1]
+    dff = w2_e.shape[-1]
+    n_up = 2 if act == SWIGLU else 1
+    dw1 = np.zeros((n_up * dff, d))
+    dw2 = np.zeros((d, dff))
+    dx = np.zeros(d)
+    out = np.empty(d)
+    _load().orc_ffn_row_bwd(d, dff, act, _dt(x_row), _ptr(x_row), 0, _ptr(w1_e), 0, _ptr(w2_e), 0,
+                            _ptr(g), _ptr(dw1), _ptr(dw2), _ptr(dx), _ptr(out))
+    return dw1, dw2, dx, out
+
+
+def gate_bwd_topk(lg, idx, dw, mode: int) -> np.ndarray:
+    """dL/dlogits from dL/d(gate weight), the expert choice held fixed."""
+    lg, idx, dw = _c(lg, np.float64), _c(idx, np.int32), _c(dw, np.float64)
+    T, E = lg.shape
+    k = idx.shape[1]
+    out = np.empty((T, E))
+    _load().orc_gate_bwd_topk(T, E, k, mode, _ptr(lg), _ptr(idx), _ptr(dw), _ptr(out))
+    return out
+
+
+def gate_bwd_ec(lg, ec_token, dw_ec) -> np.ndarray:
+    lg, ec_token, dw_ec = _c(lg, np.float64), _c(ec_token, np.int32), _c(dw_ec, np.float64)
+    T, E = lg.shape
+    C = ec_token.shape[1]
+    out = np.empty((T, E))
+    _load().orc_gate_bwd_ec(T, E, C, _ptr(lg), _ptr(ec_token), _ptr(dw_ec), _ptr(out))
+    return out
+
+
+@dataclass
+class Grads:
+    dx: np.ndarray
+    dwr: np.ndarray
+    dlogits: np.ndarray
+    dw1: np.ndarray
+    dw2: np.ndarray
+    dws1: Optional[np.ndarray]
+    dws2: Optional[np.ndarray]
+    d_slot_w: np.ndarray  # top-k: [T,k]; ExpertChoice: [E,C]
+
+
+def layer_bwd(x, wr, w1, w2, dy, fwd: LayerResult, *, k: int, routing: int, act: int,
+              ws1=None, ws2=None) -> Grads:
+    """Every gradient of the layer for upstream gradient dy [T,d], given the
+    routing of a forward pass (``layer()``), serial fp64: small problems."""
+    x, wr, w1, w2, dy = _c(x), _c(wr), _c(w1), _c(w2), _c(dy)
+    T, d = x.shape
+    E = wr.shape[0]
+    dff = w2.shape[-1]
+    n_up = 2 if act == SWIGLU else 1
+    dffs = 0 if ws2 is None else ws2.shape[-1]
+    ws1 = None if ws1 is None else _c(ws1)
+    ws2 = None if ws2 is None else _c(ws2)
+    lg = _c(fwd.logits, np.float64)
+    g = Grads(dx=np.empty((T, d)), dwr=np.empty((E, d)), dlogits=np.empty((T, E)),
+              dw1=np.empty((E, n_up * dff, d)), dw2=np.empty((E, d, dff)),
+              dws1=np.empty((n_up * dffs, d)) if dffs else None,
+              dws2=np.empty((d, dffs)) if dffs else None, d_slot_w=None)
+    lib = _load()
+    if routing == EXPERT_CHOICE:
+        C = fwd.ec_token.shape[1]
+        g.d_slot_w = np.empty((E, C))
+        lib.orc_moe_bwd_ec(T, d, E, C, dff, dffs, act, _dt(x), _ptr(x), _ptr(wr), _ptr(lg),
+                           _ptr(_c(fwd.ec_token, np.int32)), _ptr(w1), _ptr(w2), _ptr(ws1), _ptr(ws2),
+                           _ptr(dy), _ptr(g.dx), _ptr(g.dwr), _ptr(g.dlogits), _ptr(g.dw1), _ptr(g.dw2),
+                           _ptr(g.dws1), _ptr(g.dws2), _ptr(g.d_slot_w))
+    else:
+        g.d_slot_w = np.empty((T, k))
+        lib.orc_moe_bwd_topk(T, d, E, k, dff, dffs, act, _dt(x), routing, _ptr(x), _ptr(wr), _ptr(lg),
+                             _ptr(_c(fwd.idx, np.int32)), _ptr(_c(fwd.dispatch.slot_row, np.int32)),
+                             _ptr(w1), _ptr(w2), _ptr(ws1), _ptr(ws2), _ptr(dy), _ptr(g.dx), _ptr(g.dwr),
+                             _ptr(g.dlogits), _ptr(g.dw1), _ptr(g.dw2), _ptr(g.dws1), _ptr(g.dws2),
+                             _ptr(g.d_slot_w))
+    return g
+
+
+def layer_bwd_tokens(x, wr, w1, w2, dy, fwd: LayerResult, toks, *, k: int, routing: int, act: int,
+                     ws1=None, ws2=None):
+    """dx, dlogits and dL/d(gate weight) for the listed tokens only (sampled
+    checks of large problems).  ExpertChoice: the weight gradients come as
+    [ntok, E] (0 where the expert did not choose the token)."""
+    x, wr, w1, w2, dy = _c(x), _c(wr), _c(w1), _c(w2), _c(dy)
+    toks = _c(toks, np.int32)
+    T, d = x.shape
+    E = wr.shape[0]
+    dff = w2.shape[-1]
+    dffs = 0 if ws2 is None else ws2.shape[-1]
+    ws1 = None if ws1 is None else _c(ws1)
+    ws2 = None if ws2 is None else _c(ws2)
+    lg = _c(fwd.logits, np.float64)
+    n = len(toks)
+    dx = np.empty((n, d))
+    dl = np.empty((n, E))
+    lib = _load()
+    if routing == EXPERT_CHOICE:
+        C = fwd.ec_token.shape[1]
+        dw = np.empty((n, E))
+        lib.orc_moe_bwd_tokens_ec(d, E, C, dff, dffs, act, _dt(x), _ptr(x), _ptr(wr), _ptr(lg),
+                                  _ptr(_c(fwd.ec_token, np.int32)), _ptr(w1), _ptr(w2), _ptr(ws1),
+                                  _ptr(ws2), _ptr(dy), n, _ptr(toks), _ptr(dx), _ptr(dl), _ptr(dw))
+    else:
+        dw = np.empty((n, k))
+        lib.orc_moe_bwd_tokens_topk(d, E, k, dff, dffs, act, _dt(x), routing, _ptr(x), _ptr(wr),
+                                    _ptr(lg), _ptr(_c(fwd.idx, np.int32)),
+                                    _ptr(_c(fwd.dispatch.slot_row, np.int32)), _ptr(w1), _ptr(w2),
+                                    _ptr(ws1), _ptr(ws2), _ptr(dy), n, _ptr(toks), _ptr(dx), _ptr(dl),
+                                    _ptr(dw))
+    return dx, dl, dw
+
+
+def ffn_dw_elems(x, dy, w1_e, w2_e, row_tok, row_w, act: int, which: int, rr, cc) -> np.ndarray:
+    """Sampled elements of one expert's weight gradients (which 1: dW1[rr,cc],
+    2: dW2[rr,cc]) over its rows row_tok with gate weights row_w."""
+    x, dy, w1_e, w2_e = _c(x), _c(dy), _c(w1_e), _c(w2_e)
+    row_tok, row_w = _c(row_tok, np.int32), _c(row_w, np.float64)
+    rr, cc = _c(rr, np.int32), _c(cc, np.int32)
+    d = x.shape[1]
+    dff = w2_e.shape[-1]
+    out = np.empty(len(rr))
+    _load().orc_ffn_dw_elems(d, dff, act, _dt(x), _ptr(x), _ptr(dy), _ptr(w1_e), _ptr(w2_e), len(row_tok),
+                             _ptr(row_tok), _ptr(row_w), which, len(rr), _ptr(rr), _ptr(cc), _ptr(out))
+    return out
