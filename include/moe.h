@@ -1,6 +1,6 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) forward pass of one Mixture-of-Experts
- * block on one GPU's share of tokens and its local experts.
+ * moe.h -- C ABI of the MI355X (gfx950) forward and backward passes of one
+ * Mixture-of-Experts block on one GPU's share of tokens and its local experts.
  *
  * The operations follow two pages:
  *   [P1] "How MegaDLMs Implements Mixture of Experts (MoE) Architectures"
@@ -229,6 +229,67 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
                          const void *w2, const void *ws1, const void *ws2, void *y,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* --------------------------------------------------------------------------
+ * Backward pass ([P1] "Activation Checkpointing and Constraints": the layer
+ * is trained, and its recompute mode re-runs the forward inside the backward
+ * pass).  moe_layer_bwd differentiates moe_layer_fwd for an upstream
+ * gradient dy = dL/dy, re-running the expert GEMM1 (the pre-activations are
+ * recomputed, not kept).  The choice of experts (top-k, ExpertChoice
+ * selection, capacity drops) is held fixed: it is piecewise constant in the
+ * logits.  Gradients flow through
+ *   - the gate weights ([P1] "Routing Mechanisms": softmax over the logits):
+ *     SOFTMAX_ALL  dl_e = p_e (g_e - sum_i p_i g_i), g_e = dL/dw of the slot
+ *                  that chose e (p = softmax of the logits);
+ *     SOFTMAX_TOPK dl[idx_j] = w_j (dL/dw_j - sum_i w_i dL/dw_i), others 0;
+ *     ExpertChoice dl_e = S_e (g_e - sum_i S_i g_i), S = the scores;
+ *     with dL/dw of a kept slot = <dy[t], y_perm[row]> and 0 when dropped;
+ *   - the expert FFNs (GELU / SwiGLU as in moe_expert_ffn), the shared
+ *     expert (weight 1) and the router's linear layer logits = x W_r^T.
+ *
+ * Layout of the backward workspace.  Routed rows keep the forward's
+ * expert-major order, but expert e's block starts at poff[e], a multiple of
+ * 32 (pad rows are zero), so every weight-gradient contraction covers whole
+ * 32-row stages.  Offsets are bytes from the workspace start; rows of the
+ * row buffers = padded_rows (moe_max_rows() + 31 * E); shared-expert buffers
+ * have shared_rows = T rounded up to 32 rows.
+ *   poff [E+1] int32        slot_prow [slots] int32 (padded row or -1)
+ *   d_slot_w [slots] fp32   dL/dw per slot (top-k [T,k]; ExpertChoice the
+ *                           CSR order of moe_permute)
+ *   dlogits [T,E] fp32      dL/dlogits; the gradient of a logit bias is its
+ *                           sum over tokens ([E] bias) or dlogits itself
+ *   dx_router [T,d] fp32    dlogits W_r
+ *   xp, dyp, dxp [padded_rows, d]   expert inputs, output gradients (w dy),
+ *                           input gradients
+ *   z [padded_rows, n_up*d_ff]      pre-activations, then dL/dz
+ *   dh [padded_rows, d_ff]          dL/dh, then the recomputed h
+ *   xs, dys, dxs, zs, dhs   the same for the shared expert
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  size_t poff, slot_prow, d_slot_w, dlogits, dx_router, router_offset;
+  size_t xp, dyp, z, dh, dxp;
+  size_t shared_offset, xs, dys, zs, dhs, dxs;
+  size_t scratch, scratch_bytes, shared_scratch, shared_scratch_bytes;
+  size_t padded_rows, shared_rows; /* row counts, not bytes */
+  size_t total;                    /* bytes the workspace must hold */
+} moe_bwd_layout;
+moe_status moe_layer_bwd_workspace(const moe_config *cfg, moe_bwd_layout *layout);
+/* moe_layer_bwd -- gradients of the whole block.
+ *   x, w_router, w1, w2, ws1, ws2: as given to moe_layer_fwd.
+ *   fwd_workspace: the workspace of a moe_layer_fwd call on the same inputs
+ *     (its routing, permutation and y_perm are read; nothing is written).
+ *   dy [T,d] dtype: dL/dy.
+ *   Outputs (dtype, overwritten): dx [T,d], dw_router [E,d],
+ *     dw1 [E, n_up*d_ff, d], dw2 [E, d, d_ff], dws1 / dws2 (shared expert,
+ *     NULL when d_ff_shared == 0).  T = 0 writes zero weight gradients.
+ *   workspace: moe_layer_bwd_workspace().total bytes, 256-B aligned.
+ * The shared expert's backward runs on the side stream of moe_layer_fwd
+ * beside the routed part and is joined before dx is assembled.  Results are
+ * deterministic. */
+moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_router, const void *w1,
+                         const void *w2, const void *ws1, const void *ws2, const void *fwd_workspace,
+                         size_t fwd_workspace_bytes, const void *dy, void *dx, void *dw_router, void *dw1,
+                         void *dw2, void *dws1, void *dws2, void *workspace, size_t workspace_bytes,
+                         void *stream);
 const char *moe_status_string(moe_status s);
 int32_t moe_abi_version(void);
 

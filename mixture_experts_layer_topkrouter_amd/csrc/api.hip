@@ -6,6 +6,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -299,11 +301,172 @@ void make_layout(const moe_config *c, moe_workspace_layout *L) {
   L->total = off;
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass: layout of its workspace.
+int64_t padded_rows_of(const moe_config *c) {
+  return max_rows_of(c) + static_cast<int64_t>(moe::kPadRows - 1) * c->num_experts;
+}
+
+int64_t round_rows(int64_t v) { return (v + moe::kPadRows - 1) / moe::kPadRows * moe::kPadRows; }
+
+moe::BwdGemm bwd_gemm(const moe_config *c, int kind) {
+  moe::BwdGemm g{};
+  g.kind = kind;
+  g.dtype = c->dtype;
+  return g;
+}
+
+// The grouped GEMMs of one expert set's backward (routed: E experts over
+// padded rows; shared: one expert over T rounded up): their split scratch.
+size_t ffn_bwd_scratch(const moe_config *c, int E, int64_t rows, int dff) {
+  const int n_up = c->act == MOE_ACT_SWIGLU ? 2 : 1, d = c->d_model;
+  size_t need = 0;
+  moe::BwdGemm g = bwd_gemm(c, moe::BWD_NT);
+  g.E = E;
+  g.max_rows = rows;
+  g.N = n_up * dff;
+  g.K = d;
+  need = std::max(need, moe::bwd_gemm_scratch_bytes(g));
+  g.kind = moe::BWD_NN;
+  g.N = dff;
+  need = std::max(need, moe::bwd_gemm_scratch_bytes(g));
+  g.N = d;
+  g.K = n_up * dff;
+  need = std::max(need, moe::bwd_gemm_scratch_bytes(g));
+  g.kind = moe::BWD_TN;
+  g.M = d;
+  g.N = dff;
+  need = std::max(need, moe::bwd_gemm_scratch_bytes(g));
+  g.M = n_up * dff;
+  g.N = d;
+  need = std::max(need, moe::bwd_gemm_scratch_bytes(g));
+  return need;
+}
+
+void make_bwd_layout(const moe_config *c, moe_bwd_layout *L) {
+  const size_t T = static_cast<size_t>(c->num_tokens), E = static_cast<size_t>(c->num_experts);
+  const size_t d = static_cast<size_t>(c->d_model), s = elem_bytes(c);
+  const size_t n_up = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+  const bool ec = c->routing == MOE_EXPERT_CHOICE;
+  const size_t nslots = ec ? E * static_cast<size_t>(c->ec_capacity) : T * static_cast<size_t>(c->top_k);
+  const size_t P = static_cast<size_t>(padded_rows_of(c));
+  const size_t dff = static_cast<size_t>(c->d_ff), dffs = static_cast<size_t>(c->d_ff_shared);
+  const size_t Ts = dffs ? static_cast<size_t>(round_rows(c->num_tokens)) : 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  memset(L, 0, sizeof(*L));
+  L->padded_rows = P;
+  L->shared_rows = Ts;
+  L->poff = take((E + 1) * 4);
+  L->slot_prow = take(nslots * 4);
+  L->d_slot_w = take(nslots * 4);
+  L->dlogits = take(T * E * 4);
+  L->dx_router = take(T * d * 4);
+  L->router_offset = take(2 * 4);
+  L->xp = take(P * d * s);
+  L->dyp = take(P * d * s);
+  L->z = take(P * n_up * dff * s);
+  L->dh = take(P * dff * s);
+  L->dxp = take(P * d * s);
+  L->shared_offset = take(dffs ? 2 * 4 : 0);
+  L->xs = take(Ts * d * s);
+  L->dys = take(Ts * d * s);
+  L->zs = take(Ts * n_up * dffs * s);
+  L->dhs = take(Ts * dffs * s);
+  L->dxs = take(Ts * d * s);
+  L->scratch_bytes = ffn_bwd_scratch(c, c->num_experts, static_cast<int64_t>(P), c->d_ff);
+  L->scratch = take(L->scratch_bytes);
+  L->shared_scratch_bytes = dffs ? ffn_bwd_scratch(c, 1, static_cast<int64_t>(Ts), c->d_ff_shared) : 0;
+  L->shared_scratch = take(L->shared_scratch_bytes);
+  L->total = off;
+}
+
+// Backward of one expert set (the routed experts, or the shared expert as one
+// expert): recompute z = x W1^T, dh = dy W2, the activation backward
+// (z -> dz, dh -> h), dx = dz W1, dW2 = dy^T h, dW1 = dz^T x.  Rows of expert
+// e are [offs[e], offs[e+1]), multiples of 32, pad rows zero.
+moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const int32_t *offs, const void *w1,
+                        const void *w2, void *xp, void *dyp, void *z, void *dh, void *dxp, void *dw1, void *dw2,
+                        void *scratch, size_t scratch_bytes, hipStream_t st) {
+  const int n_up = c->act == MOE_ACT_SWIGLU ? 2 : 1, d = c->d_model;
+  moe::BwdGemm g = bwd_gemm(c, moe::BWD_NT);
+  g.offs = offs;
+  g.E = E;
+  g.max_rows = rows;
+  g.scratch = scratch;
+  g.scratch_bytes = scratch_bytes;
+  // z = xp W1^T  (the recomputed forward)
+  g.A = xp;
+  g.lda = d;
+  g.B = w1;
+  g.ldb = d;
+  g.b_stride = static_cast<int64_t>(n_up) * dff * d;
+  g.C = z;
+  g.ldc = static_cast<int64_t>(n_up) * dff;
+  g.N = n_up * dff;
+  g.K = d;
+  if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
+  // dh = dyp W2   (W2_e [d, dff]: K = d rows, N = dff columns)
+  g.kind = moe::BWD_NN;
+  g.A = dyp;
+  g.lda = d;
+  g.B = w2;
+  g.ldb = dff;
+  g.b_stride = static_cast<int64_t>(d) * dff;
+  g.C = dh;
+  g.ldc = dff;
+  g.N = dff;
+  g.K = d;
+  if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
+  const int act = c->act == MOE_ACT_SWIGLU ? 2 : 1;  // ACT_SWIGLU / ACT_GELU of the kernels
+  if (moe::launch_act_bwd(c->dtype, act, z, dh, offs + E, rows, dff, st) != hipSuccess) return MOE_ERR_HIP;
+  // dxp = dz W1   (W1_e [n_up*dff, d]: K = n_up*dff rows, N = d columns)
+  g.A = z;
+  g.lda = static_cast<int64_t>(n_up) * dff;
+  g.B = w1;
+  g.ldb = d;
+  g.b_stride = static_cast<int64_t>(n_up) * dff * d;
+  g.C = dxp;
+  g.ldc = d;
+  g.N = d;
+  g.K = n_up * dff;
+  if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
+  // dW2_e = dyp_e^T h_e   [d, dff]
+  g.kind = moe::BWD_TN;
+  g.A = dyp;
+  g.lda = d;
+  g.B = dh;
+  g.ldb = dff;
+  g.C = dw2;
+  g.ldc = dff;
+  g.c_stride = static_cast<int64_t>(d) * dff;
+  g.M = d;
+  g.N = dff;
+  g.K = 0;
+  if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
+  // dW1_e = dz_e^T xp_e   [n_up*dff, d]
+  g.A = z;
+  g.lda = static_cast<int64_t>(n_up) * dff;
+  g.B = xp;
+  g.ldb = d;
+  g.C = dw1;
+  g.ldc = d;
+  g.c_stride = static_cast<int64_t>(n_up) * dff * d;
+  g.M = n_up * dff;
+  g.N = d;
+  if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 const char *moe_status_string(moe_status s) {
   switch (s) {
@@ -456,6 +619,205 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
   if (s != MOE_OK) return s;
   if (join && hipStreamWaitEvent(main_st, join, 0) != hipSuccess) return MOE_ERR_HIP;
   return unpermute_impl(cfg, P(L.y_perm), tok_ptr, slot_row, slot_w, y_shared, y, stream);
+}
+
+moe_status moe_layer_bwd_workspace(const moe_config *cfg, moe_bwd_layout *layout) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  make_bwd_layout(cfg, layout);
+  return MOE_OK;
+}
+
+moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_router, const void *w1,
+                         const void *w2, const void *ws1, const void *ws2, const void *fwd_workspace,
+                         size_t fwd_workspace_bytes, const void *dy, void *dx, void *dw_router, void *dw1,
+                         void *dw2, void *dws1, void *dws2, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  const bool shared = cfg->d_ff_shared > 0;
+  if (!w_router || !w1 || !w2 || !dw_router || !dw1 || !dw2) return MOE_ERR_INVALID_ARG;
+  if (shared && (!ws1 || !ws2 || !dws1 || !dws2)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w_router) || !aligned16(w1) || !aligned16(w2) || !aligned16(dw_router) || !aligned16(dw1) ||
+      !aligned16(dw2))
+    return MOE_ERR_INVALID_ARG;
+  if (shared && (!aligned16(ws1) || !aligned16(ws2) || !aligned16(dws1) || !aligned16(dws2)))
+    return MOE_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int T = cfg->num_tokens, E = cfg->num_experts, d = cfg->d_model;
+  const int n_up = cfg->act == MOE_ACT_SWIGLU ? 2 : 1;
+  const size_t es = elem_bytes(cfg);
+  if (T == 0) {  // no tokens: every weight gradient is zero
+    if (moe::launch_zero(dw_router, static_cast<size_t>(E) * d * es, st) != hipSuccess ||
+        moe::launch_zero(dw1, static_cast<size_t>(E) * n_up * cfg->d_ff * d * es, st) != hipSuccess ||
+        moe::launch_zero(dw2, static_cast<size_t>(E) * d * cfg->d_ff * es, st) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (shared && (moe::launch_zero(dws1, static_cast<size_t>(n_up) * cfg->d_ff_shared * d * es, st) != hipSuccess ||
+                   moe::launch_zero(dws2, static_cast<size_t>(d) * cfg->d_ff_shared * es, st) != hipSuccess))
+      return MOE_ERR_HIP;
+    return MOE_OK;
+  }
+  if (!x || !dy || !dx || !fwd_workspace || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx)) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || (reinterpret_cast<uintptr_t>(fwd_workspace) & 255u) != 0)
+    return MOE_ERR_INVALID_ARG;
+  moe_workspace_layout F;
+  make_layout(cfg, &F);
+  if (fwd_workspace_bytes < F.total) return MOE_ERR_WORKSPACE;
+  moe_bwd_layout L;
+  make_bwd_layout(cfg, &L);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const int64_t prows = static_cast<int64_t>(L.padded_rows);
+  if (!gemm_fits(cfg, prows, cfg->d_ff)) return MOE_ERR_UNSUPPORTED;
+  moe_config sc = shared_config(cfg);
+  if (shared && !gemm_fits(&sc, static_cast<int64_t>(L.shared_rows), cfg->d_ff_shared)) return MOE_ERR_UNSUPPORTED;
+
+  const char *fw = static_cast<const char *>(fwd_workspace);
+  char *ws = static_cast<char *>(workspace);
+  auto F_ = [&](size_t off) { return static_cast<const void *>(fw + off); };
+  auto P = [&](size_t off) { return static_cast<void *>(ws + off); };
+  const bool ec = cfg->routing == MOE_EXPERT_CHOICE;
+  const int32_t *tok_ptr = ec ? static_cast<const int32_t *>(F_(F.tok_ptr)) : nullptr;
+  const int32_t *slot_row = static_cast<const int32_t *>(F_(F.slot_row));
+  const float *slot_w = static_cast<const float *>(ec ? F_(F.slot_w) : F_(F.topk_w));
+  const int32_t *count = static_cast<const int32_t *>(F_(F.expert_count));
+  const int64_t nslots = ec ? static_cast<int64_t>(E) * cfg->ec_capacity : static_cast<int64_t>(T) * cfg->top_k;
+  int32_t *poff = static_cast<int32_t *>(P(L.poff));
+  int32_t *slot_prow = static_cast<int32_t *>(P(L.slot_prow));
+  float *d_slot_w = static_cast<float *>(P(L.d_slot_w));
+  float *dlogits = static_cast<float *>(P(L.dlogits));
+  float *dx_router = static_cast<float *>(P(L.dx_router));
+
+  // Shared expert: depends only on x and dy, so it runs on the side stream
+  // beside the routed part and is joined before dx is assembled.
+  hipEvent_t join = nullptr;
+  if (shared) {
+    SideStream *side = side_stream();
+    if (!side) return MOE_ERR_HIP;
+    if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+      return MOE_ERR_HIP;
+    const int64_t Ts = static_cast<int64_t>(L.shared_rows);
+    int32_t *so = static_cast<int32_t *>(P(L.shared_offset));
+    if (moe::launch_fill_offsets(so, static_cast<int32_t>(Ts), side->stream) != hipSuccess ||
+        moe::launch_pad_copy(x, P(L.xs), T, Ts, static_cast<size_t>(d) * es, side->stream) != hipSuccess ||
+        moe::launch_pad_copy(dy, P(L.dys), T, Ts, static_cast<size_t>(d) * es, side->stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    s = ffn_bwd_impl(&sc, 1, cfg->d_ff_shared, Ts, so, ws1, ws2, P(L.xs), P(L.dys), P(L.zs), P(L.dhs), P(L.dxs),
+                     dws1, dws2, P(L.shared_scratch), L.shared_scratch_bytes, side->stream);
+    if (s != MOE_OK) return s;
+    if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_ERR_HIP;
+    join = side->join;
+  }
+
+  // padded offsets, then the combine's backward (dL/dw per slot, w*dy and x
+  // into the padded rows), then zero pad rows
+  if (moe::launch_bwd_offsets(count, E, max_rows_of(cfg), poff, st) != hipSuccess) return MOE_ERR_HIP;
+  moe::BwdUnpermuteArgs u{};
+  u.dtype = cfg->dtype;
+  u.T = T;
+  u.d = d;
+  u.k = ec ? 0 : cfg->top_k;
+  u.E = E;
+  u.ec_capacity = ec ? cfg->ec_capacity : 0;
+  u.rows = max_rows_of(cfg);
+  u.prows = prows;
+  u.nslots = nslots;
+  u.dy = dy;
+  u.x = x;
+  u.y_perm = F_(F.y_perm);
+  u.tok_ptr = tok_ptr;
+  u.slot_row = slot_row;
+  u.topk_idx = static_cast<const int32_t *>(F_(F.topk_idx));
+  u.offs = static_cast<const int32_t *>(F_(F.expert_offset));
+  u.poff = poff;
+  u.slot_w = slot_w;
+  u.dyp = P(L.dyp);
+  u.xp = P(L.xp);
+  u.d_slot_w = d_slot_w;
+  u.slot_prow = slot_prow;
+  if (moe::launch_unpermute_bwd(u, st) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_pad_zero(poff, count, E, prows, static_cast<size_t>(d) * es, P(L.xp), P(L.dyp), st) != hipSuccess)
+    return MOE_ERR_HIP;
+
+  // gate gradient, then the router's linear layer
+  moe::RouterBwdArgs r{};
+  r.T = T;
+  r.E = E;
+  r.k = ec ? 0 : cfg->top_k;
+  r.routing = cfg->routing;
+  r.ec_capacity = ec ? cfg->ec_capacity : 0;
+  r.nslots = nslots;
+  r.logits = static_cast<const float *>(F_(F.logits));
+  r.scores = ec ? static_cast<const float *>(F_(F.scores)) : nullptr;
+  r.topk_w = ec ? nullptr : static_cast<const float *>(F_(F.topk_w));
+  r.d_slot_w = d_slot_w;
+  r.topk_idx = ec ? nullptr : static_cast<const int32_t *>(F_(F.topk_idx));
+  r.tok_ptr = tok_ptr;
+  r.slot_row = slot_row;
+  r.dlogits = dlogits;
+  if (moe::launch_router_bwd(r, st) != hipSuccess) return MOE_ERR_HIP;
+  int32_t *ro = static_cast<int32_t *>(P(L.router_offset));
+  if (moe::launch_fill_offsets(ro, T, st) != hipSuccess) return MOE_ERR_HIP;
+  {
+    // dx_router = dlogits W_r  (fp32 [T,E] x [E,d])
+    moe::GenGemmArgs g{};
+    g.A = dlogits;
+    g.a_rs = E;
+    g.a_ks = 1;
+    g.B = w_router;
+    g.b_ks = d;
+    g.b_cs = 1;
+    g.C = dx_router;
+    g.c_rs = d;
+    g.offs = ro;
+    g.E = 1;
+    g.mode = 0;
+    g.max_rows = T;
+    g.N = d;
+    g.K = E;
+    if (moe::launch_gemm_generic(g, 0, cfg->dtype, 0, st) != hipSuccess) return MOE_ERR_HIP;
+    // dW_r = dlogits^T x  ([E,T] x [T,d])
+    moe::GenGemmArgs h{};
+    h.A = dlogits;
+    h.a_rs = 1;
+    h.a_ks = E;
+    h.B = x;
+    h.b_ks = d;
+    h.b_cs = 1;
+    h.C = dw_router;
+    h.c_rs = d;
+    h.offs = ro;
+    h.E = 1;
+    h.mode = 1;
+    h.max_rows = T;
+    h.M = E;
+    h.N = d;
+    if (moe::launch_gemm_generic(h, 0, cfg->dtype, cfg->dtype, st) != hipSuccess) return MOE_ERR_HIP;
+  }
+
+  // routed experts
+  s = ffn_bwd_impl(cfg, E, cfg->d_ff, prows, poff, w1, w2, P(L.xp), P(L.dyp), P(L.z), P(L.dh), P(L.dxp), dw1, dw2,
+                   P(L.scratch), L.scratch_bytes, st);
+  if (s != MOE_OK) return s;
+
+  // dx: the permutation's backward (each token gathers its copies'
+  // gradients) + the router term + the shared expert's
+  if (join && hipStreamWaitEvent(st, join, 0) != hipSuccess) return MOE_ERR_HIP;
+  moe::GatherDxArgs gx{};
+  gx.dtype = cfg->dtype;
+  gx.T = T;
+  gx.d = d;
+  gx.k = ec ? 0 : cfg->top_k;
+  gx.prows = prows;
+  gx.nslots = nslots;
+  gx.tok_ptr = tok_ptr;
+  gx.slot_prow = slot_prow;
+  gx.dxp = P(L.dxp);
+  gx.dx_shared = shared ? P(L.dxs) : nullptr;
+  gx.dx_router = dx_router;
+  gx.dx = dx;
+  return hip_status(moe::launch_gather_dx(gx, st));
 }
 
 }  // extern "C"

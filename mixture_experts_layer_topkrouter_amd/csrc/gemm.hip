@@ -918,4 +918,46 @@ hipError_t launch_fill_offsets(int32_t *dst, int32_t t, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Grouped GEMMs of the backward pass.
+size_t bwd_gemm_scratch_bytes(const BwdGemm &g) {
+  (void)g;
+  return 0;
+}
+
+hipError_t launch_bwd_gemm(const BwdGemm &g, hipStream_t st) {
+  GenGemmArgs a{};
+  a.A = g.A;
+  a.B = g.B;
+  a.C = g.C;
+  a.offs = g.offs;
+  a.E = g.E;
+  a.max_rows = g.max_rows;
+  a.N = g.N;
+  a.K = g.K;
+  a.M = g.M;
+  a.c_rs = g.ldc;
+  if (g.kind == BWD_TN) {
+    a.mode = 1;
+    a.a_rs = 1;
+    a.a_ks = g.lda;
+    a.b_ks = g.ldb;
+    a.b_cs = 1;
+    a.c_es = g.c_stride;
+  } else {
+    a.mode = 0;
+    a.a_rs = g.lda;
+    a.a_ks = 1;
+    a.b_es = g.b_stride;
+    if (g.kind == BWD_NT) {
+      a.b_ks = 1;
+      a.b_cs = g.ldb;
+    } else {
+      a.b_ks = g.ldb;
+      a.b_cs = 1;
+    }
+  }
+  return launch_gemm_generic(a, g.dtype, g.dtype, g.dtype, st);
+}
+
 }  // namespace moe

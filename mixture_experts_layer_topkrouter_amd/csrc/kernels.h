@@ -85,4 +85,97 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 // Fills a small int32 device array (used for the shared expert's {0, T}).
 hipError_t launch_fill_offsets(int32_t *dst, int32_t t, hipStream_t st);
 
+// ---- backward pass (backward.hip) ----------------------------------------
+// Expert blocks of the backward's row layout start on multiples of this many
+// rows (zero pad rows), so the weight-gradient GEMMs contract over whole
+// 32-row K stages.
+constexpr int kPadRows = 32;
+
+struct BwdUnpermuteArgs {
+  int dtype, T, d, k, E;
+  int ec_capacity;  // > 0: ExpertChoice (row r belongs to expert r / C)
+  int64_t rows, prows, nslots;
+  const void *dy, *x, *y_perm;
+  const int32_t *tok_ptr, *slot_row, *topk_idx, *offs, *poff;
+  const float *slot_w;
+  void *dyp, *xp;
+  float *d_slot_w;
+  int32_t *slot_prow;
+};
+hipError_t launch_unpermute_bwd(const BwdUnpermuteArgs &a, hipStream_t st);
+
+struct RouterBwdArgs {
+  int T, E, k, routing, ec_capacity;
+  int64_t nslots;
+  const float *logits, *scores, *topk_w, *d_slot_w;
+  const int32_t *topk_idx, *tok_ptr, *slot_row;
+  float *dlogits;
+};
+hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st);
+
+struct GatherDxArgs {
+  int dtype, T, d, k;
+  int64_t prows, nslots;
+  const int32_t *tok_ptr, *slot_prow;
+  const void *dxp, *dx_shared;
+  const float *dx_router;
+  void *dx;
+};
+hipError_t launch_gather_dx(const GatherDxArgs &a, hipStream_t st);
+
+hipError_t launch_bwd_offsets(const int32_t *count, int E, int64_t max_rows, int32_t *poff, hipStream_t st);
+hipError_t launch_pad_zero(const int32_t *poff, const int32_t *count, int E, int64_t prows, size_t row_bytes,
+                           void *b0, void *b1, hipStream_t st);
+hipError_t launch_pad_copy(const void *src, void *dst, int64_t rows, int64_t prows, size_t row_bytes,
+                           hipStream_t st);
+hipError_t launch_act_bwd(int dtype, int act, void *z, void *dh, const int32_t *rows_of, int64_t prows, int dff,
+                          hipStream_t st);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
+
+// Generic grouped GEMM C(r, c) = sum_k A(r, k) B(k, c), element strides:
+//   A(r, k) = A[r*a_rs + k*a_ks],  B(k, c) = B[e*b_es + k*b_ks + c*b_cs],
+//   C(r, c) = C[e*c_es + r*c_rs + c]  (e = the group; c_es used in mode 1).
+// mode 0: group e owns rows [offs[e], offs[e+1]) (< max_rows), K fixed.
+// mode 1: group e contracts over [offs[e], offs[e+1]) (< max_rows) and owns
+//         a dense M x N block of C.
+struct GenGemmArgs {
+  const void *A;
+  int64_t a_rs, a_ks;
+  const void *B;
+  int64_t b_ks, b_cs, b_es;
+  void *C;
+  int64_t c_rs, c_es;
+  const int32_t *offs;
+  int E, mode;
+  int64_t max_rows;
+  int M, N, K;
+  int m_tiles, n_tiles;  // set by the launcher
+};
+// dtypes: 0 fp32, 1 bf16 (A, B, C).
+hipError_t launch_gemm_generic(GenGemmArgs g, int a_dt, int b_dt, int c_dt, hipStream_t st);
+
+// The grouped GEMMs of the backward pass: bf16 shapes the direct-to-LDS
+// MFMA kernels take run there (gemm.hip), the rest on the generic kernel.
+//   kind NT: C[r,:] = A[r,:] B_e^T   (B_e [N, K], the forward's layout)
+//   kind NN: C[r,:] = A[r,:] B_e     (B_e [K, N])
+//   kind TN: C_e = A[rows_e,:]^T B[rows_e,:]  (C_e [M, N], contraction over
+//            the group's rows, which start on multiples of kPadRows)
+enum { BWD_NT = 0, BWD_NN = 1, BWD_TN = 2 };
+struct BwdGemm {
+  int kind, dtype;
+  const void *A, *B;
+  void *C;
+  int64_t lda, ldb, ldc;   // row strides (elements)
+  int64_t b_stride;        // per-group B elements (NT, NN)
+  int64_t c_stride;        // per-group C elements (TN)
+  const int32_t *offs;
+  int E;
+  int64_t max_rows;        // rows (NT, NN) or contraction rows (TN) bound
+  int M, N, K;             // TN: C_e is M x N; NT / NN: N outputs, K contraction
+  void *scratch;
+  size_t scratch_bytes;
+};
+size_t bwd_gemm_scratch_bytes(const BwdGemm &g);
+hipError_t launch_bwd_gemm(const BwdGemm &g, hipStream_t st);
+
 }  // namespace moe

@@ -1,7 +1,7 @@
 """Thin ctypes binding of ``libmoe_mi355x.so`` (the C ABI in ``include/moe.h``).
 
-Argument marshalling only: every step of the forward pass runs in the HIP
-kernels behind the C ABI.  torch is used for device memory and streams; the
+Argument marshalling only: every step of the forward and backward passes runs
+in the HIP kernels behind the C ABI.  torch is used for device memory and streams; the
 functions take torch tensors, pass their device pointers and torch's current
 HIP stream, and raise :class:`MoeError` on a non-OK status.  There is no CPU
 fallback: when the library is missing, loading it raises.
@@ -62,6 +62,15 @@ class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in _LAYOUT_FIELDS]
 
 
+_BWD_LAYOUT_FIELDS = ["poff", "slot_prow", "d_slot_w", "dlogits", "dx_router", "router_offset", "xp", "dyp", "z",
+                      "dh", "dxp", "shared_offset", "xs", "dys", "zs", "dhs", "dxs", "scratch", "scratch_bytes",
+                      "shared_scratch", "shared_scratch_bytes", "padded_rows", "shared_rows", "total"]
+
+
+class BwdLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in _BWD_LAYOUT_FIELDS]
+
+
 _lib = None
 
 
@@ -91,6 +100,8 @@ def load_library() -> ctypes.CDLL:
         "moe_unpermute": ([CP, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_layer_workspace": ([CP, ctypes.POINTER(WorkspaceLayout)], ctypes.c_int),
         "moe_layer_fwd": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "moe_layer_bwd_workspace": ([CP, ctypes.POINTER(BwdLayout)], ctypes.c_int),
+        "moe_layer_bwd": ([CP, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -205,6 +216,22 @@ def layer_fwd(cfg: MoeConfig, x, w_router, w1, w2, y, workspace, *, bias=None, b
            "moe_layer_fwd")
 
 
+def layer_bwd_workspace(cfg: MoeConfig) -> Dict[str, int]:
+    L = BwdLayout()
+    _check(load_library().moe_layer_bwd_workspace(ctypes.byref(cfg), ctypes.byref(L)), "moe_layer_bwd_workspace")
+    return {n: int(getattr(L, n)) for n in _BWD_LAYOUT_FIELDS}
+
+
+def layer_bwd(cfg: MoeConfig, x, w_router, w1, w2, fwd_workspace, dy, dx, dw_router, dw1, dw2, workspace, *,
+              ws1=None, ws2=None, dws1=None, dws2=None, stream=None):
+    fbytes = fwd_workspace.numel() * fwd_workspace.element_size()
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().moe_layer_bwd(ctypes.byref(cfg), _p(x), _p(w_router), _p(w1), _p(w2), _p(ws1), _p(ws2),
+                                        _p(fwd_workspace), fbytes, _p(dy), _p(dx), _p(dw_router), _p(dw1), _p(dw2),
+                                        _p(dws1), _p(dws2), _p(workspace), nbytes, _stream(stream)),
+           "moe_layer_bwd")
+
+
 # ------------------------------------------------ allocation conveniences --
 
 def alloc_workspace(cfg: MoeConfig, device="cuda") -> torch.Tensor:
@@ -310,3 +337,54 @@ class MoELayer:
     def view(self, name: str) -> torch.Tensor:
         dtype, shape = self.shapes()[name]
         return workspace_view(self.cfg, self.workspace, name, dtype, shape)
+
+    # ---- backward ----------------------------------------------------------
+    def alloc_grads(self, device="cuda"):
+        """Gradient buffers (dtype of the weights) and the backward workspace."""
+        c, d = self.cfg, self.dev
+        self.bwd_layout = layer_bwd_workspace(c)
+        self.bwd_workspace = torch.empty(max(self.bwd_layout["total"], 256), dtype=torch.uint8, device=device)
+        self.dx = torch.empty_like(d.x)
+        self.dwr = torch.empty_like(d.wr)
+        self.dw1 = torch.empty_like(d.w1)
+        self.dw2 = torch.empty_like(d.w2)
+        self.dws1 = None if d.ws1 is None else torch.empty_like(d.ws1)
+        self.dws2 = None if d.ws2 is None else torch.empty_like(d.ws2)
+
+    def backward(self, dy: torch.Tensor, stream=None):
+        """moe_layer_bwd for upstream gradient dy, after forward() on the same
+        inputs; fills self.dx, dwr, dw1, dw2 (and dws1, dws2)."""
+        if not hasattr(self, "bwd_workspace"):
+            self.alloc_grads(dy.device)
+        d = self.dev
+        layer_bwd(self.cfg, d.x, d.wr, d.w1, d.w2, self.workspace, dy, self.dx, self.dwr, self.dw1, self.dw2,
+                  self.bwd_workspace, ws1=d.ws1, ws2=d.ws2, dws1=self.dws1, dws2=self.dws2, stream=stream)
+
+    def bwd_view(self, name: str) -> torch.Tensor:
+        """A typed view of one intermediate of the backward workspace."""
+        c = self.cfg
+        T, E, d = c.num_tokens, c.num_experts, c.d_model
+        L = self.bwd_layout
+        P = L["padded_rows"]
+        dt = torch_dtype(c)
+        n_up = 2 if c.act == SWIGLU else 1
+        slots = E * c.ec_capacity if c.routing == EXPERT_CHOICE else T * c.top_k
+        shapes = {
+            "poff": (torch.int32, (E + 1,)),
+            "slot_prow": (torch.int32, (slots,)),
+            "d_slot_w": (torch.float32, (slots,)),
+            "dlogits": (torch.float32, (T, E)),
+            "dx_router": (torch.float32, (T, d)),
+            "xp": (dt, (P, d)),
+            "dyp": (dt, (P, d)),
+            "z": (dt, (P, n_up * c.d_ff)),
+            "dh": (dt, (P, c.d_ff)),
+            "dxp": (dt, (P, d)),
+        }
+        dtype, shape = shapes[name]
+        off = L[name]
+        n = 1
+        for v in shape:
+            n *= int(v)
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.bwd_workspace[off:off + nbytes].view(dtype).view(*shape)

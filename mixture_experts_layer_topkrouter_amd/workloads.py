@@ -177,6 +177,13 @@ def make_inputs(w: Workload, seed: int = 0, with_experts: bool = True) -> Dict[s
     return out
 
 
+def make_dy(w: Workload, seed: int = 0) -> np.ndarray:
+    """Upstream gradient dL/dy [T, d] for the backward pass: its own stream
+    (``default_rng(seed + 1000003)``), standard normal, rounded like x."""
+    rng = np.random.default_rng(seed + 1000003)
+    return _normal(rng, (w.T, w.d), 1.0, w.dtype, chunk_rows=4096)
+
+
 def small_variant(w: Workload, **kw) -> Workload:
     """A reduced-size copy of a workload for parity runs the oracle finishes in
     seconds (same routing structure, dtype and activation)."""

@@ -15,13 +15,14 @@ def test_library_exports_every_header_symbol():
     assert len(syms) >= 11
     for s in syms:
         assert hasattr(lib, s), s
-    for s in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_unpermute", "moe_layer_fwd"):
+    for s in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_unpermute", "moe_layer_fwd", "moe_layer_bwd",
+              "moe_layer_bwd_workspace"):
         assert s in syms
 
 
 def test_status_strings_and_version():
     lib = moe.load_library()
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
 
@@ -124,3 +125,40 @@ def test_unsupported_and_workspace_errors():
     # null output -> invalid argument
     st = lib.moe_unpermute(ctypes.byref(cfg), fake, None, fake, fake, None, None, None)
     assert st == 1
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_backward_workspace_layout(name):
+    """Rows of the backward's padded layout: each expert's block rounded up to
+    32 rows, so at most 31 pad rows per expert; the shared expert's T rows
+    rounded up to 32; every region 256-B aligned and inside the total."""
+    w = W.WORKLOADS[name]
+    cfg = moe.make_config(w)
+    L = moe.layer_bwd_workspace(cfg)
+    assert L["padded_rows"] == moe.max_rows(cfg) + 31 * w.E
+    assert L["shared_rows"] == ((w.T + 31) // 32 * 32 if w.d_ff_shared else 0)
+    n_up = 2 if w.act == W.SWIGLU else 1
+    P, s = L["padded_rows"], w.elem_bytes
+    sizes = {"xp": P * w.d * s, "dyp": P * w.d * s, "z": P * n_up * w.d_ff * s, "dh": P * w.d_ff * s,
+             "dxp": P * w.d * s, "dlogits": w.T * w.E * 4, "dx_router": w.T * w.d * 4}
+    regions = sorted((L[n], L[n] + b) for n, b in sizes.items())
+    for (a0, a1), (b0, _) in zip(regions, regions[1:]):
+        assert a1 <= b0
+    assert all(L[n] % 256 == 0 for n in sizes) and regions[-1][1] <= L["total"]
+
+
+def test_backward_argument_errors():
+    lib = moe.load_library()
+    cfg = _cfg()
+    fake = ctypes.c_void_p(256)
+    F = moe.layer_workspace(cfg)["total"]
+    B = moe.layer_bwd_workspace(cfg)["total"]
+    args = lambda fwd_bytes, ws_bytes, dx=fake: (ctypes.byref(cfg), fake, fake, fake, fake, None, None, fake,
+                                                 fwd_bytes, fake, dx, fake, fake, fake, None, None, fake, ws_bytes,
+                                                 None)
+    assert lib.moe_layer_bwd(*args(F - 1, B)) == 3      # forward workspace too small
+    assert lib.moe_layer_bwd(*args(F, B - 1)) == 3      # backward workspace too small
+    assert lib.moe_layer_bwd(*args(F, B, dx=None)) == 1  # missing output
+    sh = _cfg(d_ff_shared=64)
+    assert lib.moe_layer_bwd(ctypes.byref(sh), fake, fake, fake, fake, None, None, fake, 1 << 30, fake, fake, fake,
+                             fake, fake, None, None, fake, 1 << 30, None) == 1  # shared expert without its weights
