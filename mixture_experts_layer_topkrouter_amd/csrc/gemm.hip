@@ -233,6 +233,7 @@ struct Job {
   int e, row0, rows, nt;
   int kb, ke;           // K stages [kb, ke) of this piece
   int tail, seg, nseg;  // split tile index (-1 if whole), piece, pieces
+  int k0;               // first contraction row of the group (groups of K)
 };
 
 __device__ __forceinline__ bool map_job(const GemmParams &p, int nk, Job *j) {
@@ -244,6 +245,7 @@ __device__ __forceinline__ bool map_job(const GemmParams &p, int nk, Job *j) {
   j->tail = -1;
   j->seg = 0;
   j->nseg = 1;
+  j->k0 = 0;
   if (bid < sp.full) {
     q = xcd_remap(bid, sp.full);
   } else {
@@ -267,6 +269,57 @@ __device__ __forceinline__ bool map_job(const GemmParams &p, int nk, Job *j) {
   return find_tile<DBM>(p.offs, p.E, p.max_rows, p.n_tiles, q, &j->e, &j->row0, &j->rows, &j->nt);
 }
 
+// Operand layouts of the 256-row kernel.  NT (the forward): A [rows, K] and
+// B [N, K], both contiguous along K.  NN (data gradients): B [K, N], N
+// contiguous.  TN (weight gradients): A [K, M] and B [K, N] over the rows of
+// a group, C_e = A_e^T B_e.  A [K, ...] operand is staged in LDS as 32 rows of
+// 256 elements (512 B) per stage; chunk c (8 elements) of row kk is stored at
+// c ^ (4 * (kk & 3)), and its MFMA fragments are read with gfx950's LDS
+// transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane i reads
+// 4 elements of row i/4 at columns 4*(i%4)..+3 and receives column i of the
+// group's 4 rows.  Two such reads give a lane the 8 consecutive K values of
+// one column that a 32x32x16 operand needs.  The 32 lanes served together
+// read rows kk..kk+3 at the same 64-B column range, which the swizzle puts in
+// 4 distinct bank groups.
+enum { LAY_NT = 0, LAY_NN = 1, LAY_TN = 2 };
+
+__device__ __forceinline__ int tr_swz(int kk) { return 4 * (kk & 3); }
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t *p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)((lds_u16 *)p));
+}
+
+// Groups of K (TN): one workgroup per (group, row tile, column tile), dense;
+// row tiles innermost, so neighbouring workgroups of one XCD share the B
+// panel of a column tile.  The group's contraction rows are
+// [offs[e], offs[e+1]), whole 32-row stages.
+__device__ __forceinline__ bool map_kgroup_job(const GemmParams &p, Job *j) {
+  const int per = p.m_tiles * p.n_tiles;
+  const int total = per * p.E;
+  const int bid = blockIdx.x;
+  if (bid >= total) return false;
+  const int q = xcd_remap(bid, total);
+  const int e = q / per, r = q - e * per;
+  const int nt = r / p.m_tiles, mt = r - nt * p.m_tiles;
+  int k0, me;
+  expert_rows(p.offs, e, p.max_rows, &k0, &me);
+  j->e = __builtin_amdgcn_readfirstlane(e);
+  j->row0 = __builtin_amdgcn_readfirstlane(mt * DBM);
+  j->rows = __builtin_amdgcn_readfirstlane(min(DBM, p.m_rows - mt * DBM));
+  j->nt = __builtin_amdgcn_readfirstlane(nt);
+  j->k0 = __builtin_amdgcn_readfirstlane(k0);
+  j->kb = 0;
+  j->ke = __builtin_amdgcn_readfirstlane(me / DK);
+  j->tail = -1;
+  j->seg = 0;
+  j->nseg = 1;
+  return true;
+}
+
 // An empty asm "use" at the end of an iteration keeps that iteration's
 // fragment set live until then, so the register allocator cannot hand its
 // registers to the next stage's LDS reads while queued MFMAs still have to
@@ -282,7 +335,7 @@ __device__ __forceinline__ void keep_live(bf16x8 (&fa)[2][2][MI], bf16x8 (&fb)[2
   }
 }
 
-template <int ACT, int WAVES>
+template <int ACT, int WAVES, int LAY = LAY_NT>
 __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p) {
   // v_mfma_f32_32x32x16_bf16 (the 16x16x32 form does not keep the matrix core
   // full from one wave per SIMD).  WAVES = 4: one wave per SIMD, each owning
@@ -299,19 +352,34 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   constexpr int NR = 2 * (MI + NJ);     // fragment reads per wave per stage
   constexpr int NM = 2 * MI * NJ;       // MFMAs per wave per stage
   static_assert((WAVES == 4 ? NM / 2 : 3 * NM / 4) == NR && NM / 4 == ND, "interleave covers every read and load");
+  static_assert(LAY == LAY_NT || (ACT == ACT_NONE && WAVES == 4), "backward layouts: plain output, 4 waves");
+  constexpr bool AT = LAY == LAY_TN;  // A staged as [K][M]
+  constexpr bool BT = LAY != LAY_NT;  // B staged as [K][N]
   // one array per ring slot: A stage at [0, DSTAGE), B stage at [DSTAGE, 2*DSTAGE)
   __shared__ __attribute__((aligned(1024))) uint16_t s0[2 * DSTAGE], s1[2 * DSTAGE], s2[2 * DSTAGE],
       s3[2 * DSTAGE], s4[2 * DSTAGE];
 
   Job job;
-  if (!map_job(p, p.K / DK, &job)) return;
+  if constexpr (LAY == LAY_TN) {
+    if (!map_kgroup_job(p, &job)) return;
+  } else {
+    if (!map_job(p, p.K / DK, &job)) return;
+  }
   const int e = job.e, row0 = job.row0, rows = job.rows, nt = job.nt;
   const int l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const int wm = w >> 1, wn = w & 1;
-  // wave-uniform bases of this piece's K range: A at the tile's first row, B
-  // at the expert's weights
-  const char *A = static_cast<const char *>(p.A) + (static_cast<int64_t>(row0) * p.lda + job.kb * DK) * 2;
-  const char *B = static_cast<const char *>(p.B) + (static_cast<int64_t>(e) * p.b_stride + job.kb * DK) * 2;
+  // wave-uniform bases of this piece's K range: A at the tile's first row
+  // (TN: its first column), B at the expert's weights (TN: the column
+  // tile's first column); a stage advances them by a_step / b_step bytes
+  const int64_t kfirst = static_cast<int64_t>(job.k0) + static_cast<int64_t>(job.kb) * DK;
+  const char *A = static_cast<const char *>(p.A) +
+                  (AT ? kfirst * p.lda + row0 : static_cast<int64_t>(row0) * p.lda + job.kb * DK) * 2;
+  const char *B = static_cast<const char *>(p.B) +
+                  (BT ? (LAY == LAY_TN ? 0 : static_cast<int64_t>(e) * p.b_stride) + kfirst * p.ldb +
+                            static_cast<int64_t>(nt) * BN
+                      : static_cast<int64_t>(e) * p.b_stride + job.kb * DK) * 2;
+  const int64_t a_step = AT ? static_cast<int64_t>(DK) * p.lda * 2 : DK * 2;
+  const int64_t b_step = BT ? static_cast<int64_t>(DK) * p.ldb * 2 : DK * 2;
 
   auto slot = [&](auto S) -> uint16_t * {
     constexpr int s = decltype(S)::value;
@@ -327,30 +395,45 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   // r = q/4, stored chunk q%4, which holds logical chunk (q%4) ^ ((r>>2)&3).
   // Per-lane byte offsets from A / B (they fit 32 bits: the host limits every
   // operand to 2^31 elements).
+  // [K][.] operands: LDS chunk slot q is row kk = q/32, stored chunk q%32,
+  // which holds logical chunk (q%32) ^ tr_swz(kk); columns past the operand's
+  // width (partial tiles) read its last valid 8 columns instead.
   uint32_t a_off[ND / 2], b_off[ND / 2];
 #pragma unroll
   for (int i = 0; i < ND / 2; ++i) {
     const int q = (WAVES * i + w) * 64 + l;
     const int r = q >> 2;
     const int c = (q & 3) ^ ((r >> 2) & 3);
-    a_off[i] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
-    int br;
-    if (ACT == ACT_SWIGLU) {
-      const int col = nt * (BN / 2) + (r & (BN / 2 - 1));
-      br = (col < p.n_out ? col : 0) + (r >= BN / 2 ? p.up_off : 0);
+    const int kk = q >> 5;
+    const int tc = (q & 31) ^ tr_swz(kk);
+    if constexpr (AT) {
+      const int col = min(tc * 8, p.m_rows - row0 - 8);
+      a_off[i] = static_cast<uint32_t>((static_cast<int64_t>(kk) * p.lda + col) * 2);
     } else {
-      const int col = nt * BN + r;
-      br = col < p.n_out ? col : 0;
+      a_off[i] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
     }
-    b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(br) * p.ldb + c * 8) * 2);
+    if constexpr (BT) {
+      const int col = min(tc * 8, p.n_out - nt * BN - 8);
+      b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(kk) * p.ldb + col) * 2);
+    } else {
+      int br;
+      if (ACT == ACT_SWIGLU) {
+        const int col = nt * (BN / 2) + (r & (BN / 2 - 1));
+        br = (col < p.n_out ? col : 0) + (r >= BN / 2 ? p.up_off : 0);
+      } else {
+        const int col = nt * BN + r;
+        br = col < p.n_out ? col : 0;
+      }
+      b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(br) * p.ldb + c * 8) * 2);
+    }
   }
   // stage st of this piece: K elements [st*DK, st*DK + DK) past A / B
   auto issue = [&](auto S, int st) {
     const uint32_t base = lds_addr_of(slot(S));
 #pragma unroll
     for (int i = 0; i < ND / 2; ++i) {
-      dma16(a_off[i], A + st * DK * 2, base + (WAVES * i + w) * 64 * 16);
-      dma16(b_off[i], B + st * DK * 2, base + DSTAGE * 2 + (WAVES * i + w) * 64 * 16);
+      dma16(a_off[i], A + st * a_step, base + (WAVES * i + w) * 64 * 16);
+      dma16(b_off[i], B + st * b_step, base + DSTAGE * 2 + (WAVES * i + w) * 64 * 16);
     }
   };
 
@@ -368,6 +451,30 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
     else br = wn * 128 + j * 32;
     b_row[j] = DSTAGE + (br + frow) * DK;
   }
+  // transpose reads of a [K][.] operand: lane l (group g = l/16, i = l%16)
+  // reads row 16*ks + 8*(g/2) + 4*r + i/4 at logical column
+  // base + 16*(g%2) + 4*(i%4); a 32-column fragment starting at column 32*j
+  // of the wave's half sits at stored chunk ((4j) ^ swizzle) + (column/8)%4
+  const int tg = l >> 4, ti = l & 15;
+  const int tr_row = (8 * (tg >> 1) + (ti >> 2)) * BN;
+  const int tr_col = 16 * (tg & 1) + 4 * (ti & 3);
+  const int tr_sw = tr_swz(ti >> 2);
+  const int tr_base_a = tr_row + wm * RW + ((tr_col >> 3) << 3) + (tr_col & 7);
+  const int tr_base_b = DSTAGE + tr_row + wn * 128 + ((tr_col >> 3) << 3) + (tr_col & 7);
+  auto tr_frag = [&](const uint16_t *ls, int base, int tile, int ks) -> bf16x8 {
+    const int off = base + (((4 * tile) ^ tr_sw) << 3) + ks * 16 * BN;
+    const bf16x4 lo = lds_read_tr16(ls + off);
+    const bf16x4 hi = lds_read_tr16(ls + off + 4 * BN);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto frag_a = [&](const uint16_t *ls, int ks, int i) -> bf16x8 {
+    if constexpr (AT) return tr_frag(ls, tr_base_a, i, ks);
+    else return *reinterpret_cast<const bf16x8 *>(ls + a_row + i * 32 * DK + (ks ? fch1 : fch0));
+  };
+  auto frag_b = [&](const uint16_t *ls, int ks, int j) -> bf16x8 {
+    if constexpr (BT) return tr_frag(ls, tr_base_b, j, ks);
+    else return *reinterpret_cast<const bf16x8 *>(ls + b_row[j] + (ks ? fch1 : fch0));
+  };
 
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -388,12 +495,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
     const uint16_t *ls = slot(S);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks ? fch1 : fch0;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-        fa[set][ks][i] = *reinterpret_cast<const bf16x8 *>(ls + a_row + i * 32 * DK + ch);
+      for (int i = 0; i < MI; ++i) fa[set][ks][i] = frag_a(ls, ks, i);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) fb[set][ks][j] = *reinterpret_cast<const bf16x8 *>(ls + b_row[j] + ch);
+      for (int j = 0; j < NJ; ++j) fb[set][ks][j] = frag_b(ls, ks, j);
     }
   };
   auto mma = [&](auto SET, int ks) {
@@ -460,15 +565,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
             if (more) {  // read rd: K step rd / (MI+NJ), A tiles then B tiles
               const int rd = WAVES == 4 ? t >> 1 : (t >> 2) * 3 + (t & 3);
               const int rks = rd / (MI + NJ), r = rd % (MI + NJ);
-              const int ch = rks ? fch1 : fch0;
-              if (r < MI) fa[set ^ 1][rks][r] = *reinterpret_cast<const bf16x8 *>(ls + a_row + r * 32 * DK + ch);
-              else fb[set ^ 1][rks][r - MI] = *reinterpret_cast<const bf16x8 *>(ls + b_row[r - MI] + ch);
+              if (r < MI) fa[set ^ 1][rks][r] = frag_a(ls, rks, r);
+              else fb[set ^ 1][rks][r - MI] = frag_b(ls, rks, r - MI);
             }
           } else if ((t & 3) == kLoadSlot) {
             if (refill) {
               const int dd = t >> 2, ii = dd >> 1;
-              if ((dd & 1) == 0) dma16(a_off[ii], A + (kt + 5) * DK * 2, dbase + (WAVES * ii + w) * 64 * 16);
-              else dma16(b_off[ii], B + (kt + 5) * DK * 2, dbase + DSTAGE * 2 + (WAVES * ii + w) * 64 * 16);
+              if ((dd & 1) == 0) dma16(a_off[ii], A + (kt + 5) * a_step, dbase + (WAVES * ii + w) * 64 * 16);
+              else dma16(b_off[ii], B + (kt + 5) * b_step, dbase + DSTAGE * 2 + (WAVES * ii + w) * 64 * 16);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -581,7 +685,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   constexpr int CHUNKS = OUT_COLS / 8;  // 16-byte chunks per row
   const int tid = threadIdx.x;
   const int col0 = nt * OUT_COLS;
-  uint8_t *C = static_cast<uint8_t *>(p.C);
+  uint8_t *C = static_cast<uint8_t *>(p.C) + (LAY == LAY_TN ? static_cast<int64_t>(e) * p.c_stride * 2 : 0);
   for (int q = tid; q < DBM * CHUNKS; q += NTH) {
     const int r = q / CHUNKS, c = q - (q / CHUNKS) * CHUNKS;
     if (r >= rows || col0 + c * 8 >= p.n_out) continue;
@@ -919,13 +1023,128 @@ hipError_t launch_fill_offsets(int32_t *dst, int32_t t, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMMs of the backward pass.
+// Grouped GEMMs of the backward pass.  bf16: the recomputed forward GEMM
+// (NT) takes the kernel the forward would (256-row direct-to-LDS, skinny or
+// 128-row); the data-gradient GEMMs (NN) run the 256-row kernel with its B
+// operand staged as [K][N] when K is a multiple of 32; the weight-gradient
+// GEMMs (TN) run it with both operands staged as [K][.] over each group's
+// rows (multiples of 32 by construction).  Everything else (fp32, other K)
+// runs the generic kernel.
+namespace {
+
+enum { BP_GENERIC = 0, BP_DMA = 1, BP_SKINNY = 2, BP_V1 = 3 };
+
+struct BwdPlan {
+  int path;
+  bool split;
+};
+
+BwdPlan plan_bwd(const BwdGemm &g) {
+  BwdPlan b{BP_GENERIC, false};
+  if (g.dtype != 1 || g.E <= 0) return b;
+  const int64_t avg = g.max_rows / g.E;
+  if (g.kind == BWD_TN) {
+    b.path = BP_DMA;
+  } else if (g.kind == BWD_NN) {
+    if (g.K % DK == 0) {
+      b.path = BP_DMA;
+      b.split = g.K / DK >= kSplitMinStages;
+    }
+  } else {
+    if (avg >= kDmaMinAvgRows && g.K % DK == 0) {
+      b.path = BP_DMA;
+      b.split = g.K / DK >= kSplitMinStages;
+    } else if (avg <= kSkinnyMaxAvgRows && g.K % 64 == 0) {
+      b.path = BP_SKINNY;
+    } else {
+      b.path = BP_V1;
+    }
+  }
+  return b;
+}
+
+GemmParams bwd_params(const BwdGemm &g) {
+  GemmParams p{};
+  p.A = g.A;
+  p.lda = g.lda;
+  p.B = g.B;
+  p.ldb = g.ldb;
+  p.b_stride = g.b_stride;
+  p.C = g.C;
+  p.ldc = g.ldc;
+  p.offs = g.offs;
+  p.E = g.E;
+  p.K = g.K;
+  p.n_out = g.N;
+  p.up_off = 0;
+  p.max_rows = g.max_rows;
+  p.c_stride = g.c_stride;
+  p.m_rows = g.M;
+  p.units = round_units();
+  p.max_split = 1;
+  return p;
+}
+
+hipError_t run_bwd_dma(GemmParams p, int kind, hipStream_t st) {
+  constexpr int W = kDmaWaves;
+  if (kind == BWD_TN) {
+    p.m_tiles = (p.m_rows + DBM - 1) / DBM;
+    p.n_tiles = (p.n_out + BN - 1) / BN;
+    const int64_t blocks = static_cast<int64_t>(p.E) * p.m_tiles * p.n_tiles;
+    if (blocks <= 0) return hipSuccess;
+    gemm_bf16_dma_kernel<ACT_NONE, W, LAY_TN><<<blocks, W * kWave, 0, st>>>(p);
+    return hipGetLastError();
+  }
+  p.m_tiles = static_cast<int>(mtile_bound(p.max_rows, p.E, DBM));
+  p.n_tiles = (p.n_out + BN - 1) / BN;
+  const int64_t tiles = static_cast<int64_t>(p.m_tiles) * p.n_tiles;
+  if (tiles <= 0) return hipSuccess;
+  const int64_t blocks = tiles + p.units;
+  const bool reduce = p.max_split > 1 && p.slots > 1;
+  if (kind == BWD_NN) gemm_bf16_dma_kernel<ACT_NONE, W, LAY_NN><<<blocks, W * kWave, 0, st>>>(p);
+  else gemm_bf16_dma_kernel<ACT_NONE, W, LAY_NT><<<blocks, W * kWave, 0, st>>>(p);
+  if (reduce) split_reduce_kernel<ACT_NONE, W><<<1024, kThreads, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 size_t bwd_gemm_scratch_bytes(const BwdGemm &g) {
-  (void)g;
+  if (g.max_rows <= 0) return 0;
+  const BwdPlan b = plan_bwd(g);
+  if (b.path == BP_DMA && b.split) {
+    const int64_t mt = mtile_bound(g.max_rows, g.E, DBM);
+    const int64_t nt = (g.N + BN - 1) / BN;
+    return static_cast<size_t>(std::min<int64_t>(kSplitUnits, mt * nt * kMaxSplit)) * kPartTileBytes;
+  }
+  if (b.path == BP_SKINNY) return static_cast<size_t>(kSkinnyMaxPieces) * skinny_part_tile_bytes(64);
   return 0;
 }
 
 hipError_t launch_bwd_gemm(const BwdGemm &g, hipStream_t st) {
+  const BwdPlan b = plan_bwd(g);
+  const size_t need = bwd_gemm_scratch_bytes(g);
+  if (need > 0 && (g.scratch == nullptr || g.scratch_bytes < need)) return hipErrorInvalidValue;
+  if (b.path == BP_DMA) {
+    GemmParams p = bwd_params(g);
+    if (b.split) {
+      p.part = static_cast<float *>(g.scratch);
+      p.slots = static_cast<int>(std::min<size_t>(kSplitUnits, need / kPartTileBytes));
+      p.max_split = kMaxSplit;
+    }
+    return run_bwd_dma(p, g.kind, st);
+  }
+  if (b.path == BP_SKINNY) {
+    GemmParams p = bwd_params(g);
+    p.part = static_cast<float *>(g.scratch);
+    p.slots = static_cast<int>(std::min<size_t>(kSkinnyMaxPieces, need / skinny_part_tile_bytes(64)));
+    p.max_split = p.slots > 0 ? kSkinnyMaxSplit : 1;
+    return run_bf16_skinny(p, ACT_NONE, 64, st);
+  }
+  if (b.path == BP_V1) {
+    GemmParams p = bwd_params(g);
+    return g.max_rows / g.E >= kDmaMinAvgRows ? run_bf16<256>(p, ACT_NONE, st) : run_bf16<128>(p, ACT_NONE, st);
+  }
   GenGemmArgs a{};
   a.A = g.A;
   a.B = g.B;

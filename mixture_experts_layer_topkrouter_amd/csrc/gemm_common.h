@@ -36,6 +36,10 @@ struct GemmParams {
   // the skinny one).
   float *part;
   int units, slots, max_split;
+  // backward layouts of the 256-row kernel: C of group e starts c_stride
+  // elements after group e-1's and has m_rows rows (groups of K)
+  int64_t c_stride;
+  int m_rows;
 };
 
 namespace {

@@ -29,6 +29,14 @@ SMALL = {
     "switch_bwd_small": W.small_variant(WL["switch_top1_bf16"], T=500, d=128, E=16, d_ff=192),
     "correlated_ec_bwd_small": W.small_variant(WL["correlated_ec_bf16"], T=400, d=128, E=8, d_ff=160,
                                                ec_capacity=90),
+    # bf16 shapes on the 256-row direct-to-LDS kernel with [K][N] operands:
+    # every GEMM has partial row / column tiles
+    "bwd_dma_partial_tiles": W.small_variant(WL["mixtral_top2_bf16"], T=600, d=384, E=4, d_ff=320),
+    # the data-gradient GEMM dx = dz W1 contracts over 2 * 4096 = 8192: its
+    # last round is cut along K and reduced in a second pass
+    "bwd_ksplit_small": W.small_variant(WL["mixtral_top2_bf16"], T=256, d=128, E=2, d_ff=4096),
+    # decode-sized batch: the recomputed forward GEMM runs the skinny kernel
+    "bwd_decode_small": W.small_variant(WL["mixtral_top2_bf16"], T=64, d=512, E=8, d_ff=1024),
 }
 
 
