@@ -16,7 +16,9 @@ weights and activations fall below the ridge (decode batches, few rows per
 expert);
 ``stages`` gives every stage's time and its algorithmic HBM rate or FLOP rate;
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
-workload on the host cores.
+workload on the host cores.  ``backward`` times moe_layer_bwd (the layer's
+backward pass for a seeded upstream gradient) in a region of its own after
+the forward regions.
 """
 from __future__ import annotations
 
@@ -46,6 +48,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-sample", type=int, default=768, help="tokens the oracle computes for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-steps", type=int, default=20,
+                    help="moe_layer_bwd calls timed after the forward regions (0: skip the backward)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -208,6 +212,28 @@ def main():
     same = bool(torch.equal(y_layer.view(torch.int16) if y_layer.dtype == torch.bfloat16 else y_layer,
                             layer.y.view(torch.int16) if layer.y.dtype == torch.bfloat16 else layer.y))
 
+    # Backward: moe_layer_bwd (recomputed expert pre-activations, data and
+    # weight gradients, router and shared expert) for a seeded dy, after one
+    # forward on the same inputs; HIP events on the stream around each call.
+    bwd = None
+    if args.bwd_steps > 0:
+        dy = moe.to_device(W.make_dy(w, 0))
+        layer.forward()
+        for _ in range(min(args.warmup, 3)):
+            layer.backward(dy)
+        torch.cuda.synchronize()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.bwd_steps)]
+        tb = time.perf_counter()
+        for a, b in bev:
+            a.record(stream)
+            layer.backward(dy)
+            b.record(stream)
+        torch.cuda.synchronize()
+        tb = time.perf_counter() - tb
+        bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bev]))
+        bwd = {"ms": round(bwd_ms, 4), "tokens_per_s": round(T * args.bwd_steps / tb, 1)}
+
     if args.copy_probe_mib:
         a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
@@ -240,6 +266,18 @@ def main():
                 ent["GB/s"] = round(work[n][2] / sec / 1e9, 1)
                 ent["hbm_frac"] = round(work[n][2] / sec / 1e9 / PEAK_HBM_GBS, 4)
         stages[n] = ent
+
+    if bwd is not None:
+        # expert GEMM flops of the backward on the kept rows (no pad rows):
+        # recomputed z (n_up*d_ff x d), dh (d_ff x d), dx (n_up*d_ff x d),
+        # dW2 (d x d_ff), dW1 (n_up*d_ff x d): 2 * rows * d * d_ff * (3 n_up + 2),
+        # and the same over all T tokens for the shared expert
+        n_up = 2 if w.act == 1 else 1
+        gflops = 2 * n_rows * d * w.d_ff * (3 * n_up + 2) + 2 * T * d * w.d_ff_shared * (3 * n_up + 2)
+        peak_b = PEAK_BF16_TFLOPS if w.dtype == W.BF16 else PEAK_F32_TFLOPS
+        tf = gflops / (bwd["ms"] / 1e3) / 1e12
+        bwd.update({"expert_gemm_flops": int(gflops), "TFLOP/s_whole_pass": round(tf, 1),
+                    "frac_of_peak_whole_pass": round(tf / peak_b, 4)})
 
     # The dominant kernel is the grouped expert FFN (every kernel of one
     # moe_expert_ffn call).  Its bound follows from its arithmetic intensity:
@@ -299,6 +337,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
+        "backward": bwd,
         "event_ms_per_step": round(ev_total_ms, 4),
         "layer_fwd_matches_steps": same,
         "parity_max_rel_err_sampled": parity,

@@ -258,6 +258,7 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
  *   dlogits [T,E] fp32      dL/dlogits; the gradient of a logit bias is its
  *                           sum over tokens ([E] bias) or dlogits itself
  *   dx_router [T,d] fp32    dlogits W_r
+ *   router_part             fp32 partials of dW_r over chunks of 512 tokens
  *   xp, dyp, dxp [padded_rows, d]   expert inputs, output gradients (w dy),
  *                           input gradients
  *   z [padded_rows, n_up*d_ff]      pre-activations, then dL/dz
@@ -265,7 +266,7 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
  *   xs, dys, dxs, zs, dhs   the same for the shared expert
  * ------------------------------------------------------------------------ */
 typedef struct {
-  size_t poff, slot_prow, d_slot_w, dlogits, dx_router, router_offset;
+  size_t poff, slot_prow, d_slot_w, dlogits, dx_router, router_offset, router_part;
   size_t xp, dyp, z, dh, dxp;
   size_t shared_offset, xs, dys, zs, dhs, dxs;
   size_t scratch, scratch_bytes, shared_scratch, shared_scratch_bytes;

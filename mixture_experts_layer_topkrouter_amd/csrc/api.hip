@@ -367,6 +367,7 @@ void make_bwd_layout(const moe_config *c, moe_bwd_layout *L) {
   L->dlogits = take(T * E * 4);
   L->dx_router = take(T * d * 4);
   L->router_offset = take(2 * 4);
+  L->router_part = take(static_cast<size_t>((c->num_tokens + moe::kRouterChunk - 1) / moe::kRouterChunk) * E * d * 4);
   L->xp = take(P * d * s);
   L->dyp = take(P * d * s);
   L->z = take(P * n_up * dff * s);
@@ -777,7 +778,9 @@ moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_rou
     g.N = d;
     g.K = E;
     if (moe::launch_gemm_generic(g, 0, cfg->dtype, 0, st) != hipSuccess) return MOE_ERR_HIP;
-    // dW_r = dlogits^T x  ([E,T] x [T,d])
+    // dW_r = dlogits^T x  ([E,T] x [T,d]): fp32 partials over chunks of
+    // kRouterChunk tokens, computed side by side, then added in chunk order
+    const int chunks = (T + moe::kRouterChunk - 1) / moe::kRouterChunk;
     moe::GenGemmArgs h{};
     h.A = dlogits;
     h.a_rs = 1;
@@ -785,15 +788,20 @@ moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_rou
     h.B = x;
     h.b_ks = d;
     h.b_cs = 1;
-    h.C = dw_router;
+    h.C = P(L.router_part);
     h.c_rs = d;
-    h.offs = ro;
-    h.E = 1;
+    h.c_es = static_cast<int64_t>(E) * d;
+    h.offs = nullptr;
+    h.kchunk = moe::kRouterChunk;
+    h.E = chunks;
     h.mode = 1;
     h.max_rows = T;
     h.M = E;
     h.N = d;
-    if (moe::launch_gemm_generic(h, 0, cfg->dtype, cfg->dtype, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gemm_generic(h, 0, cfg->dtype, 0, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_sum_partials(static_cast<const float *>(P(L.router_part)), chunks, static_cast<int64_t>(E) * d,
+                                 cfg->dtype, dw_router, st) != hipSuccess)
+      return MOE_ERR_HIP;
   }
 
   // routed experts

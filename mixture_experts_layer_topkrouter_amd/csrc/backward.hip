@@ -418,6 +418,19 @@ __global__ __launch_bounds__(kThreads) void gather_dx_kernel(GatherDxArgs a) {
   }
 }
 
+// out[j] = sum over g < groups of part[g * n + j] (fixed order), in dtype.
+template <typename TC>
+__global__ __launch_bounds__(kThreads) void sum_partials_kernel(const float *__restrict__ part, int groups, int64_t n,
+                                                                void *__restrict__ out) {
+  for (int64_t j = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; j < n;
+       j += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float s = 0.f;
+    for (int g = 0; g < groups; ++g) s += part[static_cast<int64_t>(g) * n + j];
+    if constexpr (sizeof(TC) == 2) static_cast<uint16_t *>(out)[j] = f32_to_bf16(s);
+    else static_cast<float *>(out)[j] = s;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void zero_kernel(void *__restrict__ p, int64_t n16) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n16;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -457,9 +470,14 @@ __global__ __launch_bounds__(kThreads) void gemm_generic_kernel(GenGemmArgs g) {
     nt = q - mt * g.n_tiles;
     row0 = mt * GT;
     rows = min(GT, g.M - row0);
-    int me;
-    expert_rows(g.offs, e, g.max_rows, &k0, &me);
-    k1 = k0 + me;
+    if (g.offs) {
+      int me;
+      expert_rows(g.offs, e, g.max_rows, &k0, &me);
+      k1 = k0 + me;
+    } else {  // uniform chunks of kchunk contraction rows
+      k0 = static_cast<int>(min(static_cast<int64_t>(e) * g.kchunk, g.max_rows));
+      k1 = static_cast<int>(min(static_cast<int64_t>(k0) + g.kchunk, g.max_rows));
+    }
     c_base = static_cast<int64_t>(e) * g.c_es;
   }
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
@@ -623,6 +641,13 @@ hipError_t launch_gemm_generic(GenGemmArgs g, int a_dt, int b_dt, int c_dt, hipS
   else if (a_dt == 0 && b_dt == 0 && c_dt == 1) MOE_GEN(float, float, uint16_t);
   else return hipErrorInvalidValue;
 #undef MOE_GEN
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_partials(const float *part, int groups, int64_t n, int c_dt, void *out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (c_dt == 1) sum_partials_kernel<uint16_t><<<stream_blocks(n), kThreads, 0, st>>>(part, groups, n, out);
+  else sum_partials_kernel<float><<<stream_blocks(n), kThreads, 0, st>>>(part, groups, n, out);
   return hipGetLastError();
 }
 

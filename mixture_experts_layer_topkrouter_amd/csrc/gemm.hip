@@ -362,6 +362,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   Job job;
   if constexpr (LAY == LAY_TN) {
     if (!map_kgroup_job(p, &job)) return;
+    if (job.ke == 0) {
+      // a group with no rows: its gradient tile is zero (coalesced 16-B stores)
+      uint8_t *C = static_cast<uint8_t *>(p.C) + static_cast<int64_t>(job.e) * p.c_stride * 2;
+      const int c0 = job.nt * BN, ncol = min(BN, p.n_out - c0);
+      for (int q = threadIdx.x; q < job.rows * (BN / 8); q += NTH) {
+        const int r = q / (BN / 8), c = (q - r * (BN / 8)) * 8;
+        if (c < ncol) st16(C + (static_cast<int64_t>(job.row0 + r) * p.ldc + c0 + c) * 2, u32x4{0u, 0u, 0u, 0u});
+      }
+      return;
+    }
   } else {
     if (!map_job(p, p.K / DK, &job)) return;
   }

@@ -137,7 +137,7 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 //   C(r, c) = C[e*c_es + r*c_rs + c]  (e = the group; c_es used in mode 1).
 // mode 0: group e owns rows [offs[e], offs[e+1]) (< max_rows), K fixed.
 // mode 1: group e contracts over [offs[e], offs[e+1]) (< max_rows) and owns
-//         a dense M x N block of C.
+//         a dense M x N block of C; offs NULL: over [e*kchunk, (e+1)*kchunk).
 struct GenGemmArgs {
   const void *A;
   int64_t a_rs, a_ks;
@@ -149,10 +149,16 @@ struct GenGemmArgs {
   int E, mode;
   int64_t max_rows;
   int M, N, K;
+  int64_t kchunk;
   int m_tiles, n_tiles;  // set by the launcher
 };
 // dtypes: 0 fp32, 1 bf16 (A, B, C).
 hipError_t launch_gemm_generic(GenGemmArgs g, int a_dt, int b_dt, int c_dt, hipStream_t st);
+// out[j] = sum over g < groups of part[g*n + j], in a fixed order (c_dt 0 fp32, 1 bf16).
+hipError_t launch_sum_partials(const float *part, int groups, int64_t n, int c_dt, void *out, hipStream_t st);
+// Token chunk of the router weight gradient dW_r = dlogits^T x: each chunk's
+// fp32 partial is computed on its own, then the chunks are added in order.
+constexpr int kRouterChunk = 512;
 
 // The grouped GEMMs of the backward pass: bf16 shapes the direct-to-LDS
 // MFMA kernels take run there (gemm.hip), the rest on the generic kernel.

@@ -62,7 +62,8 @@ class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in _LAYOUT_FIELDS]
 
 
-_BWD_LAYOUT_FIELDS = ["poff", "slot_prow", "d_slot_w", "dlogits", "dx_router", "router_offset", "xp", "dyp", "z",
+_BWD_LAYOUT_FIELDS = ["poff", "slot_prow", "d_slot_w", "dlogits", "dx_router", "router_offset", "router_part",
+                      "xp", "dyp", "z",
                       "dh", "dxp", "shared_offset", "xs", "dys", "zs", "dhs", "dxs", "scratch", "scratch_bytes",
                       "shared_scratch", "shared_scratch_bytes", "padded_rows", "shared_rows", "total"]
 
