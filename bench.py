@@ -18,7 +18,9 @@ expert);
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.  ``backward`` times moe_layer_bwd (the layer's
 backward pass for a seeded upstream gradient) in a region of its own after
-the forward regions.
+the forward regions, in both modes: after a plain forward with the expert
+pre-activations recomputed, and after the training forward that keeps them
+(whose time is reported as ``train_fwd_ms``).
 """
 from __future__ import annotations
 
@@ -218,21 +220,29 @@ def main():
     bwd = None
     if args.bwd_steps > 0:
         dy = moe.to_device(W.make_dy(w, 0))
+
+        def timed(fn, n):
+            for _ in range(min(args.warmup, 3)):
+                fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+        # recompute mode: after a plain forward, the backward re-runs GEMM1
         layer.forward()
-        for _ in range(min(args.warmup, 3)):
-            layer.backward(dy)
-        torch.cuda.synchronize()
-        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.bwd_steps)]
-        tb = time.perf_counter()
-        for a, b in bev:
-            a.record(stream)
-            layer.backward(dy)
-            b.record(stream)
-        torch.cuda.synchronize()
-        tb = time.perf_counter() - tb
-        bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bev]))
-        bwd = {"ms": round(bwd_ms, 4), "tokens_per_s": round(T * args.bwd_steps / tb, 1)}
+        ms_re = timed(lambda: layer.backward(dy, recompute=True), args.bwd_steps)
+        # training mode: the forward keeps the pre-activations, the backward
+        # reads them
+        ms_train_fwd = timed(lambda: layer.forward(train=True), args.bwd_steps)
+        ms_saved = timed(lambda: layer.backward(dy, recompute=False), args.bwd_steps)
+        bwd = {"recompute": {"ms": round(ms_re, 4)}, "saved_z": {"ms": round(ms_saved, 4)},
+               "train_fwd_ms": round(ms_train_fwd, 4),
+               "train_step_tokens_per_s": round(T / ((ms_train_fwd + ms_saved) / 1e3), 1)}
 
     if args.copy_probe_mib:
         a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -269,15 +279,16 @@ def main():
 
     if bwd is not None:
         # expert GEMM flops of the backward on the kept rows (no pad rows):
-        # recomputed z (n_up*d_ff x d), dh (d_ff x d), dx (n_up*d_ff x d),
-        # dW2 (d x d_ff), dW1 (n_up*d_ff x d): 2 * rows * d * d_ff * (3 n_up + 2),
-        # and the same over all T tokens for the shared expert
+        # recomputed z (n_up*d_ff x d; recompute mode only), dh (d_ff x d),
+        # dx (n_up*d_ff x d), dW2 (d x d_ff), dW1 (n_up*d_ff x d), and the same
+        # over all T tokens for the shared expert
         n_up = 2 if w.act == 1 else 1
-        gflops = 2 * n_rows * d * w.d_ff * (3 * n_up + 2) + 2 * T * d * w.d_ff_shared * (3 * n_up + 2)
         peak_b = PEAK_BF16_TFLOPS if w.dtype == W.BF16 else PEAK_F32_TFLOPS
-        tf = gflops / (bwd["ms"] / 1e3) / 1e12
-        bwd.update({"expert_gemm_flops": int(gflops), "TFLOP/s_whole_pass": round(tf, 1),
-                    "frac_of_peak_whole_pass": round(tf / peak_b, 4)})
+        for mode, units in (("recompute", 3 * n_up + 2), ("saved_z", 2 * n_up + 2)):
+            gflops = 2 * (n_rows * w.d_ff + T * w.d_ff_shared) * d * units
+            tf = gflops / (bwd[mode]["ms"] / 1e3) / 1e12
+            bwd[mode].update({"expert_gemm_flops": int(gflops), "TFLOP/s_whole_pass": round(tf, 1),
+                              "frac_of_peak_whole_pass": round(tf / peak_b, 4)})
 
     # The dominant kernel is the grouped expert FFN (every kernel of one
     # moe_expert_ffn call).  Its bound follows from its arithmetic intensity:

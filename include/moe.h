@@ -205,6 +205,8 @@ typedef struct {
   size_t h, y_perm, shared_h, shared_y, scratch, scratch_bytes;
   size_t ffn_scratch, ffn_scratch_bytes;               /* moe_expert_ffn workspace */
   size_t shared_ffn_scratch, shared_ffn_scratch_bytes; /* ... of the shared expert */
+  size_t z, shared_z; /* pre-activations [rows, n_up*d_ff], [T, n_up*d_ff_shared]
+                         kept by moe_layer_fwd_train */
   size_t total; /* bytes the workspace must hold */
 } moe_workspace_layout;
 
@@ -253,6 +255,8 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
  * row buffers = padded_rows (moe_max_rows() + 31 * E); shared-expert buffers
  * have shared_rows = T rounded up to 32 rows.
  *   poff [E+1] int32        slot_prow [slots] int32 (padded row or -1)
+ *   prow_src [padded_rows] int32  forward row of each padded row (-1: pad;
+ *                           written when recompute = 0)
  *   d_slot_w [slots] fp32   dL/dw per slot (top-k [T,k]; ExpertChoice the
  *                           CSR order of moe_permute)
  *   dlogits [T,E] fp32      dL/dlogits; the gradient of a logit bias is its
@@ -266,7 +270,7 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
  *   xs, dys, dxs, zs, dhs   the same for the shared expert
  * ------------------------------------------------------------------------ */
 typedef struct {
-  size_t poff, slot_prow, d_slot_w, dlogits, dx_router, router_offset, router_part;
+  size_t poff, slot_prow, prow_src, d_slot_w, dlogits, dx_router, router_offset, router_part;
   size_t xp, dyp, z, dh, dxp;
   size_t shared_offset, xs, dys, zs, dhs, dxs;
   size_t scratch, scratch_bytes, shared_scratch, shared_scratch_bytes;
@@ -274,6 +278,15 @@ typedef struct {
   size_t total;                    /* bytes the workspace must hold */
 } moe_bwd_layout;
 moe_status moe_layer_bwd_workspace(const moe_config *cfg, moe_bwd_layout *layout);
+/* moe_layer_fwd_train -- moe_layer_fwd for training: the same outputs
+ * (within bf16 rounding: the activation is applied to the pre-activations
+ * after their rounding to dtype), and the expert pre-activations z are kept
+ * in the workspace (layout.z, layout.shared_z) so that moe_layer_bwd can skip
+ * recomputing them (recompute = 0).  Arguments as moe_layer_fwd. */
+moe_status moe_layer_fwd_train(const moe_config *cfg, const void *x, const void *w_router,
+                               const float *logit_bias, int64_t bias_row_stride, const void *w1,
+                               const void *w2, const void *ws1, const void *ws2, void *y, void *workspace,
+                               size_t workspace_bytes, void *stream);
 /* moe_layer_bwd -- gradients of the whole block.
  *   x, w_router, w1, w2, ws1, ws2: as given to moe_layer_fwd.
  *   fwd_workspace: the workspace of a moe_layer_fwd call on the same inputs
@@ -289,8 +302,8 @@ moe_status moe_layer_bwd_workspace(const moe_config *cfg, moe_bwd_layout *layout
 moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_router, const void *w1,
                          const void *w2, const void *ws1, const void *ws2, const void *fwd_workspace,
                          size_t fwd_workspace_bytes, const void *dy, void *dx, void *dw_router, void *dw1,
-                         void *dw2, void *dws1, void *dws2, void *workspace, size_t workspace_bytes,
-                         void *stream);
+                         void *dw2, void *dws1, void *dws2, int32_t recompute, void *workspace,
+                         size_t workspace_bytes, void *stream);
 const char *moe_status_string(moe_status s);
 int32_t moe_abi_version(void);
 

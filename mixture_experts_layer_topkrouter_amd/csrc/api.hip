@@ -166,7 +166,7 @@ size_t ffn_scratch_of(const moe_config *c) {
 
 moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset, const void *w1,
                     const void *w2, void *h, void *y_perm, void *workspace, size_t workspace_bytes,
-                    void *stream) {
+                    void *stream, void *z = nullptr) {
   if (max_rows_of(cfg) == 0) return MOE_OK;  // no rows: nothing to compute, empty buffers may be NULL
   if (!x_perm || !expert_offset || !w1 || !w2 || !h || !y_perm) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) || !aligned16(y_perm))
@@ -191,6 +191,7 @@ moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *ex
   a.y_perm = y_perm;
   a.scratch = workspace;
   a.scratch_bytes = workspace_bytes;
+  a.z = z;
   return hip_status(moe::launch_expert_ffn(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -287,6 +288,10 @@ void make_layout(const moe_config *c, moe_workspace_layout *L) {
   L->y_perm = take(rows * d * s);
   L->shared_h = take(c->d_ff_shared ? T * static_cast<size_t>(c->d_ff_shared) * s : 0);
   L->shared_y = take(c->d_ff_shared ? T * d * s : 0);
+  // pre-activations kept by a training forward (moe_layer_fwd_train)
+  const size_t n_up = c->act == MOE_ACT_SWIGLU ? 2 : 1;
+  L->z = take(rows * n_up * static_cast<size_t>(c->d_ff) * s);
+  L->shared_z = take(c->d_ff_shared ? T * n_up * static_cast<size_t>(c->d_ff_shared) * s : 0);
   L->scratch_bytes = ec ? 0 : moe::permute_scratch_bytes(c->num_tokens, c->top_k, c->num_experts);
   L->scratch = take(L->scratch_bytes);
   // the shared expert FFN runs beside the routed one (side stream), so each
@@ -363,6 +368,7 @@ void make_bwd_layout(const moe_config *c, moe_bwd_layout *L) {
   L->shared_rows = Ts;
   L->poff = take((E + 1) * 4);
   L->slot_prow = take(nslots * 4);
+  L->prow_src = take(P * 4);
   L->d_slot_w = take(nslots * 4);
   L->dlogits = take(T * E * 4);
   L->dx_router = take(T * d * 4);
@@ -392,7 +398,8 @@ void make_bwd_layout(const moe_config *c, moe_bwd_layout *L) {
 // e are [offs[e], offs[e+1]), multiples of 32, pad rows zero.
 moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const int32_t *offs, const void *w1,
                         const void *w2, void *xp, void *dyp, void *z, void *dh, void *dxp, void *dw1, void *dw2,
-                        void *scratch, size_t scratch_bytes, hipStream_t st) {
+                        void *scratch, size_t scratch_bytes, hipStream_t st, const void *z_saved,
+                        const int32_t *z_src, int64_t z_rows) {
   const int n_up = c->act == MOE_ACT_SWIGLU ? 2 : 1, d = c->d_model;
   moe::BwdGemm g = bwd_gemm(c, moe::BWD_NT);
   g.offs = offs;
@@ -400,17 +407,19 @@ moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const
   g.max_rows = rows;
   g.scratch = scratch;
   g.scratch_bytes = scratch_bytes;
-  // z = xp W1^T  (the recomputed forward)
-  g.A = xp;
-  g.lda = d;
-  g.B = w1;
-  g.ldb = d;
-  g.b_stride = static_cast<int64_t>(n_up) * dff * d;
-  g.C = z;
-  g.ldc = static_cast<int64_t>(n_up) * dff;
-  g.N = n_up * dff;
-  g.K = d;
-  if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
+  // z = xp W1^T  (the recomputed forward), unless a training forward kept z
+  if (!z_saved) {
+    g.A = xp;
+    g.lda = d;
+    g.B = w1;
+    g.ldb = d;
+    g.b_stride = static_cast<int64_t>(n_up) * dff * d;
+    g.C = z;
+    g.ldc = static_cast<int64_t>(n_up) * dff;
+    g.N = n_up * dff;
+    g.K = d;
+    if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
+  }
   // dh = dyp W2   (W2_e [d, dff]: K = d rows, N = dff columns)
   g.kind = moe::BWD_NN;
   g.A = dyp;
@@ -424,7 +433,8 @@ moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const
   g.K = d;
   if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
   const int act = c->act == MOE_ACT_SWIGLU ? 2 : 1;  // ACT_SWIGLU / ACT_GELU of the kernels
-  if (moe::launch_act_bwd(c->dtype, act, z, dh, offs + E, rows, dff, st) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_act_bwd(c->dtype, act, z, dh, offs + E, rows, dff, z_saved, z_src, z_rows, st) != hipSuccess)
+    return MOE_ERR_HIP;
   // dxp = dz W1   (W1_e [n_up*dff, d]: K = n_up*dff rows, N = d columns)
   g.A = z;
   g.lda = static_cast<int64_t>(n_up) * dff;
@@ -463,11 +473,83 @@ moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const
   return MOE_OK;
 }
 
+moe_status layer_fwd_impl(const moe_config *cfg, const void *x, const void *w_router, const float *logit_bias,
+                          int64_t bias_row_stride, const void *w1, const void *w2, const void *ws1,
+                          const void *ws2, void *y, void *workspace, size_t workspace_bytes, void *stream,
+                          bool train) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do, empty buffers may be NULL
+  if (!x || !w_router || !w1 || !w2 || !y || !workspace) return MOE_ERR_INVALID_ARG;
+  if (cfg->d_ff_shared > 0 && (!ws1 || !ws2)) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_ERR_INVALID_ARG;
+  if (bias_row_stride != 0 && bias_row_stride != cfg->num_experts) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w2) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->d_ff_shared > 0 && (!aligned16(ws1) || !aligned16(ws2))) return MOE_ERR_INVALID_ARG;
+  moe_workspace_layout L;
+  make_layout(cfg, &L);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const int64_t rows = max_rows_of(cfg);
+  if (!gemm_fits(cfg, rows, cfg->d_ff)) return MOE_ERR_UNSUPPORTED;
+  moe_config sc = shared_config(cfg);
+  if (cfg->d_ff_shared > 0 && !gemm_fits(&sc, cfg->num_tokens, cfg->d_ff_shared)) return MOE_ERR_UNSUPPORTED;
+
+  char *ws = static_cast<char *>(workspace);
+  auto P = [&](size_t off) { return static_cast<void *>(ws + off); };
+  const bool ec = cfg->routing == MOE_EXPERT_CHOICE;
+  float *logits = static_cast<float *>(P(L.logits));
+  int32_t *topk_idx = static_cast<int32_t *>(P(L.topk_idx));
+  float *topk_w = static_cast<float *>(P(L.topk_w));
+  float *scores = static_cast<float *>(P(L.scores));
+  int32_t *ec_token = static_cast<int32_t *>(P(L.ec_token));
+  float *ec_w = static_cast<float *>(P(L.ec_w));
+  int32_t *slot_row = static_cast<int32_t *>(P(L.slot_row));
+  float *slot_w = ec ? static_cast<float *>(P(L.slot_w)) : topk_w;
+  int32_t *tok_ptr = static_cast<int32_t *>(P(L.tok_ptr));
+  int32_t *expert_offset = static_cast<int32_t *>(P(L.expert_offset));
+
+  // Shared expert ([P3] top_k paragraph; overlapped as P1's shared-expert
+  // overlap): it reads only x, so it is forked onto a side stream right away
+  // and runs beside routing, permutation and the routed experts; the main
+  // stream waits for it just before the combine.
+  hipStream_t main_st = static_cast<hipStream_t>(stream);
+  const void *y_shared = nullptr;
+  hipEvent_t join = nullptr;
+  if (cfg->d_ff_shared > 0) {
+    SideStream *side = side_stream();
+    if (!side) return MOE_ERR_HIP;
+    if (hipEventRecord(side->fork, main_st) != hipSuccess ||
+        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+      return MOE_ERR_HIP;
+    int32_t *so = static_cast<int32_t *>(P(L.shared_offset));
+    if (moe::launch_fill_offsets(so, cfg->num_tokens, side->stream) != hipSuccess) return MOE_ERR_HIP;
+    s = ffn_impl(&sc, x, so, ws1, ws2, P(L.shared_h), P(L.shared_y), P(L.shared_ffn_scratch),
+                 L.shared_ffn_scratch_bytes, side->stream, train ? P(L.shared_z) : nullptr);
+    if (s != MOE_OK) return s;
+    if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_ERR_HIP;
+    join = side->join;
+    y_shared = P(L.shared_y);
+  }
+  s = route_impl(cfg, x, w_router, logit_bias, bias_row_stride, logits, topk_idx, topk_w, scores, ec_token, ec_w,
+                 stream);
+  if (s != MOE_OK) return s;
+  s = permute_impl(cfg, x, topk_idx, ec_token, ec_w, P(L.x_perm), static_cast<int32_t *>(P(L.row_token)), slot_row,
+                   static_cast<float *>(P(L.slot_w)), tok_ptr, static_cast<int32_t *>(P(L.expert_count)),
+                   static_cast<int32_t *>(P(L.expert_load)), expert_offset, P(L.scratch), L.scratch_bytes, stream);
+  if (s != MOE_OK) return s;
+  s = ffn_impl(cfg, P(L.x_perm), expert_offset, w1, w2, P(L.h), P(L.y_perm), P(L.ffn_scratch),
+               L.ffn_scratch_bytes, stream, train ? P(L.z) : nullptr);
+  if (s != MOE_OK) return s;
+  if (join && hipStreamWaitEvent(main_st, join, 0) != hipSuccess) return MOE_ERR_HIP;
+  return unpermute_impl(cfg, P(L.y_perm), tok_ptr, slot_row, slot_w, y_shared, y, stream);
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 4; }
+int32_t moe_abi_version(void) { return 5; }
 
 const char *moe_status_string(moe_status s) {
   switch (s) {
@@ -554,72 +636,15 @@ moe_status moe_layer_workspace(const moe_config *cfg, moe_workspace_layout *layo
 moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_router, const float *logit_bias,
                          int64_t bias_row_stride, const void *w1, const void *w2, const void *ws1,
                          const void *ws2, void *y, void *workspace, size_t workspace_bytes, void *stream) {
-  moe_status s = check_config(cfg);
-  if (s != MOE_OK) return s;
-  if (cfg->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do, empty buffers may be NULL
-  if (!x || !w_router || !w1 || !w2 || !y || !workspace) return MOE_ERR_INVALID_ARG;
-  if (cfg->d_ff_shared > 0 && (!ws1 || !ws2)) return MOE_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_ERR_INVALID_ARG;
-  if (bias_row_stride != 0 && bias_row_stride != cfg->num_experts) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w2) || !aligned16(y))
-    return MOE_ERR_INVALID_ARG;
-  if (cfg->d_ff_shared > 0 && (!aligned16(ws1) || !aligned16(ws2))) return MOE_ERR_INVALID_ARG;
-  moe_workspace_layout L;
-  make_layout(cfg, &L);
-  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
-  const int64_t rows = max_rows_of(cfg);
-  if (!gemm_fits(cfg, rows, cfg->d_ff)) return MOE_ERR_UNSUPPORTED;
-  moe_config sc = shared_config(cfg);
-  if (cfg->d_ff_shared > 0 && !gemm_fits(&sc, cfg->num_tokens, cfg->d_ff_shared)) return MOE_ERR_UNSUPPORTED;
+  return layer_fwd_impl(cfg, x, w_router, logit_bias, bias_row_stride, w1, w2, ws1, ws2, y, workspace,
+                        workspace_bytes, stream, false);
+}
 
-  char *ws = static_cast<char *>(workspace);
-  auto P = [&](size_t off) { return static_cast<void *>(ws + off); };
-  const bool ec = cfg->routing == MOE_EXPERT_CHOICE;
-  float *logits = static_cast<float *>(P(L.logits));
-  int32_t *topk_idx = static_cast<int32_t *>(P(L.topk_idx));
-  float *topk_w = static_cast<float *>(P(L.topk_w));
-  float *scores = static_cast<float *>(P(L.scores));
-  int32_t *ec_token = static_cast<int32_t *>(P(L.ec_token));
-  float *ec_w = static_cast<float *>(P(L.ec_w));
-  int32_t *slot_row = static_cast<int32_t *>(P(L.slot_row));
-  float *slot_w = ec ? static_cast<float *>(P(L.slot_w)) : topk_w;
-  int32_t *tok_ptr = static_cast<int32_t *>(P(L.tok_ptr));
-  int32_t *expert_offset = static_cast<int32_t *>(P(L.expert_offset));
-
-  // Shared expert ([P3] top_k paragraph; overlapped as P1's shared-expert
-  // overlap): it reads only x, so it is forked onto a side stream right away
-  // and runs beside routing, permutation and the routed experts; the main
-  // stream waits for it just before the combine.
-  hipStream_t main_st = static_cast<hipStream_t>(stream);
-  const void *y_shared = nullptr;
-  hipEvent_t join = nullptr;
-  if (cfg->d_ff_shared > 0) {
-    SideStream *side = side_stream();
-    if (!side) return MOE_ERR_HIP;
-    if (hipEventRecord(side->fork, main_st) != hipSuccess ||
-        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
-      return MOE_ERR_HIP;
-    int32_t *so = static_cast<int32_t *>(P(L.shared_offset));
-    if (moe::launch_fill_offsets(so, cfg->num_tokens, side->stream) != hipSuccess) return MOE_ERR_HIP;
-    s = ffn_impl(&sc, x, so, ws1, ws2, P(L.shared_h), P(L.shared_y), P(L.shared_ffn_scratch),
-                 L.shared_ffn_scratch_bytes, side->stream);
-    if (s != MOE_OK) return s;
-    if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_ERR_HIP;
-    join = side->join;
-    y_shared = P(L.shared_y);
-  }
-  s = route_impl(cfg, x, w_router, logit_bias, bias_row_stride, logits, topk_idx, topk_w, scores, ec_token, ec_w,
-                 stream);
-  if (s != MOE_OK) return s;
-  s = permute_impl(cfg, x, topk_idx, ec_token, ec_w, P(L.x_perm), static_cast<int32_t *>(P(L.row_token)), slot_row,
-                   static_cast<float *>(P(L.slot_w)), tok_ptr, static_cast<int32_t *>(P(L.expert_count)),
-                   static_cast<int32_t *>(P(L.expert_load)), expert_offset, P(L.scratch), L.scratch_bytes, stream);
-  if (s != MOE_OK) return s;
-  s = ffn_impl(cfg, P(L.x_perm), expert_offset, w1, w2, P(L.h), P(L.y_perm), P(L.ffn_scratch),
-               L.ffn_scratch_bytes, stream);
-  if (s != MOE_OK) return s;
-  if (join && hipStreamWaitEvent(main_st, join, 0) != hipSuccess) return MOE_ERR_HIP;
-  return unpermute_impl(cfg, P(L.y_perm), tok_ptr, slot_row, slot_w, y_shared, y, stream);
+moe_status moe_layer_fwd_train(const moe_config *cfg, const void *x, const void *w_router, const float *logit_bias,
+                               int64_t bias_row_stride, const void *w1, const void *w2, const void *ws1,
+                               const void *ws2, void *y, void *workspace, size_t workspace_bytes, void *stream) {
+  return layer_fwd_impl(cfg, x, w_router, logit_bias, bias_row_stride, w1, w2, ws1, ws2, y, workspace,
+                        workspace_bytes, stream, true);
 }
 
 moe_status moe_layer_bwd_workspace(const moe_config *cfg, moe_bwd_layout *layout) {
@@ -633,8 +658,8 @@ moe_status moe_layer_bwd_workspace(const moe_config *cfg, moe_bwd_layout *layout
 moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_router, const void *w1,
                          const void *w2, const void *ws1, const void *ws2, const void *fwd_workspace,
                          size_t fwd_workspace_bytes, const void *dy, void *dx, void *dw_router, void *dw1,
-                         void *dw2, void *dws1, void *dws2, void *workspace, size_t workspace_bytes,
-                         void *stream) {
+                         void *dw2, void *dws1, void *dws2, int32_t recompute, void *workspace,
+                         size_t workspace_bytes, void *stream) {
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
   const bool shared = cfg->d_ff_shared > 0;
@@ -705,7 +730,8 @@ moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_rou
         moe::launch_pad_copy(dy, P(L.dys), T, Ts, static_cast<size_t>(d) * es, side->stream) != hipSuccess)
       return MOE_ERR_HIP;
     s = ffn_bwd_impl(&sc, 1, cfg->d_ff_shared, Ts, so, ws1, ws2, P(L.xs), P(L.dys), P(L.zs), P(L.dhs), P(L.dxs),
-                     dws1, dws2, P(L.shared_scratch), L.shared_scratch_bytes, side->stream);
+                     dws1, dws2, P(L.shared_scratch), L.shared_scratch_bytes, side->stream,
+                     recompute ? nullptr : F_(F.shared_z), nullptr, T);
     if (s != MOE_OK) return s;
     if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_ERR_HIP;
     join = side->join;
@@ -737,8 +763,11 @@ moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_rou
   u.xp = P(L.xp);
   u.d_slot_w = d_slot_w;
   u.slot_prow = slot_prow;
+  int32_t *prow_src = recompute ? nullptr : static_cast<int32_t *>(P(L.prow_src));
+  u.prow_src = prow_src;
   if (moe::launch_unpermute_bwd(u, st) != hipSuccess) return MOE_ERR_HIP;
-  if (moe::launch_pad_zero(poff, count, E, prows, static_cast<size_t>(d) * es, P(L.xp), P(L.dyp), st) != hipSuccess)
+  if (moe::launch_pad_zero(poff, count, E, prows, static_cast<size_t>(d) * es, P(L.xp), P(L.dyp), prow_src, st) !=
+      hipSuccess)
     return MOE_ERR_HIP;
 
   // gate gradient, then the router's linear layer
@@ -806,7 +835,7 @@ moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_rou
 
   // routed experts
   s = ffn_bwd_impl(cfg, E, cfg->d_ff, prows, poff, w1, w2, P(L.xp), P(L.dyp), P(L.z), P(L.dh), P(L.dxp), dw1, dw2,
-                   P(L.scratch), L.scratch_bytes, st);
+                   P(L.scratch), L.scratch_bytes, st, recompute ? nullptr : F_(F.z), prow_src, max_rows_of(cfg));
   if (s != MOE_OK) return s;
 
   // dx: the permutation's backward (each token gathers its copies'

@@ -173,6 +173,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_bwd_kernel(BwdUnpermuteArg
     if (l == 0) {
       a.d_slot_w[s] = dot;
       a.slot_prow[s] = p;
+      if (a.prow_src) a.prow_src[p] = r;
     }
   }
 }
@@ -181,11 +182,14 @@ __global__ __launch_bounds__(kThreads) void unpermute_bwd_kernel(BwdUnpermuteArg
 // up to two row buffers (one workgroup per expert).
 __global__ __launch_bounds__(kThreads) void pad_zero_kernel(const int32_t *__restrict__ poff,
                                                             const int32_t *__restrict__ count, int64_t prows,
-                                                            size_t row_bytes, void *b0, void *b1) {
+                                                            size_t row_bytes, void *b0, void *b1,
+                                                            int32_t *__restrict__ prow_src) {
   const int e = blockIdx.x;
   const int64_t p0 = min(max(static_cast<int64_t>(poff[e]), static_cast<int64_t>(0)), prows);
   const int64_t p1 = min(max(static_cast<int64_t>(poff[e + 1]), p0), prows);
   const int64_t first = min(p0 + max(count[e], 0), p1);
+  if (prow_src)
+    for (int64_t r = first + threadIdx.x; r < p1; r += blockDim.x) prow_src[r] = -1;
   const int64_t nch = static_cast<int64_t>(row_bytes / 16);
   const int64_t n = (p1 - first) * nch;
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
@@ -303,32 +307,46 @@ __device__ __forceinline__ float gelu_grad_f(float z) {
 }
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + expf(-z)); }
 
-// Activation backward on rows [0, rows_of) of the padded layout, in place:
+// Activation backward on rows [0, rows_of) of the padded layout:
 //   GELU:   z -> dz = dh * gelu'(z),         dh -> h = gelu(z)
 //   SwiGLU: (a, b) -> (dh * b * silu'(a), dh * silu(a)),  dh -> h = silu(a) b
 // z is [rows, n_up*dff] (SwiGLU: gate columns, then up columns), dh [rows, dff].
+// The pre-activations are read from z itself (in place), or, when z_src is
+// given, from row src_row(p) of z_src (the forward's saved z): src[p] when a
+// map is given (-1: a pad row, whose z is 0), else p itself for p < src_rows.
 template <bool BF16, int ACT>
 __global__ __launch_bounds__(kThreads) void act_bwd_kernel(void *__restrict__ z, void *__restrict__ dh,
                                                            const int32_t *__restrict__ rows_of, int64_t prows,
-                                                           int dff) {
+                                                           int dff, const void *__restrict__ z_src,
+                                                           const int32_t *__restrict__ src, int64_t src_rows) {
   constexpr int kElems = BF16 ? 8 : 4;
   const int64_t rows = min(max(static_cast<int64_t>(*rows_of), static_cast<int64_t>(0)), prows);
   const int nch = dff / kElems;
   const int64_t n = rows * nch;
   const int n_up = ACT == ACT_SWIGLU ? 2 : 1;
   const size_t es = BF16 ? 2 : 4;
+  const size_t zrow = static_cast<size_t>(n_up) * dff * es;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t r = i / nch;
     const int c = static_cast<int>(i - r * nch);
-    uint8_t *zr = static_cast<uint8_t *>(z) + static_cast<size_t>(r) * n_up * dff * es;
+    uint8_t *zr = static_cast<uint8_t *>(z) + static_cast<size_t>(r) * zrow;
     uint8_t *dr = static_cast<uint8_t *>(dh) + static_cast<size_t>(r) * dff * es;
+    const uint8_t *zin = zr;
+    bool live = true;
+    if (z_src) {
+      const int64_t q = src ? static_cast<int64_t>(src[r]) : (r < src_rows ? r : -1);
+      live = q >= 0 && q < src_rows;
+      zin = static_cast<const uint8_t *>(z_src) + static_cast<size_t>(live ? q : 0) * zrow;
+    }
     float fa[kElems], fg[kElems];
-    unpack<BF16>(ld16(zr + static_cast<size_t>(c) * 16), fa);
+    unpack<BF16>(live ? ld16(zin + static_cast<size_t>(c) * 16) : u32x4{0u, 0u, 0u, 0u}, fa);
     unpack<BF16>(ld16(dr + static_cast<size_t>(c) * 16), fg);
     if (ACT == ACT_SWIGLU) {
       float fb[kElems], da[kElems], db[kElems], h[kElems];
-      unpack<BF16>(ld16(zr + static_cast<size_t>(dff) * es + static_cast<size_t>(c) * 16), fb);
+      unpack<BF16>(live ? ld16(zin + static_cast<size_t>(dff) * es + static_cast<size_t>(c) * 16)
+                        : u32x4{0u, 0u, 0u, 0u},
+                   fb);
 #pragma unroll
       for (int q = 0; q < kElems; ++q) {
         const float sg = sigmoid_f(fa[q]);
@@ -350,6 +368,40 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(void *__restrict__ z,
       st16(zr + static_cast<size_t>(c) * 16, pack<BF16>(dz));
       st16(dr + static_cast<size_t>(c) * 16, pack<BF16>(h));
     }
+  }
+}
+
+// Activation of a training forward (the expert GEMM1 wrote its raw
+// pre-activations z, which the backward reuses): rows [0, rows_of),
+//   GELU: h = gelu(z);  SwiGLU: h = silu(a) * b  (z = [a | b]).
+template <bool BF16, int ACT>
+__global__ __launch_bounds__(kThreads) void act_fwd_kernel(const void *__restrict__ z, void *__restrict__ h,
+                                                           const int32_t *__restrict__ rows_of, int64_t max_rows,
+                                                           int dff) {
+  constexpr int kElems = BF16 ? 8 : 4;
+  const int64_t rows = min(max(static_cast<int64_t>(*rows_of), static_cast<int64_t>(0)), max_rows);
+  const int nch = dff / kElems;
+  const int64_t n = rows * nch;
+  const int n_up = ACT == ACT_SWIGLU ? 2 : 1;
+  const size_t es = BF16 ? 2 : 4;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = i / nch;
+    const int c = static_cast<int>(i - r * nch);
+    const uint8_t *zr = static_cast<const uint8_t *>(z) + static_cast<size_t>(r) * n_up * dff * es;
+    float fa[kElems], out[kElems];
+    unpack<BF16>(ld16(zr + static_cast<size_t>(c) * 16), fa);
+    if (ACT == ACT_SWIGLU) {
+      float fb[kElems];
+      unpack<BF16>(ld16(zr + static_cast<size_t>(dff) * es + static_cast<size_t>(c) * 16), fb);
+#pragma unroll
+      for (int q = 0; q < kElems; ++q) out[q] = fa[q] * sigmoid_f(fa[q]) * fb[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < kElems; ++q) out[q] = gelu_f(fa[q]);
+    }
+    st16(static_cast<uint8_t *>(h) + (static_cast<size_t>(r) * dff + static_cast<size_t>(c) * kElems) * es,
+         pack<BF16>(out));
   }
 }
 
@@ -569,8 +621,8 @@ hipError_t launch_unpermute_bwd(const BwdUnpermuteArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_pad_zero(const int32_t *poff, const int32_t *count, int E, int64_t prows, size_t row_bytes,
-                           void *b0, void *b1, hipStream_t st) {
-  pad_zero_kernel<<<E, kThreads, 0, st>>>(poff, count, prows, row_bytes, b0, b1);
+                           void *b0, void *b1, int32_t *prow_src, hipStream_t st) {
+  pad_zero_kernel<<<E, kThreads, 0, st>>>(poff, count, prows, row_bytes, b0, b1, prow_src);
   return hipGetLastError();
 }
 
@@ -589,16 +641,34 @@ hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_act_bwd(int dtype, int act, void *z, void *dh, const int32_t *rows_of, int64_t prows, int dff,
-                          hipStream_t st) {
+                          const void *z_src, const int32_t *src, int64_t src_rows, hipStream_t st) {
   if (prows == 0) return hipSuccess;
   const int blocks = stream_blocks(prows * (dff / (dtype == 1 ? 8 : 4)));
+#define MOE_ACTB(B, A) act_bwd_kernel<B, A><<<blocks, kThreads, 0, st>>>(z, dh, rows_of, prows, dff, z_src, src, src_rows)
   if (dtype == 1) {
-    if (act == ACT_SWIGLU) act_bwd_kernel<true, ACT_SWIGLU><<<blocks, kThreads, 0, st>>>(z, dh, rows_of, prows, dff);
-    else act_bwd_kernel<true, ACT_GELU><<<blocks, kThreads, 0, st>>>(z, dh, rows_of, prows, dff);
+    if (act == ACT_SWIGLU) MOE_ACTB(true, ACT_SWIGLU);
+    else MOE_ACTB(true, ACT_GELU);
   } else {
-    if (act == ACT_SWIGLU) act_bwd_kernel<false, ACT_SWIGLU><<<blocks, kThreads, 0, st>>>(z, dh, rows_of, prows, dff);
-    else act_bwd_kernel<false, ACT_GELU><<<blocks, kThreads, 0, st>>>(z, dh, rows_of, prows, dff);
+    if (act == ACT_SWIGLU) MOE_ACTB(false, ACT_SWIGLU);
+    else MOE_ACTB(false, ACT_GELU);
   }
+#undef MOE_ACTB
+  return hipGetLastError();
+}
+
+hipError_t launch_act_fwd(int dtype, int act, const void *z, void *h, const int32_t *rows_of, int64_t max_rows,
+                          int dff, hipStream_t st) {
+  if (max_rows == 0) return hipSuccess;
+  const int blocks = stream_blocks(max_rows * (dff / (dtype == 1 ? 8 : 4)));
+#define MOE_ACTF(B, A) act_fwd_kernel<B, A><<<blocks, kThreads, 0, st>>>(z, h, rows_of, max_rows, dff)
+  if (dtype == 1) {
+    if (act == ACT_SWIGLU) MOE_ACTF(true, ACT_SWIGLU);
+    else MOE_ACTF(true, ACT_GELU);
+  } else {
+    if (act == ACT_SWIGLU) MOE_ACTF(false, ACT_SWIGLU);
+    else MOE_ACTF(false, ACT_GELU);
+  }
+#undef MOE_ACTF
   return hipGetLastError();
 }
 

@@ -978,7 +978,15 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   g1.units = units;
   g1.slots = slots;
   g1.max_split = f.split1 ? kMaxSplit : 1;
-  const int act1 = a.act == 1 ? ACT_SWIGLU : ACT_GELU;
+  // training forward: GEMM1 keeps its raw pre-activations z (both SwiGLU
+  // halves), a second pass applies the activation
+  int act1 = a.act == 1 ? ACT_SWIGLU : ACT_GELU;
+  if (a.z) {
+    g1.C = a.z;
+    g1.ldc = static_cast<int64_t>(n_up) * a.d_ff;
+    g1.n_out = n_up * a.d_ff;
+    act1 = ACT_NONE;
+  }
   hipError_t err;
   if (a.dtype == 0) {
     err = run_f32(g1, act1, st);
@@ -992,6 +1000,9 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
     err = f.bm == 256 ? run_bf16<256>(g1, act1, st) : run_bf16<128>(g1, act1, st);
   }
   if (err != hipSuccess) return err;
+  if (a.z && (err = launch_act_fwd(a.dtype, a.act == 1 ? ACT_SWIGLU : ACT_GELU, a.z, a.h, a.expert_offset + a.E,
+                                   a.max_rows, a.d_ff, st)) != hipSuccess)
+    return err;
   GemmParams g2{};
   g2.A = a.h;
   g2.lda = a.d_ff;

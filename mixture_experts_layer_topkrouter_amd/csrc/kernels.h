@@ -65,6 +65,7 @@ struct FfnArgs {
   void *h, *y_perm;
   void *scratch;  // ffn_scratch_bytes() bytes, 256-B aligned
   size_t scratch_bytes;
+  void *z;        // optional [max_rows, n_up*d_ff]: keep the pre-activations
 };
 size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows);
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st);
@@ -101,6 +102,7 @@ struct BwdUnpermuteArgs {
   void *dyp, *xp;
   float *d_slot_w;
   int32_t *slot_prow;
+  int32_t *prow_src;  // optional [prows]: compact row of each padded row
 };
 hipError_t launch_unpermute_bwd(const BwdUnpermuteArgs &a, hipStream_t st);
 
@@ -125,11 +127,13 @@ hipError_t launch_gather_dx(const GatherDxArgs &a, hipStream_t st);
 
 hipError_t launch_bwd_offsets(const int32_t *count, int E, int64_t max_rows, int32_t *poff, hipStream_t st);
 hipError_t launch_pad_zero(const int32_t *poff, const int32_t *count, int E, int64_t prows, size_t row_bytes,
-                           void *b0, void *b1, hipStream_t st);
+                           void *b0, void *b1, int32_t *prow_src, hipStream_t st);
 hipError_t launch_pad_copy(const void *src, void *dst, int64_t rows, int64_t prows, size_t row_bytes,
                            hipStream_t st);
 hipError_t launch_act_bwd(int dtype, int act, void *z, void *dh, const int32_t *rows_of, int64_t prows, int dff,
-                          hipStream_t st);
+                          const void *z_src, const int32_t *src, int64_t src_rows, hipStream_t st);
+hipError_t launch_act_fwd(int dtype, int act, const void *z, void *h, const int32_t *rows_of, int64_t max_rows,
+                          int dff, hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 
 // Generic grouped GEMM C(r, c) = sum_k A(r, k) B(k, c), element strides:

@@ -55,14 +55,15 @@ class MoeConfig(ctypes.Structure):
 _LAYOUT_FIELDS = ["logits", "topk_idx", "topk_w", "scores", "ec_token", "ec_w", "x_perm", "row_token",
                   "slot_row", "slot_w", "tok_ptr", "expert_count", "expert_load", "expert_offset",
                   "shared_offset", "h", "y_perm", "shared_h", "shared_y", "scratch", "scratch_bytes",
-                  "ffn_scratch", "ffn_scratch_bytes", "shared_ffn_scratch", "shared_ffn_scratch_bytes", "total"]
+                  "ffn_scratch", "ffn_scratch_bytes", "shared_ffn_scratch", "shared_ffn_scratch_bytes", "z",
+                  "shared_z", "total"]
 
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in _LAYOUT_FIELDS]
 
 
-_BWD_LAYOUT_FIELDS = ["poff", "slot_prow", "d_slot_w", "dlogits", "dx_router", "router_offset", "router_part",
+_BWD_LAYOUT_FIELDS = ["poff", "slot_prow", "prow_src", "d_slot_w", "dlogits", "dx_router", "router_offset", "router_part",
                       "xp", "dyp", "z",
                       "dh", "dxp", "shared_offset", "xs", "dys", "zs", "dhs", "dxs", "scratch", "scratch_bytes",
                       "shared_scratch", "shared_scratch_bytes", "padded_rows", "shared_rows", "total"]
@@ -102,7 +103,8 @@ def load_library() -> ctypes.CDLL:
         "moe_layer_workspace": ([CP, ctypes.POINTER(WorkspaceLayout)], ctypes.c_int),
         "moe_layer_fwd": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_layer_bwd_workspace": ([CP, ctypes.POINTER(BwdLayout)], ctypes.c_int),
-        "moe_layer_bwd": ([CP, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "moe_layer_fwd_train": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "moe_layer_bwd": ([CP, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, ctypes.c_int32, P, sz, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -210,11 +212,14 @@ def layer_workspace(cfg: MoeConfig) -> Dict[str, int]:
 
 
 def layer_fwd(cfg: MoeConfig, x, w_router, w1, w2, y, workspace, *, bias=None, bias_stride: int = 0, ws1=None,
-              ws2=None, stream=None):
+              ws2=None, train: bool = False, stream=None):
+    """moe_layer_fwd, or moe_layer_fwd_train (keeps the expert
+    pre-activations for a backward without recompute) when train is set."""
     nbytes = workspace.numel() * workspace.element_size()
-    _check(load_library().moe_layer_fwd(ctypes.byref(cfg), _p(x), _p(w_router), _p(bias), bias_stride, _p(w1),
-                                        _p(w2), _p(ws1), _p(ws2), _p(y), _p(workspace), nbytes, _stream(stream)),
-           "moe_layer_fwd")
+    lib = load_library()
+    fn = lib.moe_layer_fwd_train if train else lib.moe_layer_fwd
+    _check(fn(ctypes.byref(cfg), _p(x), _p(w_router), _p(bias), bias_stride, _p(w1), _p(w2), _p(ws1), _p(ws2), _p(y),
+              _p(workspace), nbytes, _stream(stream)), "moe_layer_fwd_train" if train else "moe_layer_fwd")
 
 
 def layer_bwd_workspace(cfg: MoeConfig) -> Dict[str, int]:
@@ -224,12 +229,13 @@ def layer_bwd_workspace(cfg: MoeConfig) -> Dict[str, int]:
 
 
 def layer_bwd(cfg: MoeConfig, x, w_router, w1, w2, fwd_workspace, dy, dx, dw_router, dw1, dw2, workspace, *,
-              ws1=None, ws2=None, dws1=None, dws2=None, stream=None):
+              ws1=None, ws2=None, dws1=None, dws2=None, recompute: bool = True, stream=None):
     fbytes = fwd_workspace.numel() * fwd_workspace.element_size()
     nbytes = workspace.numel() * workspace.element_size()
     _check(load_library().moe_layer_bwd(ctypes.byref(cfg), _p(x), _p(w_router), _p(w1), _p(w2), _p(ws1), _p(ws2),
                                         _p(fwd_workspace), fbytes, _p(dy), _p(dx), _p(dw_router), _p(dw1), _p(dw2),
-                                        _p(dws1), _p(dws2), _p(workspace), nbytes, _stream(stream)),
+                                        _p(dws1), _p(dws2), int(bool(recompute)), _p(workspace), nbytes,
+                                        _stream(stream)),
            "moe_layer_bwd")
 
 
@@ -302,10 +308,12 @@ class MoELayer:
         self.workspace = torch.empty(max(self.layout["total"], 256), dtype=torch.uint8, device=device)
         self.y = torch.empty((cfg.num_tokens, cfg.d_model), dtype=torch_dtype(cfg), device=device)
 
-    def forward(self, stream=None) -> torch.Tensor:
+    def forward(self, stream=None, train: bool = False) -> torch.Tensor:
+        """moe_layer_fwd (train=True: moe_layer_fwd_train, which keeps the
+        expert pre-activations for backward(recompute=False))."""
         d = self.dev
         layer_fwd(self.cfg, d.x, d.wr, d.w1, d.w2, self.y, self.workspace, bias=d.bias, bias_stride=d.bias_stride,
-                  ws1=d.ws1, ws2=d.ws2, stream=stream)
+                  ws1=d.ws1, ws2=d.ws2, train=train, stream=stream)
         return self.y
 
     def shapes(self) -> Dict[str, tuple]:
@@ -352,14 +360,16 @@ class MoELayer:
         self.dws1 = None if d.ws1 is None else torch.empty_like(d.ws1)
         self.dws2 = None if d.ws2 is None else torch.empty_like(d.ws2)
 
-    def backward(self, dy: torch.Tensor, stream=None):
+    def backward(self, dy: torch.Tensor, recompute: bool = True, stream=None):
         """moe_layer_bwd for upstream gradient dy, after forward() on the same
-        inputs; fills self.dx, dwr, dw1, dw2 (and dws1, dws2)."""
+        inputs (recompute=False needs forward(train=True)); fills self.dx,
+        dwr, dw1, dw2 (and dws1, dws2)."""
         if not hasattr(self, "bwd_workspace"):
             self.alloc_grads(dy.device)
         d = self.dev
         layer_bwd(self.cfg, d.x, d.wr, d.w1, d.w2, self.workspace, dy, self.dx, self.dwr, self.dw1, self.dw2,
-                  self.bwd_workspace, ws1=d.ws1, ws2=d.ws2, dws1=self.dws1, dws2=self.dws2, stream=stream)
+                  self.bwd_workspace, ws1=d.ws1, ws2=d.ws2, dws1=self.dws1, dws2=self.dws2, recompute=recompute,
+                  stream=stream)
 
     def bwd_view(self, name: str) -> torch.Tensor:
         """A typed view of one intermediate of the backward workspace."""

@@ -22,7 +22,7 @@ def test_library_exports_every_header_symbol():
 
 def test_status_strings_and_version():
     lib = moe.load_library()
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
 
@@ -154,11 +154,11 @@ def test_backward_argument_errors():
     F = moe.layer_workspace(cfg)["total"]
     B = moe.layer_bwd_workspace(cfg)["total"]
     args = lambda fwd_bytes, ws_bytes, dx=fake: (ctypes.byref(cfg), fake, fake, fake, fake, None, None, fake,
-                                                 fwd_bytes, fake, dx, fake, fake, fake, None, None, fake, ws_bytes,
-                                                 None)
+                                                 fwd_bytes, fake, dx, fake, fake, fake, None, None, 1, fake,
+                                                 ws_bytes, None)
     assert lib.moe_layer_bwd(*args(F - 1, B)) == 3      # forward workspace too small
     assert lib.moe_layer_bwd(*args(F, B - 1)) == 3      # backward workspace too small
     assert lib.moe_layer_bwd(*args(F, B, dx=None)) == 1  # missing output
     sh = _cfg(d_ff_shared=64)
     assert lib.moe_layer_bwd(ctypes.byref(sh), fake, fake, fake, fake, None, None, fake, 1 << 30, fake, fake, fake,
-                             fake, fake, None, None, fake, 1 << 30, None) == 1  # shared expert without its weights
+                             fake, fake, None, None, 1, fake, 1 << 30, None) == 1  # shared expert without its weights

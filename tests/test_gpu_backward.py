@@ -40,15 +40,18 @@ SMALL = {
 }
 
 
-def _run(w: W.Workload, seed: int = 0):
+def _run(w: W.Workload, seed: int = 0, recompute: bool = True):
+    """Forward, then backward.  recompute=False: the training forward keeps the
+    expert pre-activations and the backward reads them instead of re-running
+    the expert GEMM1."""
     inp = inputs(w, seed)
     cfg = moe.make_config(w)
     dev = moe.upload(inp)
     layer = moe.MoELayer(cfg, dev)
-    layer.forward()
+    layer.forward(train=not recompute)
     dy_np = W.make_dy(w, seed)
     dy = moe.to_device(dy_np)
-    layer.backward(dy)
+    layer.backward(dy, recompute=recompute)
     torch.cuda.synchronize()
     return layer, inp, dy_np
 
@@ -103,11 +106,21 @@ def _slot_w_ref(w, layer, g):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("recompute", [True, False], ids=["recompute", "saved_z"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_backward_parity_small(name):
+def test_backward_parity_small(name, recompute):
     w = SMALL[name]
-    say(f"[bwd small] {name}: T={w.T} d={w.d} E={w.E} k={w.k} d_ff={w.d_ff} shared={w.d_ff_shared}")
-    layer, inp, dy = _run(w)
+    say(f"[bwd small] {name}: T={w.T} d={w.d} E={w.E} k={w.k} d_ff={w.d_ff} shared={w.d_ff_shared} "
+        f"recompute={recompute}")
+    layer, inp, dy = _run(w, recompute=recompute)
+    if not recompute:
+        # the training forward's output is the layer's output too
+        ref = oracle.layer(inp["x"], inp["wr"], inp["w1"], inp["w2"], k=w.k, routing=w.routing, act=w.act, cf=w.cf,
+                           ec_capacity=w.ec_capacity, bias=inp["bias"], bias_stride=inp["bias_stride"],
+                           ws1=inp["ws1"], ws2=inp["ws2"], given_logits=layer.view("logits").cpu().numpy(),
+                           given_scores=(layer.view("scores").cpu().numpy() if w.routing == W.EXPERT_CHOICE
+                                         else None))
+        _check("y (training forward)", host_float(layer.y), ref.y, TOL_Y[w.dtype])
     _check_layout(w, layer, inp)
     fwd = _oracle_fwd(w, layer, inp)
     g = oracle.layer_bwd(inp["x"], inp["wr"], inp["w1"], inp["w2"], dy, fwd, k=w.k, routing=w.routing, act=w.act,
@@ -144,10 +157,12 @@ def _expert_rows(w, layer, fwd, e):
 def test_backward_parity_full_size(name):
     """Full workloads: dx, dlogits and dL/dw on sampled tokens; sampled
     elements of each weight gradient; the router's gradients (dx term and
-    dW_r) from the GPU's dlogits, whose sampled rows are checked first."""
+    dW_r) from the GPU's dlogits, whose sampled rows are checked first.
+    (The bf16 workloads run the training forward and the backward that
+    reads its saved pre-activations, the way the benchmark times it.)"""
     w = WL[name]
     say(f"[bwd full] {name}")
-    layer, inp, dy = _run(w)
+    layer, inp, dy = _run(w, recompute=w.dtype != W.BF16)
     tol = TOL_Y[w.dtype]
     _check_layout(w, layer, inp)
     lg = layer.view("logits").cpu().numpy()
