@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=20,
                     help="moe_layer_bwd calls timed after the forward regions (0: skip the backward)")
+    ap.add_argument("--cold-iters", type=int, default=50,
+                    help="per-stage cold timings: calls of each stage, each after a 512-MiB write that evicts "
+                         "L2 and MALL; the median is reported (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -150,40 +153,40 @@ def main():
     stream = torch.cuda.current_stream()
     names = ["route", "permute", "expert_ffn"] + (["shared_ffn"] if w.d_ff_shared else []) + ["unpermute"]
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def stage_fns():
+        """One callable per stage, in order (each rewrites only its own outputs,
+        so any stage can be re-run on its own once a whole step has run)."""
+        fns = []
         if ec:
-            moe.route(cfg, dev.x, dev.wr, logits, bias=dev.bias, bias_stride=dev.bias_stride, scores=scores,
-                      ec_token=ec_token, ec_w=ec_w)
+            fns.append(lambda: moe.route(cfg, dev.x, dev.wr, logits, bias=dev.bias, bias_stride=dev.bias_stride,
+                                         scores=scores, ec_token=ec_token, ec_w=ec_w))
+            fns.append(lambda: moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off,
+                                           ec_token=ec_token, ec_w=ec_w, slot_w=slot_w, tok_ptr=tok_ptr))
         else:
-            moe.route(cfg, dev.x, dev.wr, logits, topk_idx, topk_w, bias=dev.bias, bias_stride=dev.bias_stride)
-        if ev is not None:
-            ev[1].record(stream)
-        if ec:
-            moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off, ec_token=ec_token, ec_w=ec_w,
-                        slot_w=slot_w, tok_ptr=tok_ptr)
-        else:
-            moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off, topk_idx=topk_idx, scratch=scratch)
-        if ev is not None:
-            ev[2].record(stream)
-        moe.expert_ffn(cfg, x_perm, off, dev.w1, dev.w2, h, y_perm, ffn_ws)
-        i = 3
-        if ev is not None:
-            ev[i].record(stream)
-        y_sh = None
+            fns.append(lambda: moe.route(cfg, dev.x, dev.wr, logits, topk_idx, topk_w, bias=dev.bias,
+                                         bias_stride=dev.bias_stride))
+            fns.append(lambda: moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off,
+                                           topk_idx=topk_idx, scratch=scratch))
+        fns.append(lambda: moe.expert_ffn(cfg, x_perm, off, dev.w1, dev.w2, h, y_perm, ffn_ws))
         if w.d_ff_shared:
-            moe.expert_ffn(scfg, dev.x, soff, dev.ws1, dev.ws2, hs, ys, sffn_ws)
-            y_sh = ys
-            i += 1
+            fns.append(lambda: moe.expert_ffn(scfg, dev.x, soff, dev.ws1, dev.ws2, hs, ys, sffn_ws))
+        if ec:
+            fns.append(lambda: moe.unpermute(cfg, y_perm, slot_row, slot_w, layer.y, tok_ptr=tok_ptr,
+                                             y_shared=ys if w.d_ff_shared else None))
+        else:
+            fns.append(lambda: moe.unpermute(cfg, y_perm, slot_row, topk_w, layer.y,
+                                             y_shared=ys if w.d_ff_shared else None))
+        return fns
+
+    fns = stage_fns()
+
+    def step(ev=None):
+        for i, fn in enumerate(fns):
             if ev is not None:
                 ev[i].record(stream)
-        if ec:
-            moe.unpermute(cfg, y_perm, slot_row, slot_w, layer.y, tok_ptr=tok_ptr, y_shared=y_sh)
-        else:
-            moe.unpermute(cfg, y_perm, slot_row, topk_w, layer.y, y_shared=y_sh)
+            fn()
         if ev is not None:
-            ev[i + 1].record(stream)
+            ev[len(fns)].record(stream)
 
     # The headline: K calls of moe_layer_fwd (the whole layer, shared expert
     # overlapped on its side stream), between two synchronisations.
@@ -209,10 +212,34 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, n in enumerate(names)}
+    stage_med = {n: float(np.median([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                 for j, n in enumerate(names)}
     ev_total_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][-1]) for i in range(args.steps)]))
     # the step-by-step path and moe_layer_fwd give the same bits
     same = bool(torch.equal(y_layer.view(torch.int16) if y_layer.dtype == torch.bfloat16 else y_layer,
                             layer.y.view(torch.int16) if layer.y.dtype == torch.bfloat16 else layer.y))
+
+    # Cold stage timings: each stage alone, after a 512-MiB write on the same
+    # stream that leaves neither L2 nor the 256-MB MALL holding its inputs;
+    # median over the calls.
+    cold_ms = None
+    if args.cold_iters > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold_ms = {}
+        for n, fn in zip(names, fns):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.cold_iters)]
+            for a, b in ev:
+                flush.fill_(1)
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            cold_ms[n] = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        del flush
+        cold_same = bool(torch.equal(y_layer.view(torch.int16) if y_layer.dtype == torch.bfloat16 else y_layer,
+                                     layer.y.view(torch.int16) if layer.y.dtype == torch.bfloat16 else layer.y))
+        same = same and cold_same
 
     # Backward: moe_layer_bwd (recomputed expert pre-activations, data and
     # weight gradients, router and shared expert) for a seeded dy, after one
@@ -260,17 +287,24 @@ def main():
     for n in names:
         kind = work[n][0]
         sec = stage_ms[n] / 1e3
-        ent = {"ms": round(stage_ms[n], 4)}
+        ent = {"ms": round(stage_ms[n], 4), "median_ms": round(stage_med[n], 4)}
         if kind == "bytes":
             ent["GB/s"] = round(work[n][1] / sec / 1e9, 1)
             ent["hbm_frac"] = round(work[n][1] / sec / 1e9 / PEAK_HBM_GBS, 4)
             ent["bytes"] = int(work[n][1])
+            if cold_ms is not None:
+                ent["cold_median_ms"] = round(cold_ms[n], 4)
+                ent["cold_GB/s"] = round(work[n][1] / (cold_ms[n] / 1e3) / 1e9, 1)
+                ent["cold_hbm_frac"] = round(work[n][1] / (cold_ms[n] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
         else:
             tf = work[n][1] / sec / 1e12
             peak = PEAK_BF16_TFLOPS if w.dtype == W.BF16 else PEAK_F32_TFLOPS
             ent["TFLOP/s"] = round(tf, 1)
             ent["mfma_frac" if w.dtype == W.BF16 else "fp32_frac"] = round(tf / peak, 4)
             ent["flops"] = int(work[n][1])
+            if cold_ms is not None:
+                ent["cold_median_ms"] = round(cold_ms[n], 4)
+                ent["cold_TFLOP/s"] = round(work[n][1] / (cold_ms[n] / 1e3) / 1e12, 1)
             if len(work[n]) > 2:
                 ent["min_bytes"] = int(work[n][2])
                 ent["GB/s"] = round(work[n][2] / sec / 1e9, 1)

@@ -47,6 +47,41 @@ namespace {
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16 (round to nearest even; gfx950's
+// v_cvt_pk_bf16_f32), lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Accumulator values of a 32x32 MFMA tile reach memory as rows.  Value
+// 4g+t of lane l sits at row 8g + 4(l/32) + t, column l%32, so for each g a
+// lane holds a 4-row slice of one column.  quad_rows() transposes these 4x4
+// blocks inside each lane quad: lane s of a quad returns row 4(..)+s of its
+// group at the quad's four columns, as 4 packed bf16 (8 bytes, memory order).
+// Two exchanges with neighbour lanes (DPP quad permutations) and byte
+// permutes; every lane of the wave must execute it.
+__device__ __forceinline__ u32x2 quad_rows(float f0, float f1, float f2, float f3) {
+  const int l = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+  // pairs: lanes 2m, 2m+1 (columns c, c+1) swap so that the even lane keeps
+  // rows t = 0, 2 and the odd lane rows 1, 3, each at both columns
+  const uint32_t p0 = pack_bf16x2(f0, f1), p1 = pack_bf16x2(f2, f3);
+  const uint32_t q0 = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(p0), 0xB1, 0xF, 0xF, false));
+  const uint32_t q1 = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(p1), 0xB1, 0xF, 0xF, false));
+  const uint32_t sel = (l & 1) ? 0x03020706u : 0x05040100u;  // odd: (q.hi, p.hi); even: (p.lo, q.lo)
+  const uint32_t r0 = __builtin_amdgcn_perm(q0, p0, sel);
+  const uint32_t r1 = __builtin_amdgcn_perm(q1, p1, sel);
+  // lanes s, s^2 (column pairs 0-1 and 2-3) swap one row each
+  const bool upper = (l & 2) != 0;
+  const uint32_t send = upper ? r0 : r1;
+  const uint32_t recv = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(send), 0x4E, 0xF, 0xF, false));
+  return upper ? u32x2{recv, r1} : u32x2{r0, recv};
+}
+
 // Block -> tile for the grouped GEMMs is done by every wave on its own (no
 // LDS): the grid is an upper bound on the tile count and the real count
 // follows from the device-side expert offsets.
