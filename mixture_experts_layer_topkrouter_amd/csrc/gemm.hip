@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < NJ / 2; ++j) {
           const int col = nt * (BN / 2) + wn * 64 + j * 16 + (l & 15);
-          if (col < p.n_out) crow[col] = f32_to_bf16(silu(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
+          if (col < p.n_out) crow[col] = f32_to_bf16(silu_fast(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
         }
       } else {
 #pragma unroll
@@ -651,37 +651,54 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
     return;
   }
 
-  // Epilogue straight from the accumulators: activation, then quad_rows()
-  // turns each 4-row column slice of a lane into one 8-byte row piece, and a
-  // wave store writes 8 rows x 64 B (the two 64-B halves of each 128-B line
-  // come from neighbouring 32-column tiles, stored back to back).  No LDS and no
-  // barrier: the tile's stores overlap the next workgroup's prologue on the CU.
+  // Epilogue: activation, then quad_rows() turns each 4-row column slice of a
+  // lane into one 8-byte row piece, written to LDS (the ring is free by now);
+  // then the block stores whole rows with 16-byte coalesced writes.  Row pitch
+  // = row bytes + 64: the 8 rows one ds_write_b64 covers (8 x 64 B) fall on
+  // the 4 distinct 64-B bank quarters twice, the minimum for 512 B.
   constexpr int OUT_COLS = (ACT == ACT_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
   constexpr int NJO = (ACT == ACT_SWIGLU) ? NJ / 2 : NJ;      // output tiles per wave row
-  uint8_t *C = static_cast<uint8_t *>(p.C) + (LAY == LAY_TN ? static_cast<int64_t>(e) * p.c_stride * 2 : 0);
-  const int lr0 = wm * RW + 4 * (l >> 5) + (l & 3);  // + 32 i + 8 g
-  const int lc0 = nt * OUT_COLS + wn * (OUT_COLS / 2) + 4 * ((l & 31) >> 2);  // + 32 j
+  constexpr int PITCH = OUT_COLS * 2 + 64;                     // bytes per LDS row
+  static_assert(DBM * PITCH <= NST * 2 * DSTAGE * 2, "epilogue tile must fit in the ring");
+  // The five slot arrays fill the 160 KB exactly, so they are contiguous; the
+  // epilogue tile starts at whichever of them has the lowest LDS address.
+  uint16_t *lo = s0;
+  if (lds_addr_of(s1) < lds_addr_of(lo)) lo = s1;
+  if (lds_addr_of(s2) < lds_addr_of(lo)) lo = s2;
+  if (lds_addr_of(s3) < lds_addr_of(lo)) lo = s3;
+  if (lds_addr_of(s4) < lds_addr_of(lo)) lo = s4;
+  uint8_t *ep = reinterpret_cast<uint8_t *>(lo);
+  const int lr0 = wm * RW + 4 * (l >> 5) + (l & 3);                // + 32 i + 8 g
+  const int lc0 = wn * (OUT_COLS / 2) + 4 * ((l & 31) >> 2);       // + 32 j
+  __syncthreads();  // every wave is done with the ring
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
       for (int j = 0; j < NJO; ++j) {
-        const int col = lc0 + 32 * j;
         float f[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float x = acc[i][j][4 * g + t];
-          if (ACT == ACT_SWIGLU) f[t] = silu(x) * acc[i][j + NJ / 2][4 * g + t];
+          if (ACT == ACT_SWIGLU) f[t] = silu_fast(x) * acc[i][j + NJ / 2][4 * g + t];
           else if (ACT == ACT_GELU) f[t] = gelu_erf(x);
           else f[t] = x;
         }
         const u32x2 v = quad_rows(f[0], f[1], f[2], f[3]);
-        const int r = lr0 + 32 * i + 8 * g;
-        if (r < rows && col < p.n_out)
-          *reinterpret_cast<u32x2 *>(C + (static_cast<int64_t>(row0 + r) * p.ldc + col) * 2) = v;
+        *reinterpret_cast<u32x2 *>(ep + (lr0 + 32 * i + 8 * g) * PITCH + (lc0 + 32 * j) * 2) = v;
       }
     }
+  }
+  __syncthreads();
+  constexpr int CHUNKS = OUT_COLS / 8;  // 16-byte chunks per row
+  const int col0 = nt * OUT_COLS;
+  uint8_t *C = static_cast<uint8_t *>(p.C) + (LAY == LAY_TN ? static_cast<int64_t>(e) * p.c_stride * 2 : 0);
+  for (int q = threadIdx.x; q < DBM * CHUNKS; q += NTH) {
+    const int r = q / CHUNKS, c = q - (q / CHUNKS) * CHUNKS;
+    if (r >= rows || col0 + c * 8 >= p.n_out) continue;
+    const u32x4 val = *reinterpret_cast<const u32x4 *>(ep + r * PITCH + c * 16);
+    st16(C + (static_cast<int64_t>(row0 + r) * p.ldc + col0 + c * 8) * 2, val);
   }
 }
 
@@ -725,7 +742,7 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (r0 + r >= rows) continue;
-      const float v = ACT == ACT_SWIGLU ? silu(a[r]) * u[r] : (ACT == ACT_GELU ? gelu_erf(a[r]) : a[r]);
+      const float v = ACT == ACT_SWIGLU ? silu_fast(a[r]) * u[r] : (ACT == ACT_GELU ? gelu_erf(a[r]) : a[r]);
       C[static_cast<int64_t>(row0 + r0 + r) * p.ldc + col] = f32_to_bf16(v);
     }
   }

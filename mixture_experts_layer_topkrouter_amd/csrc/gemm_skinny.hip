@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
       uint16_t *crow = Cp + static_cast<int64_t>(job.row0 + r) * p.ldc;
       if (ACT == ACT_SWIGLU) {
         const int col = nt * (SBN / 2) + w * 32 + (l & 31);
-        if (col < p.n_out) crow[col] = f32_to_bf16(silu(acc[i][0][v]) * acc[i][1][v]);
+        if (col < p.n_out) crow[col] = f32_to_bf16(silu_fast(acc[i][0][v]) * acc[i][1][v]);
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void skinny_reduce_kernel(GemmParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (r0 + r >= rows) continue;
-      const float v = ACT == ACT_SWIGLU ? silu(a[r]) * u[r] : (ACT == ACT_GELU ? gelu_erf(a[r]) : a[r]);
+      const float v = ACT == ACT_SWIGLU ? silu_fast(a[r]) * u[r] : (ACT == ACT_GELU ? gelu_erf(a[r]) : a[r]);
       Cp[static_cast<int64_t>(row0 + r0 + r) * p.ldc + col] = f32_to_bf16(v);
     }
   }
