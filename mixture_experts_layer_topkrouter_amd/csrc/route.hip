@@ -16,9 +16,13 @@
 //   The router weight is tiny and stays in L2; x is streamed once from HBM.
 // * the gate runs on the logits tile while it is still in LDS: one wave per
 //   token, lane l holds experts l, l+64, l+128, l+192; each of the k picks is a
-//   64-lane butterfly arg-max under the order (value desc, index asc) with IEEE
-//   comparisons (so -0 == +0), which is a strict total order, so every lane
-//   agrees on the winner.
+//   wave arg-max under the order (value desc, index asc) with IEEE comparisons
+//   (so -0 == +0), a strict total order.  The wave reductions (arg-max, max,
+//   sum) run on DPP lane shifts inside rows of 16 lanes plus two row
+//   broadcasts, a few cycles per step instead of an LDS-crossbar round trip
+//   per butterfly level; lane 63 ends with the result, which readlane makes
+//   wave-uniform.  The order of the steps is fixed, so sums are
+//   deterministic.
 // * ExpertChoice: one workgroup per expert keeps its score column in LDS,
 //   finds the C-th largest score by an 8-bit radix select (scores are >= 0,
 //   so their bit patterns order like the values), then compacts the chosen
@@ -30,6 +34,81 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
+
+// DPP controls (gfx9): row_shr:n = 0x110 + n; row_bcast:15 / :31.
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// The value of lane `src` of the wave at the lane this step reads (DPP; a
+// lane whose source is out of range, or outside row_mask, keeps its own).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false);
+}
+
+// (vb, ib) ranks before (va, ia): larger value, equal values by lower index.
+__device__ __forceinline__ bool ranks_before(float vb, int ib, float va, int ia) {
+  return vb > va || (vb == va && ib < ia);
+}
+
+// Wave arg-max of (v, i) under ranks_before; returns it wave-uniform.  Row
+// shifts 1, 2, 4, 8 leave each row's best in its lane 15, the two row
+// broadcasts carry rows 0 and 2 into rows 1 and 3, then row 1 into 2 and 3.
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+#define MOE_ARGMAX_STEP(C, R)                   \
+  {                                             \
+    const float ov = dpp_f<C, R>(v);            \
+    const int oi = dpp_i<C, R>(i);              \
+    if (ranks_before(ov, oi, v, i)) {           \
+      v = ov;                                   \
+      i = oi;                                   \
+    }                                           \
+  }
+  MOE_ARGMAX_STEP(kRowShr1, 0xf)
+  MOE_ARGMAX_STEP(kRowShr2, 0xf)
+  MOE_ARGMAX_STEP(kRowShr4, 0xf)
+  MOE_ARGMAX_STEP(kRowShr8, 0xf)
+  MOE_ARGMAX_STEP(kRowBcast15, 0xa)
+  MOE_ARGMAX_STEP(kRowBcast31, 0xc)
+#undef MOE_ARGMAX_STEP
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<kRowShr1, 0xf>(v));
+  v = fmaxf(v, dpp_f<kRowShr2, 0xf>(v));
+  v = fmaxf(v, dpp_f<kRowShr4, 0xf>(v));
+  v = fmaxf(v, dpp_f<kRowShr8, 0xf>(v));
+  v = fmaxf(v, dpp_f<kRowBcast15, 0xa>(v));
+  v = fmaxf(v, dpp_f<kRowBcast31, 0xc>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Wave sum in a fixed order.  A shifted-in value is added only where the
+// source lane exists (the DPP keeps the lane's own value elsewhere, which
+// must not be added twice).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  const int l = lane_id() & 15, row = lane_id() >> 4;
+  float o;
+  o = dpp_f<kRowShr1, 0xf>(v);
+  if (l >= 1) v += o;
+  o = dpp_f<kRowShr2, 0xf>(v);
+  if (l >= 2) v += o;
+  o = dpp_f<kRowShr4, 0xf>(v);
+  if (l >= 4) v += o;
+  o = dpp_f<kRowShr8, 0xf>(v);
+  if (l >= 8) v += o;
+  o = dpp_f<kRowBcast15, 0xa>(v);
+  if (row & 1) v += o;
+  o = dpp_f<kRowBcast31, 0xc>(v);
+  if (row >= 2) v += o;
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 
 // Gate for `rows` tokens whose logits sit in LDS (row stride ld).
 __device__ void gate_rows(const float *tile, int ld, int rows, int t0, int T, int E, int k,
@@ -55,69 +134,54 @@ __device__ void gate_rows(const float *tile, int ld, int rows, int t0, int T, in
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (valid[q]) m = fmaxf(m, v[q]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+      m = wave_max_dpp(m);
       float s = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (valid[q]) s += expf(v[q] - m);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
-      s = __shfl(s, 0, kWave);
+      s = wave_sum_dpp(s);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (valid[q]) scores[(int64_t)t * E + l + kWave * q] = expf(v[q] - m) / s;
       continue;
     }
     int my_idx = -1;
-    float my_val = 0.f;
+    float my_val = 0.f, top = 0.f;
     for (int j = 0; j < k; ++j) {
-      bool have = false;
-      float bv = 0.f;
+      // this lane's best untaken candidate; lanes without one offer
+      // (-inf, INT_MAX), which every real candidate ranks before
+      float bv = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // q ascending is index ascending: a strict '>' keeps the lower index on ties
-        if (!taken[q] && (!have || v[q] > bv)) {
-          have = true;
+        if (!taken[q] && (bi == 0x7fffffff || v[q] > bv)) {
           bv = v[q];
           bi = l + kWave * q;
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        const int oh = __shfl_xor(have ? 1 : 0, o, kWave);
-        if (oh && (!have || ov > bv || (ov == bv && oi < bi))) {
-          have = true;
-          bv = ov;
-          bi = oi;
-        }
-      }
+      wave_argmax(bv, bi);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (bi == l + kWave * q) taken[q] = true;
+      if (j == 0) top = bv;
       if (l == j) {
         my_idx = bi;
         my_val = bv;
       }
     }
-    const float top = __shfl(my_val, 0, kWave);
     float w;
     if (routing == 0) {  // softmax over all E, read at the chosen experts
       float s = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (valid[q]) s += expf(v[q] - top);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
-      s = __shfl(s, 0, kWave);
+      s = wave_sum_dpp(s);
       w = expf(my_val - top) / s;
-    } else {  // softmax over the k chosen logits
+    } else {  // softmax over the k chosen logits, added in slot order
       const float ex = (l < k) ? expf(my_val - top) : 0.f;
       float s = 0.f;
-      for (int jj = 0; jj < k; ++jj) s += __shfl(ex, jj, kWave);
+      for (int jj = 0; jj < k; ++jj) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), jj));
       w = ex / s;
     }
     if (l < k) {
@@ -162,9 +226,10 @@ __global__ __launch_bounds__(kRouteBf16Threads) void route_bf16_kernel(
   constexpr int RED = (NW / 2) * MT * NT * kWave;  // float4s of the reduction buffer
   static_assert(BT * LD <= RED * 4 || RED == 0, "logits tile fits in the reduction buffer");
   // steps in flight per wave: as many as fit next to the accumulators in
-  // about 192 registers (4 per fragment), at most 8
+  // about 192 registers (4 per fragment), at most 16 (with 16 tokens, 16
+  // experts and d = 4096, every load of a wave is in flight at once)
   constexpr int D_FIT = (192 - 4 * MT * NT) / (4 * (MT + NT));
-  constexpr int D = D_FIT < 1 ? 1 : (D_FIT > 8 ? 8 : D_FIT);
+  constexpr int D = D_FIT < 1 ? 1 : (D_FIT > 16 ? 16 : D_FIT);
   __shared__ f32x4 red[RED];  // partial tiles, then the logits tile
   float *tile = reinterpret_cast<float *>(red);
   const int l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
