@@ -40,15 +40,42 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (static_cast<uint64_t>(1) << lane_id()) - 1;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (integer, exact).
+// DPP lane moves (gfx9 encodings): row_shr:n (0x110 + n) shifts inside rows
+// of 16 lanes; row_bcast:15 carries lane 15 of rows 0 and 2 into rows 1 and
+// 3, row_bcast:31 carries lane 31 into rows 2 and 3.  A lane whose source
+// lane does not exist, or whose row is outside ROWS, keeps its own value.
+// A few cycles each, where a cross-lane shuffle is an LDS-crossbar round trip.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (integer, exact; every
+// lane of the wave must be active): prefix sums inside each row of 16 by
+// row shifts 1, 2, 4, 8, then the row totals carried up by the broadcasts.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int n = __shfl_up(v, o, kWave);
-    if (l >= o) v += n;
-  }
+  const int l = lane_id() & 15, row = lane_id() >> 4;
+  int o = dpp_move<kDppRowShr1>(v);
+  if (l >= 1) v += o;
+  o = dpp_move<kDppRowShr2>(v);
+  if (l >= 2) v += o;
+  o = dpp_move<kDppRowShr4>(v);
+  if (l >= 4) v += o;
+  o = dpp_move<kDppRowShr8>(v);
+  if (l >= 8) v += o;
+  o = dpp_move<kDppRowBcast15, 0xa>(v);
+  if (row & 1) v += o;
+  o = dpp_move<kDppRowBcast31, 0xc>(v);
+  if (row >= 2) v += o;
   return v;
+}
+
+// Sum over the 64 lanes (integer, exact), the same in every lane.
+__device__ __forceinline__ int wave_sum_int(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), kWave - 1);
 }
 
 // Exclusive prefix sum over a whole block (blockDim.x threads, multiple of 64,

@@ -110,10 +110,7 @@ __device__ __forceinline__ int count_mtiles(const int32_t *__restrict__ offs, in
   for (int e0 = 0; e0 < E; e0 += kWave) {
     int o0 = 0, me = 0;
     if (e0 + l < E) expert_rows(offs, e0 + l, max_rows, &o0, &me);
-    int t = (me + BM - 1) / BM;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
-    m_tiles += t;
+    m_tiles += wave_sum_int((me + BM - 1) / BM);
   }
   // the same in every lane; readfirstlane lets the compiler treat everything
   // derived from it (and the branches on it) as wave-uniform
@@ -148,15 +145,15 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offs, int 
     const int excl = incl - tiles;
     const uint64_t hit = __ballot(e < E && q >= excl * n_tiles && q < incl * n_tiles);
     if (hit) {
-      const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-      fe = __shfl(e, src, kWave);
-      fo0 = __shfl(o0, src, kWave);
-      fme = __shfl(me, src, kWave);
-      fexcl = __shfl(excl, src, kWave);
-      ftiles = __shfl(tiles, src, kWave);
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<unsigned long long>(hit)) - 1);
+      fe = __builtin_amdgcn_readlane(e, src);
+      fo0 = __builtin_amdgcn_readlane(o0, src);
+      fme = __builtin_amdgcn_readlane(me, src);
+      fexcl = __builtin_amdgcn_readlane(excl, src);
+      ftiles = __builtin_amdgcn_readlane(tiles, src);
       break;
     }
-    carry = __shfl(incl, kWave - 1, kWave);
+    carry = __builtin_amdgcn_readlane(incl, kWave - 1);
   }
   fe = __builtin_amdgcn_readfirstlane(fe);
   if (fe < 0) return false;

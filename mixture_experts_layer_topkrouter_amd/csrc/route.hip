@@ -35,19 +35,18 @@ namespace {
 
 constexpr int kRouteThreads = 256;
 
-// DPP controls (gfx9): row_shr:n = 0x110 + n; row_bcast:15 / :31.
-constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+// The DPP moves of common.h on floats and ints (a lane whose source lane is
+// out of range, or outside the row mask, keeps its own value).
+constexpr int kRowShr1 = kDppRowShr1, kRowShr2 = kDppRowShr2, kRowShr4 = kDppRowShr4, kRowShr8 = kDppRowShr8;
+constexpr int kRowBcast15 = kDppRowBcast15, kRowBcast31 = kDppRowBcast31;
 
-// The value of lane `src` of the wave at the lane this step reads (DPP; a
-// lane whose source is out of range, or outside row_mask, keeps its own).
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xf, false));
+  return __int_as_float(dpp_move<CTRL, ROWS>(__float_as_int(v)));
 }
 template <int CTRL, int ROWS>
 __device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false);
+  return dpp_move<CTRL, ROWS>(v);
 }
 
 // (vb, ib) ranks before (va, ia): larger value, equal values by lower index.
