@@ -35,6 +35,15 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Token rows are read once here: non-temporal loads keep them from
+// displacing other lines in L2 (measured: the median after an
+// L2/MALL-evicting write drops from 31 to 25 us on the Mixtral slice, the
+// warm time is unchanged; non-temporal stores of x_perm, which the expert
+// GEMM reads next, were slower).
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 constexpr int kGroups = kPermuteBlock / kWave;  // 16 groups of 64 per block
 
 __global__ __launch_bounds__(kThreads) void count_kernel(const int32_t *__restrict__ idx, int64_t A, int E,
@@ -125,7 +134,7 @@ __device__ __forceinline__ void copy_row(const uint8_t *__restrict__ x, size_t r
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
       const int c = c0 + u * kWave + l;
-      if (c < nchunk) v[u] = ld16(src + static_cast<size_t>(c) * 16);
+      if (c < nchunk) v[u] = ld16_stream(src + static_cast<size_t>(c) * 16);
     }
     for (int j = 0; j < k; ++j) {
       const int rj = __shfl(row, j, kWave);
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(kFusedThreads) void count_scatter_kernel(
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
       const int c = u * kWave + l;
-      v[u] = (has_t && c < nchunk) ? ld16(src + static_cast<size_t>(c) * 16) : u32x4{0u, 0u, 0u, 0u};
+      v[u] = (has_t && c < nchunk) ? ld16_stream(src + static_cast<size_t>(c) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
   }
   for (int e = tid; e < E; e += kFusedThreads) {
