@@ -37,6 +37,7 @@
 //   the hidden activation is written once, in bf16.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "gemm_common.h"
 
@@ -547,13 +548,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   // interleaved with the NR fragment reads of stage kt+1 (into the other
   // register set) and the ND DMA instructions that refill stage kt's slot
   // with stage kt+5; sched_barrier pins this order, so the LDS reads and the
-  // loads issue in the shadow of the matrix core.
-  auto iter = [&](auto S, auto SET, int kt) {
+  // loads issue in the shadow of the matrix core.  A steady iteration (at
+  // least 5 stages after it) has every read and refill and waits with three
+  // stages still in flight: all of that is known at compile time, so its
+  // loads and wait carry no branches (measured: a branch per load and a
+  // branch tree per wait cost a tenth of the K loop).
+  auto iter = [&](auto S, auto SET, int kt, auto STEADY) {
     constexpr int s = decltype(S)::value;
     constexpr int set = decltype(SET)::value;
-    const bool more = kt + 1 < nk;
-    const bool refill = kt + 5 < nk;
-    if (more) wait_stage(kt + 1, min(nk - 1, kt + 4));
+    constexpr bool steady = decltype(STEADY)::value;
+    const bool more = steady || kt + 1 < nk;
+    const bool refill = steady || kt + 5 < nk;
+    if constexpr (steady) {
+      wait_vm<3 * ND>();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      if (more) wait_stage(kt + 1, min(nk - 1, kt + 4));
+    }
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t *ls = slot(Slot<(s + 1) % NST>{});
     const uint32_t dbase = lds_addr_of(slot(S));
@@ -592,28 +603,44 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
     keep_live<set>(fa, fb);
     __builtin_amdgcn_sched_barrier(0);
   };
+  using Steady = std::integral_constant<bool, true>;
+  using Edge = std::integral_constant<bool, false>;
   int kt = 0;
-  for (; kt + 9 < nk; kt += 10) {
-    iter(Slot<0>{}, Slot<0>{}, kt);
-    iter(Slot<1>{}, Slot<1>{}, kt + 1);
-    iter(Slot<2>{}, Slot<0>{}, kt + 2);
-    iter(Slot<3>{}, Slot<1>{}, kt + 3);
-    iter(Slot<4>{}, Slot<0>{}, kt + 4);
-    iter(Slot<0>{}, Slot<1>{}, kt + 5);
-    iter(Slot<1>{}, Slot<0>{}, kt + 6);
-    iter(Slot<2>{}, Slot<1>{}, kt + 7);
-    iter(Slot<3>{}, Slot<0>{}, kt + 8);
-    iter(Slot<4>{}, Slot<1>{}, kt + 9);
+  // ten steady iterations while at least 15 stages remain (the last of them
+  // still refills stage kt + 14)
+  for (; kt + 14 < nk; kt += 10) {
+    iter(Slot<0>{}, Slot<0>{}, kt, Steady{});
+    iter(Slot<1>{}, Slot<1>{}, kt + 1, Steady{});
+    iter(Slot<2>{}, Slot<0>{}, kt + 2, Steady{});
+    iter(Slot<3>{}, Slot<1>{}, kt + 3, Steady{});
+    iter(Slot<4>{}, Slot<0>{}, kt + 4, Steady{});
+    iter(Slot<0>{}, Slot<1>{}, kt + 5, Steady{});
+    iter(Slot<1>{}, Slot<0>{}, kt + 6, Steady{});
+    iter(Slot<2>{}, Slot<1>{}, kt + 7, Steady{});
+    iter(Slot<3>{}, Slot<0>{}, kt + 8, Steady{});
+    iter(Slot<4>{}, Slot<1>{}, kt + 9, Steady{});
   }
-  if (kt < nk) iter(Slot<0>{}, Slot<0>{}, kt);
-  if (kt + 1 < nk) iter(Slot<1>{}, Slot<1>{}, kt + 1);
-  if (kt + 2 < nk) iter(Slot<2>{}, Slot<0>{}, kt + 2);
-  if (kt + 3 < nk) iter(Slot<3>{}, Slot<1>{}, kt + 3);
-  if (kt + 4 < nk) iter(Slot<4>{}, Slot<0>{}, kt + 4);
-  if (kt + 5 < nk) iter(Slot<0>{}, Slot<1>{}, kt + 5);
-  if (kt + 6 < nk) iter(Slot<1>{}, Slot<0>{}, kt + 6);
-  if (kt + 7 < nk) iter(Slot<2>{}, Slot<1>{}, kt + 7);
-  if (kt + 8 < nk) iter(Slot<3>{}, Slot<0>{}, kt + 8);
+  for (; kt + 9 < nk; kt += 10) {
+    iter(Slot<0>{}, Slot<0>{}, kt, Edge{});
+    iter(Slot<1>{}, Slot<1>{}, kt + 1, Edge{});
+    iter(Slot<2>{}, Slot<0>{}, kt + 2, Edge{});
+    iter(Slot<3>{}, Slot<1>{}, kt + 3, Edge{});
+    iter(Slot<4>{}, Slot<0>{}, kt + 4, Edge{});
+    iter(Slot<0>{}, Slot<1>{}, kt + 5, Edge{});
+    iter(Slot<1>{}, Slot<0>{}, kt + 6, Edge{});
+    iter(Slot<2>{}, Slot<1>{}, kt + 7, Edge{});
+    iter(Slot<3>{}, Slot<0>{}, kt + 8, Edge{});
+    iter(Slot<4>{}, Slot<1>{}, kt + 9, Edge{});
+  }
+  if (kt < nk) iter(Slot<0>{}, Slot<0>{}, kt, Edge{});
+  if (kt + 1 < nk) iter(Slot<1>{}, Slot<1>{}, kt + 1, Edge{});
+  if (kt + 2 < nk) iter(Slot<2>{}, Slot<0>{}, kt + 2, Edge{});
+  if (kt + 3 < nk) iter(Slot<3>{}, Slot<1>{}, kt + 3, Edge{});
+  if (kt + 4 < nk) iter(Slot<4>{}, Slot<0>{}, kt + 4, Edge{});
+  if (kt + 5 < nk) iter(Slot<0>{}, Slot<1>{}, kt + 5, Edge{});
+  if (kt + 6 < nk) iter(Slot<1>{}, Slot<0>{}, kt + 6, Edge{});
+  if (kt + 7 < nk) iter(Slot<2>{}, Slot<1>{}, kt + 7, Edge{});
+  if (kt + 8 < nk) iter(Slot<3>{}, Slot<0>{}, kt + 8, Edge{});
 
   if (job.nseg > 1) {
     // K-split piece: store the fp32 partial in accumulator order (lane l of
