@@ -551,8 +551,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   // loads issue in the shadow of the matrix core.  A steady iteration (at
   // least 5 stages after it) has every read and refill and waits with three
   // stages still in flight: all of that is known at compile time, so its
-  // loads and wait carry no branches (measured: a branch per load and a
-  // branch tree per wait cost a tenth of the K loop).
+  // loads and wait carry no branches (a branch per load and a branch tree
+  // per wait gave 185 instructions and 14 branches per stage; without them
+  // 95 and none, and the Mixtral-slice FFN went from 2.79 to 2.75 ms).
   auto iter = [&](auto S, auto SET, int kt, auto STEADY) {
     constexpr int s = decltype(S)::value;
     constexpr int set = decltype(SET)::value;
