@@ -305,7 +305,15 @@ __device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.f + erff
 __device__ __forceinline__ float gelu_grad_f(float z) {
   return 0.5f * (1.f + erff(z * 0.70710678118654752f)) + z * 0.39894228040143268f * expf(-0.5f * z * z);
 }
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + expf(-z)); }
+// bf16 data: the sigmoid from the hardware base-2 exponential and reciprocal
+// (about 1 ulp each, far below bf16 rounding; measured on the Mixtral slice:
+// act_fwd 131 -> 122 us, act_bwd unchanged at ~255 us, which is HBM-bound).
+// fp32 data keeps expf and an IEEE divide.
+template <bool FAST>
+__device__ __forceinline__ float sigmoid_t(float z) {
+  if constexpr (FAST) return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
+  else return 1.f / (1.f + expf(-z));
+}
 
 // Activation backward on rows [0, rows_of) of the padded layout:
 //   GELU:   z -> dz = dh * gelu'(z),         dh -> h = gelu(z)
@@ -349,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(void *__restrict__ z,
                    fb);
 #pragma unroll
       for (int q = 0; q < kElems; ++q) {
-        const float sg = sigmoid_f(fa[q]);
+        const float sg = sigmoid_t<BF16>(fa[q]);
         const float si = fa[q] * sg;
         da[q] = fg[q] * fb[q] * (sg + fa[q] * sg * (1.f - sg));
         db[q] = fg[q] * si;
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void act_fwd_kernel(const void *__restric
       float fb[kElems];
       unpack<BF16>(ld16(zr + static_cast<size_t>(dff) * es + static_cast<size_t>(c) * 16), fb);
 #pragma unroll
-      for (int q = 0; q < kElems; ++q) out[q] = fa[q] * sigmoid_f(fa[q]) * fb[q];
+      for (int q = 0; q < kElems; ++q) out[q] = fa[q] * sigmoid_t<BF16>(fa[q]) * fb[q];
     } else {
 #pragma unroll
       for (int q = 0; q < kElems; ++q) out[q] = gelu_f(fa[q]);
