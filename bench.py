@@ -356,7 +356,14 @@ def main():
                            ec_capacity=w.ec_capacity, bias=inp["bias"], bias_stride=inp["bias_stride"],
                            ws1=inp["ws1"], ws2=inp["ws2"], toks=toks)
         tc = time.perf_counter() - tc
+        cpu_model = None
+        try:
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+        except OSError:
+            pass
         cpu = {"value": round(len(toks) / tc, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model,
                "sample": f"fp64 oracle: router logits, gate and dispatch of all {T} tokens plus the expert FFN "
                          f"and combine of {len(toks)} sampled tokens; value = sampled tokens / wall time "
                          f"({tc:.1f} s)"}
