@@ -4,7 +4,9 @@
 One step = the whole forward pass of one MoE block (route, permute, grouped
 expert FFN, shared expert when present, unpermute) over one batch of seeded
 synthetic tokens already resident in HBM: one moe_layer_fwd call (the
-shared expert runs beside the rest on its side stream).  A second timed
+shared expert runs beside the rest on its side stream).  ``value`` is the
+wall-clock rate over the back-to-back calls; the same calls timed one by one
+with HIP events give ``layer_fwd_median_ms``.  A second timed
 region calls the individual entry points back to back on one stream (the
 same kernels) with a HIP event between the stages, which gives each stage's
 average duration; its output is checked to match moe_layer_fwd bit for bit.
@@ -200,6 +202,15 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     y_layer = layer.y.clone()
+    # the same calls one at a time between HIP events on the stream: the
+    # median layer time (tokens/s at the median is reported beside `value`)
+    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in lev:
+        a.record(stream)
+        layer.forward()
+        b.record(stream)
+    torch.cuda.synchronize()
+    layer_med_ms = float(np.median([a.elapsed_time(b) for a, b in lev]))
 
     # Stage breakdown: the same kernels through the individual entry points,
     # one stream, HIP events between the stages (a second timed region).
@@ -391,6 +402,8 @@ def main():
         "stages": stages,
         "backward": bwd,
         "event_ms_per_step": round(ev_total_ms, 4),
+        "layer_fwd_median_ms": round(layer_med_ms, 4),
+        "tokens_per_s_at_median": round(T / (layer_med_ms / 1e3), 1),
         "layer_fwd_matches_steps": same,
         "parity_max_rel_err_sampled": parity,
         "device": dev_name,
