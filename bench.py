@@ -6,7 +6,8 @@ expert FFN, shared expert when present, unpermute) over one batch of seeded
 synthetic tokens already resident in HBM: one moe_layer_fwd call (the
 shared expert runs beside the rest on its side stream).  ``value`` is the
 wall-clock rate over the back-to-back calls; the same calls timed one by one
-with HIP events give ``layer_fwd_median_ms``.  A second timed
+with HIP events give ``layer_fwd_median_ms``, and the layer captured once
+into a HIP graph and replayed gives ``graph_replay``.  A second timed
 region calls the individual entry points back to back on one stream (the
 same kernels) with a HIP event between the stages, which gives each stage's
 average duration; its output is checked to match moe_layer_fwd bit for bit.
@@ -57,6 +58,8 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=50,
                     help="per-stage cold timings: calls of each stage, each after a 512-MiB write that evicts "
                          "L2 and MALL; the median is reported (0: skip)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the HIP-graph replay timing of the layer")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -211,6 +214,33 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     layer_med_ms = float(np.median([a.elapsed_time(b) for a, b in lev]))
+    # the same layer captured once into a HIP graph and replayed K times (the
+    # launches of one step become one graph launch; the outputs must match)
+    graph = None
+    if args.graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            layer.forward()
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            layer.forward()
+        torch.cuda.synchronize()
+        for _ in range(min(args.warmup, 3)):
+            g.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter() - tg
+        gsame = bool(torch.equal(y_layer.view(torch.int16) if y_layer.dtype == torch.bfloat16 else y_layer,
+                                 layer.y.view(torch.int16) if layer.y.dtype == torch.bfloat16 else layer.y))
+        graph = {"ms_per_step": round(tg * 1e3 / args.steps, 4), "tokens_per_s": round(T * args.steps / tg, 1),
+                 "matches_eager": gsame}
+        del g
 
     # Stage breakdown: the same kernels through the individual entry points,
     # one stream, HIP events between the stages (a second timed region).
@@ -403,6 +433,7 @@ def main():
         "backward": bwd,
         "event_ms_per_step": round(ev_total_ms, 4),
         "layer_fwd_median_ms": round(layer_med_ms, 4),
+        "graph_replay": graph,
         "tokens_per_s_at_median": round(T / (layer_med_ms / 1e3), 1),
         "layer_fwd_matches_steps": same,
         "parity_max_rel_err_sampled": parity,
