@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=50,
                     help="per-stage cold timings: calls of each stage, each after a 512-MiB write that evicts "
                          "L2 and MALL; the median is reported (0: skip)")
+    ap.add_argument("--no-hbm-probe", dest="hbm_probe", action="store_false",
+                    help="skip the copy / fill / read rate measurement of the device's HBM")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the HIP-graph replay timing of the layer")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -312,6 +314,32 @@ def main():
                "train_fwd_ms": round(ms_train_fwd, 4),
                "train_step_tokens_per_s": round(T / ((ms_train_fwd + ms_saved) / 1e3), 1)}
 
+    # Practical HBM stream rates of this device, for reading the HBM-bound
+    # stages against: a device-to-device copy (read + write) and a fill
+    # (write), each over 1 GiB, median of 5 event-timed runs.
+    hbm_probe = None
+    if args.hbm_probe:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+
+        def rate(fn, moved):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            return round(moved / (float(np.median(ts)) / 1e3) / 1e9, 1)
+
+        hbm_probe = {"copy_GB/s": rate(lambda: dst.copy_(src), 2 * nbytes),
+                     "fill_GB/s": rate(lambda: dst.fill_(1.0), nbytes), "bytes": nbytes}
+        del src, dst
+
     if args.copy_probe_mib:
         a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
@@ -434,6 +462,7 @@ def main():
         "event_ms_per_step": round(ev_total_ms, 4),
         "layer_fwd_median_ms": round(layer_med_ms, 4),
         "graph_replay": graph,
+        "hbm_probe": hbm_probe,
         "tokens_per_s_at_median": round(T / (layer_med_ms / 1e3), 1),
         "layer_fwd_matches_steps": same,
         "parity_max_rel_err_sampled": parity,
