@@ -27,7 +27,7 @@
  *        - top_k paragraph: an always-used shared expert next to the routed
  *          top-k experts.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - selection key is the logit value; ties go to the lower expert index;
  *     comparisons are IEEE (so -0 == +0);
  *   - SOFTMAX_ALL: weight = softmax over all E experts at the chosen index,
