@@ -72,8 +72,13 @@ typedef struct {
   int32_t top_k;           /* k: experts per token, 1..min(E,16) (top-k modes)   */
   int32_t d_ff;            /* expert hidden width, multiple of 8                 */
   int32_t d_ff_shared;     /* shared expert hidden width, 0 = no shared expert   */
-  float capacity_factor;   /* [P3] capacity_factor; 0 = dropless ([P1]
-                              "Activation Checkpointing and Constraints")       */
+  double capacity_factor;  /* [P3] capacity_factor; 0 = dropless ([P1]
+                              "Activation Checkpointing and Constraints").
+                              A double, so that the capacity below is the
+                              same ceil(cf*T*k/E) a caller computes from
+                              the factor it wrote (a float32 factor such as
+                              1.2 is stored slightly high and can round the
+                              capacity up by one)                             */
   int32_t ec_capacity;     /* ExpertChoice: tokens per expert, 1..T             */
   int32_t dtype;           /* moe_dtype of x, weights and activations            */
   int32_t act;             /* moe_act of the routed and the shared experts       */
@@ -85,7 +90,8 @@ typedef struct {
 int64_t moe_max_rows(const moe_config *cfg);
 
 /* Capacity C = ceil(cf*T*k/E) of [P3] "Key Parameters" (capacity_factor: cf
- * times the expected average load), or -1 when dropless or ExpertChoice. */
+ * times the expected average load), or -1 when dropless or ExpertChoice.
+ * Evaluated in IEEE double as ((cf*T)*k)/E. */
 int64_t moe_capacity(const moe_config *cfg);
 
 /* --------------------------------------------------------------------------
@@ -207,6 +213,8 @@ typedef struct {
   size_t shared_ffn_scratch, shared_ffn_scratch_bytes; /* ... of the shared expert */
   size_t z, shared_z; /* pre-activations [rows, n_up*d_ff], [T, n_up*d_ff_shared]
                          kept by moe_layer_fwd_train */
+  size_t stamp;       /* int32 written by the forward's last step: which of
+                         moe_layer_fwd / moe_layer_fwd_train filled z */
   size_t total; /* bytes the workspace must hold */
 } moe_workspace_layout;
 
@@ -255,6 +263,10 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
  * row buffers = padded_rows (moe_max_rows() + 31 * E); shared-expert buffers
  * have shared_rows = T rounded up to 32 rows.
  *   poff [E+1] int32        slot_prow [slots] int32 (padded row or -1)
+ *   roff [E+1] int32        offsets the recomputed GEMM1 runs over: poff, or
+ *                           all zero when the forward kept its
+ *                           pre-activations (shared_roff: the same for the
+ *                           shared expert's {0, rows})
  *   prow_src [padded_rows] int32  forward row of each padded row (-1: pad;
  *                           written when recompute = 0)
  *   d_slot_w [slots] fp32   dL/dw per slot (top-k [T,k]; ExpertChoice the
@@ -270,9 +282,9 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
  *   xs, dys, dxs, zs, dhs   the same for the shared expert
  * ------------------------------------------------------------------------ */
 typedef struct {
-  size_t poff, slot_prow, prow_src, d_slot_w, dlogits, dx_router, router_offset, router_part;
+  size_t poff, roff, slot_prow, prow_src, d_slot_w, dlogits, dx_router, router_offset, router_part;
   size_t xp, dyp, z, dh, dxp;
-  size_t shared_offset, xs, dys, zs, dhs, dxs;
+  size_t shared_offset, shared_roff, xs, dys, zs, dhs, dxs;
   size_t scratch, scratch_bytes, shared_scratch, shared_scratch_bytes;
   size_t padded_rows, shared_rows; /* row counts, not bytes */
   size_t total;                    /* bytes the workspace must hold */
@@ -289,8 +301,14 @@ moe_status moe_layer_fwd_train(const moe_config *cfg, const void *x, const void 
                                size_t workspace_bytes, void *stream);
 /* moe_layer_bwd -- gradients of the whole block.
  *   x, w_router, w1, w2, ws1, ws2: as given to moe_layer_fwd.
- *   fwd_workspace: the workspace of a moe_layer_fwd call on the same inputs
- *     (its routing, permutation and y_perm are read; nothing is written).
+ *   fwd_workspace: the workspace of a moe_layer_fwd or moe_layer_fwd_train
+ *     call on the same inputs (its routing, permutation and y_perm are read;
+ *     nothing is written).
+ *   recompute: 1 re-runs the expert GEMM1; 0 reads the pre-activations a
+ *     training forward kept.  The forward's last step stamps the workspace
+ *     with which forward ran, and the device checks that stamp: after a
+ *     plain moe_layer_fwd, recompute = 0 re-runs GEMM1 as well, so the
+ *     gradients never come from stale pre-activations.
  *   dy [T,d] dtype: dL/dy.
  *   Outputs (dtype, overwritten): dx [T,d], dw_router [E,d],
  *     dw1 [E, n_up*d_ff, d], dw2 [E, d, d_ff], dws1 / dws2 (shared expert,

@@ -29,7 +29,7 @@ moe_status check_config(const moe_config *c) {
   if (c->d_model % 8 || c->d_ff % 8 || c->d_ff_shared % 8) return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (c->act != MOE_ACT_GELU && c->act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
-  if (!(c->capacity_factor >= 0.f) || !isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (!(c->capacity_factor >= 0.0) || !isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (c->routing == MOE_EXPERT_CHOICE) {
     if (c->num_tokens < 1 || c->ec_capacity < 1 || c->ec_capacity > c->num_tokens) return MOE_ERR_INVALID_ARG;
     if (c->num_tokens > kEcMaxTokens) return MOE_ERR_UNSUPPORTED;
@@ -44,8 +44,9 @@ moe_status check_config(const moe_config *c) {
 }
 
 int64_t capacity_of(const moe_config *c) {
-  if (c->routing == MOE_EXPERT_CHOICE || c->capacity_factor == 0.f) return -1;
-  const double v = ceil(static_cast<double>(c->capacity_factor) * c->num_tokens * c->top_k / c->num_experts);
+  if (c->routing == MOE_EXPERT_CHOICE || c->capacity_factor == 0.0) return -1;
+  const double v = ceil(c->capacity_factor * static_cast<double>(c->num_tokens) * static_cast<double>(c->top_k) /
+                        static_cast<double>(c->num_experts));
   return static_cast<int64_t>(v);
 }
 
@@ -197,7 +198,7 @@ moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *ex
 
 moe_status unpermute_impl(const moe_config *cfg, const void *y_perm, const int32_t *tok_ptr,
                           const int32_t *slot_row, const float *slot_w, const void *y_shared, void *y,
-                          void *stream) {
+                          void *stream, int32_t *stamp = nullptr, int32_t stamp_val = 0) {
   if (cfg->num_tokens == 0) return MOE_OK;
   if (!y_perm || !slot_row || !slot_w || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(y_perm) || !aligned16(y) || (y_shared && !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
@@ -216,6 +217,8 @@ moe_status unpermute_impl(const moe_config *cfg, const void *y_perm, const int32
   a.rows = max_rows_of(cfg);
   a.nslots = cfg->routing == MOE_EXPERT_CHOICE ? static_cast<int64_t>(cfg->num_experts) * cfg->ec_capacity
                                                 : static_cast<int64_t>(cfg->num_tokens) * cfg->top_k;
+  a.stamp = stamp;
+  a.stamp_val = stamp_val;
   return hip_status(moe::launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -246,7 +249,7 @@ moe_config shared_config(const moe_config *cfg) {
   moe_config s = *cfg;
   s.num_experts = 1;
   s.top_k = 1;
-  s.capacity_factor = 0.f;
+  s.capacity_factor = 0.0;
   s.routing = MOE_TOPK_SOFTMAX_ALL;
   s.d_ff = cfg->d_ff_shared;
   s.d_ff_shared = 0;
@@ -292,6 +295,7 @@ void make_layout(const moe_config *c, moe_workspace_layout *L) {
   const size_t n_up = c->act == MOE_ACT_SWIGLU ? 2 : 1;
   L->z = take(rows * n_up * static_cast<size_t>(c->d_ff) * s);
   L->shared_z = take(c->d_ff_shared ? T * n_up * static_cast<size_t>(c->d_ff_shared) * s : 0);
+  L->stamp = take(4);
   L->scratch_bytes = ec ? 0 : moe::permute_scratch_bytes(c->num_tokens, c->top_k, c->num_experts);
   L->scratch = take(L->scratch_bytes);
   // the shared expert FFN runs beside the routed one (side stream), so each
@@ -367,6 +371,7 @@ void make_bwd_layout(const moe_config *c, moe_bwd_layout *L) {
   L->padded_rows = P;
   L->shared_rows = Ts;
   L->poff = take((E + 1) * 4);
+  L->roff = take((E + 1) * 4);
   L->slot_prow = take(nslots * 4);
   L->prow_src = take(P * 4);
   L->d_slot_w = take(nslots * 4);
@@ -380,6 +385,7 @@ void make_bwd_layout(const moe_config *c, moe_bwd_layout *L) {
   L->dh = take(P * dff * s);
   L->dxp = take(P * d * s);
   L->shared_offset = take(dffs ? 2 * 4 : 0);
+  L->shared_roff = take(dffs ? 2 * 4 : 0);
   L->xs = take(Ts * d * s);
   L->dys = take(Ts * d * s);
   L->zs = take(Ts * n_up * dffs * s);
@@ -399,7 +405,7 @@ void make_bwd_layout(const moe_config *c, moe_bwd_layout *L) {
 moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const int32_t *offs, const void *w1,
                         const void *w2, void *xp, void *dyp, void *z, void *dh, void *dxp, void *dw1, void *dw2,
                         void *scratch, size_t scratch_bytes, hipStream_t st, const void *z_saved,
-                        const int32_t *z_src, int64_t z_rows) {
+                        const int32_t *z_src, int64_t z_rows, const int32_t *roff, const int32_t *stamp) {
   const int n_up = c->act == MOE_ACT_SWIGLU ? 2 : 1, d = c->d_model;
   moe::BwdGemm g = bwd_gemm(c, moe::BWD_NT);
   g.offs = offs;
@@ -407,8 +413,12 @@ moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const
   g.max_rows = rows;
   g.scratch = scratch;
   g.scratch_bytes = scratch_bytes;
-  // z = xp W1^T  (the recomputed forward), unless a training forward kept z
-  if (!z_saved) {
+  // z = xp W1^T (the recomputed forward).  When the caller asks for the
+  // kept pre-activations this GEMM runs over roff, which the device set to
+  // all zeros after reading the forward's stamp if a training forward kept
+  // z (its workgroups then exit at once), and to offs otherwise.
+  {
+    g.offs = z_saved ? roff : offs;
     g.A = xp;
     g.lda = d;
     g.B = w1;
@@ -419,6 +429,7 @@ moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const
     g.N = n_up * dff;
     g.K = d;
     if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
+    g.offs = offs;
   }
   // dh = dyp W2   (W2_e [d, dff]: K = d rows, N = dff columns)
   g.kind = moe::BWD_NN;
@@ -433,7 +444,8 @@ moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const
   g.K = d;
   if (moe::launch_bwd_gemm(g, st) != hipSuccess) return MOE_ERR_HIP;
   const int act = c->act == MOE_ACT_SWIGLU ? 2 : 1;  // ACT_SWIGLU / ACT_GELU of the kernels
-  if (moe::launch_act_bwd(c->dtype, act, z, dh, offs + E, rows, dff, z_saved, z_src, z_rows, st) != hipSuccess)
+  if (moe::launch_act_bwd(c->dtype, act, z, dh, offs + E, rows, dff, z_saved, z_src, z_rows, st,
+                          z_saved ? stamp : nullptr) != hipSuccess)
     return MOE_ERR_HIP;
   // dxp = dz W1   (W1_e [n_up*dff, d]: K = n_up*dff rows, N = d columns)
   g.A = z;
@@ -542,14 +554,15 @@ moe_status layer_fwd_impl(const moe_config *cfg, const void *x, const void *w_ro
                L.ffn_scratch_bytes, stream, train ? P(L.z) : nullptr);
   if (s != MOE_OK) return s;
   if (join && hipStreamWaitEvent(main_st, join, 0) != hipSuccess) return MOE_ERR_HIP;
-  return unpermute_impl(cfg, P(L.y_perm), tok_ptr, slot_row, slot_w, y_shared, y, stream);
+  return unpermute_impl(cfg, P(L.y_perm), tok_ptr, slot_row, slot_w, y_shared, y, stream,
+                        static_cast<int32_t *>(P(L.stamp)), train ? moe::kStampTrain : moe::kStampPlain);
 }
 
 }  // namespace
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 5; }
+int32_t moe_abi_version(void) { return 6; }
 
 const char *moe_status_string(moe_status s) {
   switch (s) {
@@ -714,6 +727,7 @@ moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_rou
   float *d_slot_w = static_cast<float *>(P(L.d_slot_w));
   float *dlogits = static_cast<float *>(P(L.dlogits));
   float *dx_router = static_cast<float *>(P(L.dx_router));
+  const int32_t *stamp = static_cast<const int32_t *>(F_(F.stamp));
 
   // Shared expert: depends only on x and dy, so it runs on the side stream
   // beside the routed part and is joined before dx is assembled.
@@ -725,13 +739,15 @@ moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_rou
       return MOE_ERR_HIP;
     const int64_t Ts = static_cast<int64_t>(L.shared_rows);
     int32_t *so = static_cast<int32_t *>(P(L.shared_offset));
+    int32_t *sro = static_cast<int32_t *>(P(L.shared_roff));
     if (moe::launch_fill_offsets(so, static_cast<int32_t>(Ts), side->stream) != hipSuccess ||
+        (!recompute && moe::launch_fill_offsets(sro, static_cast<int32_t>(Ts), side->stream, stamp) != hipSuccess) ||
         moe::launch_pad_copy(x, P(L.xs), T, Ts, static_cast<size_t>(d) * es, side->stream) != hipSuccess ||
         moe::launch_pad_copy(dy, P(L.dys), T, Ts, static_cast<size_t>(d) * es, side->stream) != hipSuccess)
       return MOE_ERR_HIP;
     s = ffn_bwd_impl(&sc, 1, cfg->d_ff_shared, Ts, so, ws1, ws2, P(L.xs), P(L.dys), P(L.zs), P(L.dhs), P(L.dxs),
                      dws1, dws2, P(L.shared_scratch), L.shared_scratch_bytes, side->stream,
-                     recompute ? nullptr : F_(F.shared_z), nullptr, T);
+                     recompute ? nullptr : F_(F.shared_z), nullptr, T, sro, stamp);
     if (s != MOE_OK) return s;
     if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_ERR_HIP;
     join = side->join;
@@ -739,7 +755,9 @@ moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_rou
 
   // padded offsets, then the combine's backward (dL/dw per slot, w*dy and x
   // into the padded rows), then zero pad rows
-  if (moe::launch_bwd_offsets(count, E, max_rows_of(cfg), poff, st) != hipSuccess) return MOE_ERR_HIP;
+  int32_t *roff = static_cast<int32_t *>(P(L.roff));
+  if (moe::launch_bwd_offsets(count, E, max_rows_of(cfg), poff, st, recompute ? nullptr : stamp, roff) != hipSuccess)
+    return MOE_ERR_HIP;
   moe::BwdUnpermuteArgs u{};
   u.dtype = cfg->dtype;
   u.T = T;
@@ -835,7 +853,8 @@ moe_status moe_layer_bwd(const moe_config *cfg, const void *x, const void *w_rou
 
   // routed experts
   s = ffn_bwd_impl(cfg, E, cfg->d_ff, prows, poff, w1, w2, P(L.xp), P(L.dyp), P(L.z), P(L.dh), P(L.dxp), dw1, dw2,
-                   P(L.scratch), L.scratch_bytes, st, recompute ? nullptr : F_(F.z), prow_src, max_rows_of(cfg));
+                   P(L.scratch), L.scratch_bytes, st, recompute ? nullptr : F_(F.z), prow_src, max_rows_of(cfg), roff,
+                   stamp);
   if (s != MOE_OK) return s;
 
   // dx: the permutation's backward (each token gathers its copies'

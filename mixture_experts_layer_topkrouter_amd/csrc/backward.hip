@@ -87,8 +87,11 @@ __device__ __forceinline__ void token_slots(const int32_t *tok_ptr, int t, int k
 
 // Padded offsets: poff[e+1] = poff[e] + (count_e rounded up to 32).
 __global__ __launch_bounds__(kThreads) void bwd_offsets_kernel(const int32_t *__restrict__ count, int E,
-                                                               int64_t max_rows, int32_t *__restrict__ poff) {
+                                                               int64_t max_rows, int32_t *__restrict__ poff,
+                                                               const int32_t *__restrict__ stamp,
+                                                               int32_t *__restrict__ roff) {
   __shared__ int tmp[kThreads / kWave + 1];
+  const bool none = roff && *stamp == kStampTrain;  // saved pre-activations: nothing to recompute
   int carry = 0;
   for (int e0 = 0; e0 < E; e0 += kThreads) {
     const int e = e0 + threadIdx.x;
@@ -98,9 +101,11 @@ __global__ __launch_bounds__(kThreads) void bwd_offsets_kernel(const int32_t *__
     int total;
     const int ex = block_excl_scan(v, tmp, &total);
     if (e < E) poff[e] = carry + ex;
+    if (roff && e < E) roff[e] = none ? 0 : carry + ex;
     carry += total;
   }
   if (threadIdx.x == 0) poff[E] = carry;
+  if (roff && threadIdx.x == 0) roff[E] = none ? 0 : carry;
 }
 
 // Backward of the combine (token_unpermutation), one wave per token.  For
@@ -322,12 +327,17 @@ __device__ __forceinline__ float sigmoid_t(float z) {
 // The pre-activations are read from z itself (in place), or, when z_src is
 // given, from row src_row(p) of z_src (the forward's saved z): src[p] when a
 // map is given (-1: a pad row, whose z is 0), else p itself for p < src_rows.
+// With `stamp` given, z_src is used only when *stamp == kStampTrain (the
+// forward that filled it was a training forward); otherwise z holds the
+// recomputed pre-activations and is read in place.
 template <bool BF16, int ACT>
 __global__ __launch_bounds__(kThreads) void act_bwd_kernel(void *__restrict__ z, void *__restrict__ dh,
                                                            const int32_t *__restrict__ rows_of, int64_t prows,
                                                            int dff, const void *__restrict__ z_src,
-                                                           const int32_t *__restrict__ src, int64_t src_rows) {
+                                                           const int32_t *__restrict__ src, int64_t src_rows,
+                                                           const int32_t *__restrict__ stamp) {
   constexpr int kElems = BF16 ? 8 : 4;
+  if (z_src && stamp && *stamp != kStampTrain) z_src = nullptr;
   const int64_t rows = min(max(static_cast<int64_t>(*rows_of), static_cast<int64_t>(0)), prows);
   const int nch = dff / kElems;
   const int64_t n = rows * nch;
@@ -615,8 +625,9 @@ int stream_blocks(int64_t items) {
 
 }  // namespace
 
-hipError_t launch_bwd_offsets(const int32_t *count, int E, int64_t max_rows, int32_t *poff, hipStream_t st) {
-  bwd_offsets_kernel<<<1, kThreads, 0, st>>>(count, E, max_rows, poff);
+hipError_t launch_bwd_offsets(const int32_t *count, int E, int64_t max_rows, int32_t *poff, hipStream_t st,
+                              const int32_t *stamp, int32_t *roff) {
+  bwd_offsets_kernel<<<1, kThreads, 0, st>>>(count, E, max_rows, poff, stamp, stamp ? roff : nullptr);
   return hipGetLastError();
 }
 
@@ -649,10 +660,11 @@ hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_act_bwd(int dtype, int act, void *z, void *dh, const int32_t *rows_of, int64_t prows, int dff,
-                          const void *z_src, const int32_t *src, int64_t src_rows, hipStream_t st) {
+                          const void *z_src, const int32_t *src, int64_t src_rows, hipStream_t st,
+                          const int32_t *stamp) {
   if (prows == 0) return hipSuccess;
   const int blocks = stream_blocks(prows * (dff / (dtype == 1 ? 8 : 4)));
-#define MOE_ACTB(B, A) act_bwd_kernel<B, A><<<blocks, kThreads, 0, st>>>(z, dh, rows_of, prows, dff, z_src, src, src_rows)
+#define MOE_ACTB(B, A) act_bwd_kernel<B, A><<<blocks, kThreads, 0, st>>>(z, dh, rows_of, prows, dff, z_src, src, src_rows, stamp)
   if (dtype == 1) {
     if (act == ACT_SWIGLU) MOE_ACTB(true, ACT_SWIGLU);
     else MOE_ACTB(true, ACT_GELU);

@@ -43,8 +43,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
                                                            const float *__restrict__ slot_w,
                                                            const void *__restrict__ y_shared_,
                                                            void *__restrict__ y_, int T, int d, int k,
-                                                           int64_t rows, int64_t nslots) {
+                                                           int64_t rows, int64_t nslots, int32_t *__restrict__ stamp,
+                                                           int32_t stamp_val) {
   constexpr int kElems = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  if (stamp && blockIdx.x == 0 && threadIdx.x == 0) *stamp = stamp_val;
   const int t = blockIdx.x * kTokens + wave_id();
   if (t >= T) return;
   const int l = lane_id();
@@ -143,16 +145,16 @@ void launch(const CombineArgs &a, int blocks, hipStream_t st) {
   const int per_lane = (nchunk + kWave - 1) / kWave;
   if (per_lane <= 1)
     combine_kernel<BF16, 1><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots);
+                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots, a.stamp, a.stamp_val);
   else if (per_lane <= 2)
     combine_kernel<BF16, 2><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots);
+                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots, a.stamp, a.stamp_val);
   else if (per_lane <= 8)
     combine_kernel<BF16, 4><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots);
+                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots, a.stamp, a.stamp_val);
   else
     combine_kernel<BF16, 8><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots);
+                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots, a.stamp, a.stamp_val);
 }
 
 }  // namespace

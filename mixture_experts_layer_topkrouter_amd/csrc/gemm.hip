@@ -1057,15 +1057,15 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   return f.bm == 256 ? run_bf16<256>(g2, ACT_NONE, st) : run_bf16<128>(g2, ACT_NONE, st);
 }
 
-__global__ void fill_offsets_kernel(int32_t *dst, int32_t t) {
+__global__ void fill_offsets_kernel(int32_t *dst, int32_t t, const int32_t *stamp) {
   if (threadIdx.x == 0) {
     dst[0] = 0;
-    dst[1] = t;
+    dst[1] = (stamp && *stamp == kStampTrain) ? 0 : t;
   }
 }
 
-hipError_t launch_fill_offsets(int32_t *dst, int32_t t, hipStream_t st) {
-  fill_offsets_kernel<<<1, 64, 0, st>>>(dst, t);
+hipError_t launch_fill_offsets(int32_t *dst, int32_t t, hipStream_t st, const int32_t *stamp) {
+  fill_offsets_kernel<<<1, 64, 0, st>>>(dst, t, stamp);
   return hipGetLastError();
 }
 

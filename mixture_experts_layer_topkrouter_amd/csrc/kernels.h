@@ -80,11 +80,19 @@ struct CombineArgs {
   void *y;
   int64_t rows;    // rows of y_perm
   int64_t nslots;  // entries of slot_row / slot_w
+  int32_t *stamp;  // optional: workgroup 0 writes stamp_val here once the
+  int32_t stamp_val;  // combine has been enqueued (the forward's last step)
 };
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st);
 
+// Stamps moe_layer_fwd / moe_layer_fwd_train leave in their workspace: the
+// backward reads the saved pre-activations only after a training forward
+// (kStampTrain) and recomputes them otherwise.
+constexpr int32_t kStampPlain = 0x3e5f0000, kStampTrain = 0x3e5f0001;
+
 // Fills a small int32 device array (used for the shared expert's {0, T}).
-hipError_t launch_fill_offsets(int32_t *dst, int32_t t, hipStream_t st);
+// With `stamp` given, dst = {0, 0} when *stamp == kStampTrain (device-side).
+hipError_t launch_fill_offsets(int32_t *dst, int32_t t, hipStream_t st, const int32_t *stamp = nullptr);
 
 // ---- backward pass (backward.hip) ----------------------------------------
 // Expert blocks of the backward's row layout start on multiples of this many
@@ -125,13 +133,19 @@ struct GatherDxArgs {
 };
 hipError_t launch_gather_dx(const GatherDxArgs &a, hipStream_t st);
 
-hipError_t launch_bwd_offsets(const int32_t *count, int E, int64_t max_rows, int32_t *poff, hipStream_t st);
+// poff = padded exclusive offsets; with roff given, also roff = poff, or all
+// zeros when *stamp == kStampTrain (the recompute GEMM then has no rows).
+hipError_t launch_bwd_offsets(const int32_t *count, int E, int64_t max_rows, int32_t *poff, hipStream_t st,
+                              const int32_t *stamp = nullptr, int32_t *roff = nullptr);
 hipError_t launch_pad_zero(const int32_t *poff, const int32_t *count, int E, int64_t prows, size_t row_bytes,
                            void *b0, void *b1, int32_t *prow_src, hipStream_t st);
 hipError_t launch_pad_copy(const void *src, void *dst, int64_t rows, int64_t prows, size_t row_bytes,
                            hipStream_t st);
+// z_src (the saved pre-activations) is read when given and, if `stamp` is
+// given too, only when *stamp == kStampTrain; otherwise z is read in place.
 hipError_t launch_act_bwd(int dtype, int act, void *z, void *dh, const int32_t *rows_of, int64_t prows, int dff,
-                          const void *z_src, const int32_t *src, int64_t src_rows, hipStream_t st);
+                          const void *z_src, const int32_t *src, int64_t src_rows, hipStream_t st,
+                          const int32_t *stamp = nullptr);
 hipError_t launch_act_fwd(int dtype, int act, const void *z, void *h, const int32_t *rows_of, int64_t max_rows,
                           int dff, hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);

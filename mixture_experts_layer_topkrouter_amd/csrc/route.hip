@@ -2,8 +2,8 @@
 // scores plus a per-expert top-C selection (ExpertChoiceRouter).
 //
 // "How MegaDLMs Implements Mixture of Experts (MoE) Architectures", section
-// "Routing Mechanisms: Top-K vs Expert Choice": the TopKRouter computes dense
-// gate logits with a learned linear layer, applies a softmax and keeps the k
+// "Routing Mechanisms: Top-K vs Expert Choice": the TopKRouter scores every
+// expert for every token with one trained linear map, applies a softmax and keeps the k
 // best experts per token (probability weights + routing map); the
 // ExpertChoiceRouter lets each expert choose its tokens by routing score.
 //

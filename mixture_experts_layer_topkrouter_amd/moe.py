@@ -44,7 +44,7 @@ class MoeConfig(ctypes.Structure):
         ("top_k", ctypes.c_int32),
         ("d_ff", ctypes.c_int32),
         ("d_ff_shared", ctypes.c_int32),
-        ("capacity_factor", ctypes.c_float),
+        ("capacity_factor", ctypes.c_double),
         ("ec_capacity", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("act", ctypes.c_int32),
@@ -56,16 +56,16 @@ _LAYOUT_FIELDS = ["logits", "topk_idx", "topk_w", "scores", "ec_token", "ec_w", 
                   "slot_row", "slot_w", "tok_ptr", "expert_count", "expert_load", "expert_offset",
                   "shared_offset", "h", "y_perm", "shared_h", "shared_y", "scratch", "scratch_bytes",
                   "ffn_scratch", "ffn_scratch_bytes", "shared_ffn_scratch", "shared_ffn_scratch_bytes", "z",
-                  "shared_z", "total"]
+                  "shared_z", "stamp", "total"]
 
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in _LAYOUT_FIELDS]
 
 
-_BWD_LAYOUT_FIELDS = ["poff", "slot_prow", "prow_src", "d_slot_w", "dlogits", "dx_router", "router_offset", "router_part",
+_BWD_LAYOUT_FIELDS = ["poff", "roff", "slot_prow", "prow_src", "d_slot_w", "dlogits", "dx_router", "router_offset", "router_part",
                       "xp", "dyp", "z",
-                      "dh", "dxp", "shared_offset", "xs", "dys", "zs", "dhs", "dxs", "scratch", "scratch_bytes",
+                      "dh", "dxp", "shared_offset", "shared_roff", "xs", "dys", "zs", "dhs", "dxs", "scratch", "scratch_bytes",
                       "shared_scratch", "shared_scratch_bytes", "padded_rows", "shared_rows", "total"]
 
 
@@ -136,6 +136,44 @@ def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _arg(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype], numel: int):
+    """Device pointer of `t` after the checks the C ABI cannot make from a bare
+    pointer: the element type (None: any, e.g. byte workspaces), a dense
+    layout, at least `numel` elements, and a GPU tensor.  None passes NULL
+    (the library decides whether that argument may be NULL)."""
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: holds {t.numel()} elements, needs at least {numel}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor, got device {t.device}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+_I32, _F32 = torch.int32, torch.float32
+
+
+def _dims(cfg: MoeConfig) -> dict:
+    """Element counts of every buffer the entry points take, for this config."""
+    T, E, d = cfg.num_tokens, cfg.num_experts, cfg.d_model
+    ec = cfg.routing == EXPERT_CHOICE
+    C = cfg.ec_capacity if ec else 0
+    k = 0 if ec else cfg.top_k
+    n_up = 2 if cfg.act == SWIGLU else 1
+    rows = max(max_rows(cfg), 0)
+    return {"T": T, "E": E, "d": d, "C": C, "k": k, "rows": rows, "slots": E * C if ec else T * k,
+            "w1": E * n_up * cfg.d_ff * d, "w2": E * d * cfg.d_ff, "ws1": n_up * cfg.d_ff_shared * d,
+            "ws2": d * cfg.d_ff_shared}
+
+
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -159,9 +197,15 @@ def capacity(cfg: MoeConfig) -> int:
 def route(cfg: MoeConfig, x: Optional[torch.Tensor], w_router: Optional[torch.Tensor], logits: torch.Tensor,
           topk_idx=None, topk_w=None, bias=None, bias_stride: int = 0, scores=None, ec_token=None, ec_w=None,
           stream=None):
-    _check(load_library().moe_route(ctypes.byref(cfg), _p(x), _p(w_router), _p(bias), bias_stride, _p(logits),
-                                    _p(topk_idx), _p(topk_w), _p(scores), _p(ec_token), _p(ec_w),
-                                    _stream(stream)), "moe_route")
+    n, dt = _dims(cfg), torch_dtype(cfg)
+    T, E = n["T"], n["E"]
+    _check(load_library().moe_route(
+        ctypes.byref(cfg), _arg(x, "x", dt, T * n["d"]), _arg(w_router, "w_router", dt, E * n["d"]),
+        _arg(bias, "logit_bias", _F32, E if bias_stride == 0 else T * E), bias_stride,
+        _arg(logits, "logits", _F32, T * E), _arg(topk_idx, "topk_idx", _I32, T * n["k"]),
+        _arg(topk_w, "topk_w", _F32, T * n["k"]), _arg(scores, "scores", _F32, T * E),
+        _arg(ec_token, "ec_token", _I32, E * n["C"]), _arg(ec_w, "ec_w", _F32, E * n["C"]), _stream(stream)),
+        "moe_route")
 
 
 def permute_scratch_bytes(cfg: MoeConfig) -> int:
@@ -172,11 +216,16 @@ def permute_scratch_bytes(cfg: MoeConfig) -> int:
 
 def permute(cfg: MoeConfig, x, x_perm, row_token, slot_row, expert_count, expert_load, expert_offset, *,
             topk_idx=None, ec_token=None, ec_w=None, slot_w=None, tok_ptr=None, scratch=None, stream=None):
-    nbytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
-    _check(load_library().moe_permute(ctypes.byref(cfg), _p(x), _p(topk_idx), _p(ec_token), _p(ec_w), _p(x_perm),
-                                      _p(row_token), _p(slot_row), _p(slot_w), _p(tok_ptr), _p(expert_count),
-                                      _p(expert_load), _p(expert_offset), _p(scratch), nbytes, _stream(stream)),
-           "moe_permute")
+    n, dt = _dims(cfg), torch_dtype(cfg)
+    T, E, d, rows = n["T"], n["E"], n["d"], n["rows"]
+    _check(load_library().moe_permute(
+        ctypes.byref(cfg), _arg(x, "x", dt, T * d), _arg(topk_idx, "topk_idx", _I32, T * n["k"]),
+        _arg(ec_token, "ec_token", _I32, E * n["C"]), _arg(ec_w, "ec_w", _F32, E * n["C"]),
+        _arg(x_perm, "x_perm", dt, rows * d), _arg(row_token, "row_token", _I32, rows),
+        _arg(slot_row, "slot_row", _I32, n["slots"]), _arg(slot_w, "slot_w", _F32, n["slots"]),
+        _arg(tok_ptr, "tok_ptr", _I32, T + 1), _arg(expert_count, "expert_count", _I32, E),
+        _arg(expert_load, "expert_load", _I32, E), _arg(expert_offset, "expert_offset", _I32, E + 1),
+        _arg(scratch, "scratch", None, 0), _nbytes(scratch), _stream(stream)), "moe_permute")
 
 
 def expert_ffn_workspace_bytes(cfg: MoeConfig) -> int:
@@ -195,14 +244,22 @@ def expert_ffn(cfg: MoeConfig, x_perm, expert_offset, w1, w2, h, y_perm, workspa
     """moe_expert_ffn.  `workspace` is a uint8 device tensor of
     expert_ffn_workspace_bytes(cfg) bytes (see alloc_ffn_workspace); None
     passes NULL, which the library rejects when the configuration needs one."""
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().moe_expert_ffn(ctypes.byref(cfg), _p(x_perm), _p(expert_offset), _p(w1), _p(w2), _p(h),
-                                         _p(y_perm), _p(workspace), nbytes, _stream(stream)), "moe_expert_ffn")
+    n, dt = _dims(cfg), torch_dtype(cfg)
+    rows, d = n["rows"], n["d"]
+    _check(load_library().moe_expert_ffn(
+        ctypes.byref(cfg), _arg(x_perm, "x_perm", dt, rows * d), _arg(expert_offset, "expert_offset", _I32, n["E"] + 1),
+        _arg(w1, "w1", dt, n["w1"]), _arg(w2, "w2", dt, n["w2"]), _arg(h, "h", dt, rows * cfg.d_ff),
+        _arg(y_perm, "y_perm", dt, rows * d), _arg(workspace, "workspace", None, 0), _nbytes(workspace),
+        _stream(stream)), "moe_expert_ffn")
 
 
 def unpermute(cfg: MoeConfig, y_perm, slot_row, slot_w, y, *, tok_ptr=None, y_shared=None, stream=None):
-    _check(load_library().moe_unpermute(ctypes.byref(cfg), _p(y_perm), _p(tok_ptr), _p(slot_row), _p(slot_w),
-                                        _p(y_shared), _p(y), _stream(stream)), "moe_unpermute")
+    n, dt = _dims(cfg), torch_dtype(cfg)
+    T, d = n["T"], n["d"]
+    _check(load_library().moe_unpermute(
+        ctypes.byref(cfg), _arg(y_perm, "y_perm", dt, n["rows"] * d), _arg(tok_ptr, "tok_ptr", _I32, T + 1),
+        _arg(slot_row, "slot_row", _I32, n["slots"]), _arg(slot_w, "slot_w", _F32, n["slots"]),
+        _arg(y_shared, "y_shared", dt, T * d), _arg(y, "y", dt, T * d), _stream(stream)), "moe_unpermute")
 
 
 def layer_workspace(cfg: MoeConfig) -> Dict[str, int]:
@@ -215,11 +272,15 @@ def layer_fwd(cfg: MoeConfig, x, w_router, w1, w2, y, workspace, *, bias=None, b
               ws2=None, train: bool = False, stream=None):
     """moe_layer_fwd, or moe_layer_fwd_train (keeps the expert
     pre-activations for a backward without recompute) when train is set."""
-    nbytes = workspace.numel() * workspace.element_size()
+    n, dt = _dims(cfg), torch_dtype(cfg)
+    T, E, d = n["T"], n["E"], n["d"]
     lib = load_library()
     fn = lib.moe_layer_fwd_train if train else lib.moe_layer_fwd
-    _check(fn(ctypes.byref(cfg), _p(x), _p(w_router), _p(bias), bias_stride, _p(w1), _p(w2), _p(ws1), _p(ws2), _p(y),
-              _p(workspace), nbytes, _stream(stream)), "moe_layer_fwd_train" if train else "moe_layer_fwd")
+    _check(fn(ctypes.byref(cfg), _arg(x, "x", dt, T * d), _arg(w_router, "w_router", dt, E * d),
+              _arg(bias, "logit_bias", _F32, E if bias_stride == 0 else T * E), bias_stride,
+              _arg(w1, "w1", dt, n["w1"]), _arg(w2, "w2", dt, n["w2"]), _arg(ws1, "ws1", dt, n["ws1"]),
+              _arg(ws2, "ws2", dt, n["ws2"]), _arg(y, "y", dt, T * d), _arg(workspace, "workspace", None, 0),
+              _nbytes(workspace), _stream(stream)), "moe_layer_fwd_train" if train else "moe_layer_fwd")
 
 
 def layer_bwd_workspace(cfg: MoeConfig) -> Dict[str, int]:
@@ -230,13 +291,16 @@ def layer_bwd_workspace(cfg: MoeConfig) -> Dict[str, int]:
 
 def layer_bwd(cfg: MoeConfig, x, w_router, w1, w2, fwd_workspace, dy, dx, dw_router, dw1, dw2, workspace, *,
               ws1=None, ws2=None, dws1=None, dws2=None, recompute: bool = True, stream=None):
-    fbytes = fwd_workspace.numel() * fwd_workspace.element_size()
-    nbytes = workspace.numel() * workspace.element_size()
-    _check(load_library().moe_layer_bwd(ctypes.byref(cfg), _p(x), _p(w_router), _p(w1), _p(w2), _p(ws1), _p(ws2),
-                                        _p(fwd_workspace), fbytes, _p(dy), _p(dx), _p(dw_router), _p(dw1), _p(dw2),
-                                        _p(dws1), _p(dws2), int(bool(recompute)), _p(workspace), nbytes,
-                                        _stream(stream)),
-           "moe_layer_bwd")
+    n, dt = _dims(cfg), torch_dtype(cfg)
+    T, E, d = n["T"], n["E"], n["d"]
+    _check(load_library().moe_layer_bwd(
+        ctypes.byref(cfg), _arg(x, "x", dt, T * d), _arg(w_router, "w_router", dt, E * d), _arg(w1, "w1", dt, n["w1"]),
+        _arg(w2, "w2", dt, n["w2"]), _arg(ws1, "ws1", dt, n["ws1"]), _arg(ws2, "ws2", dt, n["ws2"]),
+        _arg(fwd_workspace, "fwd_workspace", None, 0), _nbytes(fwd_workspace), _arg(dy, "dy", dt, T * d),
+        _arg(dx, "dx", dt, T * d), _arg(dw_router, "dw_router", dt, E * d), _arg(dw1, "dw1", dt, n["w1"]),
+        _arg(dw2, "dw2", dt, n["w2"]), _arg(dws1, "dws1", dt, n["ws1"]), _arg(dws2, "dws2", dt, n["ws2"]),
+        int(bool(recompute)), _arg(workspace, "workspace", None, 0), _nbytes(workspace), _stream(stream)),
+        "moe_layer_bwd")
 
 
 # ------------------------------------------------ allocation conveniences --

@@ -103,7 +103,7 @@ def _c(a, dtype=None):
 # ---------------------------------------------------------------------------
 
 def logits(x, wr, bias=None, bias_stride: int = 0) -> np.ndarray:
-    """Router logits in fp64 ("Routing Mechanisms": a learned linear gate)."""
+    """Router logits in fp64 ("Routing Mechanisms": one trained linear map per token)."""
     x, wr = _c(x), _c(wr)
     assert _dt(x) == _dt(wr)
     T, d = x.shape

@@ -9,8 +9,8 @@
  *
  * What it follows (page title, then section):
  *   [P1] "How MegaDLMs Implements Mixture of Experts (MoE) Architectures"
- *        - "Routing Mechanisms: Top-K vs Expert Choice": the TopKRouter turns
- *          tokens into dense gate logits with a learned linear layer, applies a
+ *        - "Routing Mechanisms: Top-K vs Expert Choice": the TopKRouter scores
+ *          every expert for every token with one trained linear map, applies a
  *          softmax and keeps the k best experts per token, handing the
  *          dispatcher probability weights plus a routing map; the
  *          ExpertChoiceRouter lets every expert pick its tokens by score.
@@ -68,7 +68,8 @@ static double ld(const void *p, int64_t i, int dt) {
   return (double)f;
 }
 
-/* [P1] Routing Mechanisms: dense gate logits through a learned linear layer.
+/* [P1] Routing Mechanisms: the router scores every expert for every token with
+ * one trained linear map (no bias of its own; the optional bias is an input).
  * logits[t,e] = sum_i x[t,i] * W_r[e,i]  (+ bias).  bias_stride 0: bias[e];
  * bias_stride E: bias[t*E+e]; bias NULL: no bias. */
 void orc_logits(int T, int d, int E, int dt, const void *x, const void *wr,

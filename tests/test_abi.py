@@ -22,7 +22,7 @@ def test_library_exports_every_header_symbol():
 
 def test_status_strings_and_version():
     lib = moe.load_library()
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
 
@@ -162,3 +162,69 @@ def test_backward_argument_errors():
     sh = _cfg(d_ff_shared=64)
     assert lib.moe_layer_bwd(ctypes.byref(sh), fake, fake, fake, fake, None, None, fake, 1 << 30, fake, fake, fake,
                              fake, fake, None, None, 1, fake, 1 << 30, None) == 1  # shared expert without its weights
+
+
+@pytest.mark.parametrize("cf", [0.3, 0.5, 1.0, 1.1, 1.2, 1.25, 1.6, 2.2, 3.7])
+def test_capacity_agrees_with_oracle(cf):
+    """moe_capacity and the oracle's capacity evaluate ceil(cf*T*k/E) the same
+    way (cf travels as a double), including shapes where cf*T*k/E is an
+    integer that a float32 factor would have pushed over (1.2 * 100 / 4)."""
+    import oracle
+    for T in (1, 7, 100, 256, 1000, 4096, 16384):
+        for k in (1, 2, 6):
+            for E in (4, 8, 10, 64, 128):
+                if k > E:
+                    continue
+                cfg = _cfg(num_tokens=T, num_experts=E, top_k=k, capacity_factor=cf)
+                assert moe.capacity(cfg) == oracle.capacity(cf, T, k, E), (cf, T, k, E)
+
+
+def test_capacity_of_factors_float32_cannot_hold():
+    """Factors whose float32 value sits above the decimal one: the capacity is
+    still cf times the average load, rounded up (P3's capacity_factor)."""
+    for cf, T, k, E, want in ((1.2, 100, 1, 4, 30), (1.1, 1000, 1, 4, 275), (0.3, 100, 1, 10, 3),
+                              (1.25, 256, 2, 8, 80), (1.0, 16384, 1, 128, 128)):
+        assert moe.capacity(_cfg(num_tokens=T, num_experts=E, top_k=k, capacity_factor=cf)) == want
+
+
+@pytest.mark.parametrize("case", ["dtype", "contiguity", "size", "device"])
+def test_binding_checks_tensors_before_the_call(case):
+    """The binding rejects a tensor of the wrong element type, a strided view,
+    a buffer too short for the configuration, or a host tensor, before it
+    hands a pointer to the library (CPU tensors: no GPU is involved)."""
+    import torch
+    cfg = _cfg(num_tokens=16, d_model=64, num_experts=8, top_k=2, dtype=W.F32)
+    T, E, d, k = 16, 8, 64, 2
+    x = torch.zeros(T, d)
+    wr = torch.zeros(E, d)
+    logits = torch.zeros(T, E)
+    idx = torch.zeros(T, k, dtype=torch.int32)
+    tw = torch.zeros(T, k)
+    if case == "dtype":
+        bad = dict(x=x.to(torch.float64))
+        err = TypeError
+    elif case == "contiguity":
+        bad = dict(x=torch.zeros(d, T).t())
+        err = ValueError
+    elif case == "size":
+        bad = dict(x=torch.zeros(T - 1, d))
+        err = ValueError
+    else:
+        bad = {}
+        err = ValueError
+    args = dict(x=x, w_router=wr, logits=logits, topk_idx=idx, topk_w=tw)
+    args.update(bad)
+    with pytest.raises(err):
+        moe.route(cfg, args["x"], args["w_router"], args["logits"], args["topk_idx"], args["topk_w"],
+                  stream=_NoStream())
+    # the other entry points check their tensors the same way
+    with pytest.raises(ValueError):
+        moe.unpermute(cfg, torch.zeros(T * k, d), torch.zeros(T, k, dtype=torch.int32), torch.zeros(T, k),
+                      torch.zeros(T - 1, d), stream=_NoStream())
+
+
+class _NoStream:
+    """Stands in for a stream: the checks fail before it is read."""
+    @property
+    def cuda_stream(self):
+        raise AssertionError("the binding reached the library call")
