@@ -45,7 +45,9 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1, /* a host-side check failed; nothing was enqueued */
   MOE_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. E > 256)        */
   MOE_ERR_WORKSPACE = 3,   /* workspace/scratch smaller than required          */
-  MOE_ERR_HIP = 4          /* a HIP launch failed                              */
+  MOE_ERR_HIP = 4,         /* a HIP launch failed                              */
+  MOE_ERR_NOALLOC_LIMIT = 5 /* the allocation-free entry point's static scratch
+                               is smaller than this configuration needs       */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -149,6 +151,28 @@ moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk
                        int32_t *row_token, int32_t *slot_row, float *slot_w, int32_t *tok_ptr,
                        int32_t *expert_count, int32_t *expert_load, int32_t *expert_offset,
                        void *scratch, size_t scratch_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * moe_permute_noalloc -- moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results without the scratch
+ * pair.  Its per-block counts and ranks live in a static device array of
+ * MOE_PERMUTE_NOALLOC_MAX_BYTES that each GPU the library runs on holds until
+ * the process ends; the call itself allocates nothing.  A configuration whose
+ * moe_permute_scratch_bytes() exceeds that maximum returns
+ * MOE_ERR_NOALLOC_LIMIT and enqueues nothing (about 1.7 M assignments T*k
+ * with 256 experts; ExpertChoice and T*k <= 8192 use no scratch at all).
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls enqueued on one stream are ordered, but two calls that
+ * overlap on one GPU (different streams or host threads without ordering)
+ * race and give undefined results.
+ * ------------------------------------------------------------------------ */
+#define MOE_PERMUTE_NOALLOC_MAX_BYTES (8u << 20)
+moe_status moe_permute_noalloc(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                               const int32_t *ec_token, const float *ec_w, void *x_perm,
+                               int32_t *row_token, int32_t *slot_row, float *slot_w, int32_t *tok_ptr,
+                               int32_t *expert_count, int32_t *expert_load, int32_t *expert_offset,
+                               void *stream);
 
 /* Bytes of device workspace moe_expert_ffn needs for this configuration:
  * room for the fp32 partial tiles of GEMM tiles cut along K.

@@ -7,9 +7,15 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.h"
+
+// Scratch of moe_permute_noalloc: one copy per GPU, resident for the life of
+// the process.  Host code never uses this name as an address (on the host
+// it is only a stand-in); noalloc_scratch() looks up the device address.
+static __device__ __align__(256) unsigned char scratch[MOE_PERMUTE_NOALLOC_MAX_BYTES];
 
 namespace {
 
@@ -159,6 +165,23 @@ moe_status permute_impl(const moe_config *cfg, const void *x, const int32_t *top
   a.rank = reinterpret_cast<int32_t *>(static_cast<char *>(scratch) +
                                        align256(static_cast<size_t>(nblk * cfg->num_experts) * 4));
   return hip_status(moe::launch_permute_topk(a, st));
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+void *noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
 }
 
 size_t ffn_scratch_of(const moe_config *c) {
@@ -571,6 +594,7 @@ const char *moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_NOALLOC_LIMIT: return "larger than the allocation-free entry point's static scratch";
   }
   return "unknown status";
 }
@@ -612,6 +636,22 @@ moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk
   if (s != MOE_OK) return s;
   return permute_impl(cfg, x, topk_idx, ec_token, ec_w, x_perm, row_token, slot_row, slot_w, tok_ptr,
                       expert_count, expert_load, expert_offset, scratch, scratch_bytes, stream);
+}
+
+moe_status moe_permute_noalloc(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                               const int32_t *ec_token, const float *ec_w, void *x_perm, int32_t *row_token,
+                               int32_t *slot_row, float *slot_w, int32_t *tok_ptr, int32_t *expert_count,
+                               int32_t *expert_load, int32_t *expert_offset, void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  const size_t need = cfg->routing == MOE_EXPERT_CHOICE
+                          ? 0
+                          : moe::permute_scratch_bytes(cfg->num_tokens, cfg->top_k, cfg->num_experts);
+  if (need > MOE_PERMUTE_NOALLOC_MAX_BYTES) return MOE_ERR_NOALLOC_LIMIT;
+  void *ws = nullptr;
+  if (need > 0 && !(ws = noalloc_scratch())) return MOE_ERR_HIP;
+  return permute_impl(cfg, x, topk_idx, ec_token, ec_w, x_perm, row_token, slot_row, slot_w, tok_ptr, expert_count,
+                      expert_load, expert_offset, ws, need, stream);
 }
 
 moe_status moe_expert_ffn_workspace_bytes(const moe_config *cfg, size_t *bytes) {

@@ -27,7 +27,7 @@ GELU, SWIGLU = 0, 1
 SOFTMAX_ALL, SOFTMAX_TOPK, EXPERT_CHOICE = 0, 1, 2
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
-          4: "MOE_ERR_HIP"}
+          4: "MOE_ERR_HIP", 5: "MOE_ERR_NOALLOC_LIMIT"}
 
 
 class MoeError(RuntimeError):
@@ -97,6 +97,7 @@ def load_library() -> ctypes.CDLL:
         "moe_route": ([CP, P, P, P, i64, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_permute_scratch_bytes": ([CP, ctypes.POINTER(sz)], ctypes.c_int),
         "moe_permute": ([CP, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "moe_permute_noalloc": ([CP, P, P, P, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_expert_ffn_workspace_bytes": ([CP, ctypes.POINTER(sz)], ctypes.c_int),
         "moe_expert_ffn": ([CP, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_unpermute": ([CP, P, P, P, P, P, P, P], ctypes.c_int),
@@ -226,6 +227,22 @@ def permute(cfg: MoeConfig, x, x_perm, row_token, slot_row, expert_count, expert
         _arg(tok_ptr, "tok_ptr", _I32, T + 1), _arg(expert_count, "expert_count", _I32, E),
         _arg(expert_load, "expert_load", _I32, E), _arg(expert_offset, "expert_offset", _I32, E + 1),
         _arg(scratch, "scratch", None, 0), _nbytes(scratch), _stream(stream)), "moe_permute")
+
+
+def permute_noalloc(cfg: MoeConfig, x, x_perm, row_token, slot_row, expert_count, expert_load, expert_offset, *,
+                    topk_idx=None, ec_token=None, ec_w=None, slot_w=None, tok_ptr=None, stream=None):
+    """moe_permute_noalloc: moe_permute with its scratch in the library's
+    static device array (nothing is allocated per call)."""
+    n, dt = _dims(cfg), torch_dtype(cfg)
+    T, E, d, rows = n["T"], n["E"], n["d"], n["rows"]
+    _check(load_library().moe_permute_noalloc(
+        ctypes.byref(cfg), _arg(x, "x", dt, T * d), _arg(topk_idx, "topk_idx", _I32, T * n["k"]),
+        _arg(ec_token, "ec_token", _I32, E * n["C"]), _arg(ec_w, "ec_w", _F32, E * n["C"]),
+        _arg(x_perm, "x_perm", dt, rows * d), _arg(row_token, "row_token", _I32, rows),
+        _arg(slot_row, "slot_row", _I32, n["slots"]), _arg(slot_w, "slot_w", _F32, n["slots"]),
+        _arg(tok_ptr, "tok_ptr", _I32, T + 1), _arg(expert_count, "expert_count", _I32, E),
+        _arg(expert_load, "expert_load", _I32, E), _arg(expert_offset, "expert_offset", _I32, E + 1),
+        _stream(stream)), "moe_permute_noalloc")
 
 
 def expert_ffn_workspace_bytes(cfg: MoeConfig) -> int:
