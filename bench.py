@@ -59,26 +59,35 @@ def parse():
                     help="per-stage cold timings: calls of each stage, each after a 512-MiB write that evicts "
                          "L2 and MALL; the median is reported (0: skip)")
     ap.add_argument("--no-hbm-probe", dest="hbm_probe", action="store_false",
-                    help="skip the copy / fill / read rate measurement of the device's HBM")
+                    help="skip the read / write / copy rate measurement of the device's HBM")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the HIP-graph replay timing of the layer")
+    ap.add_argument("--no-workloads", dest="workloads", action="store_false",
+                    help="skip the other workloads (each: median layer time and stage breakdown, "
+                         "after the headline's timed regions)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
-def algorithmic(w, n_rows: int, n_active: int):
-    """Algorithmic work per stage (bytes or flops), from the kept rows N and
-    the number of experts that received rows."""
+def algorithmic(w, n_rows: int, n_active: int, t_used: int = None):
+    """Algorithmic work per stage (bytes or flops), from the kept rows N, the
+    number of experts that received rows and the number of tokens with at
+    least one kept row (t_used; default every token)."""
     s = w.elem_bytes
     T, d, E = w.T, w.d, w.E
     k = w.k if w.routing != 2 else 0
     A = w.assignments
+    t_used = T if t_used is None else t_used
     n_mat = 3 if w.act == 1 else 2
     out = {}
-    route_b = T * d * s + E * d * s + T * E * 4 + (T * k * 8 if k else T * E * 4 + E * w.ec_capacity * 8)
+    # x and W_r read, logits written, the bias read (per expert or per token),
+    # then top-k indices and weights, or scores and the per-expert choice
+    bias_b = {"none": 0, "expert": E * 4, "pairs": T * E * 4}[w.bias]
+    route_b = T * d * s + E * d * s + T * E * 4 + bias_b + (T * k * 8 if k else T * E * 4 + E * w.ec_capacity * 8)
     out["route"] = ("bytes", route_b)
-    out["permute"] = ("bytes", T * d * s + n_rows * d * s + A * 12)
+    # rows of tokens with a kept slot read once, kept rows written, indices
+    out["permute"] = ("bytes", t_used * d * s + n_rows * d * s + A * 12)
     ffn_flops = n_rows * 2 * n_mat * d * w.d_ff
     w_bytes = n_active * n_mat * d * w.d_ff * s
     out["expert_ffn"] = ("flops", ffn_flops, w_bytes + n_rows * d * s * 2 + n_rows * w.d_ff * s * 2)
@@ -115,29 +124,13 @@ def gemm_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU exchange is not built",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    from mixture_experts_layer_topkrouter_amd import moe
-    from mixture_experts_layer_topkrouter_amd import workloads as W
-
-    w = W.WORKLOADS[args.workload]
-    torch.cuda.set_device(0)
-    dev_name = torch.cuda.get_device_name(0)
-    t_gen = time.time()
-    inp = W.make_inputs(w, seed=0)
-    t_gen = time.time() - t_gen
-    cfg = moe.make_config(w)
-    dev = moe.upload(inp)
-    layer = moe.MoELayer(cfg, dev)  # owns the workspace and y; its views are the intermediates
+def stage_functions(w, cfg, dev, layer, moe, W, torch):
+    """One callable per stage of the step-by-step path (route, permute, routed
+    FFN, shared FFN, unpermute), on the intermediates of `layer`'s workspace;
+    each rewrites only its own outputs, so any stage can be re-run on its own
+    once a whole step has run."""
     T, E, d = w.T, w.E, w.d
     ec = w.routing == W.EXPERT_CHOICE
-    k = 0 if ec else w.k
     V = layer.view
     logits = V("logits")
     x_perm, row_token, slot_row = V("x_perm"), V("row_token"), V("slot_row")
@@ -185,7 +178,131 @@ def main():
                                              y_shared=ys if w.d_ff_shared else None))
         return fns
 
-    fns = stage_fns()
+    return names, stage_fns()
+
+
+def kept_counts(w, layer, W):
+    """Kept rows N, experts with rows, and tokens with at least one kept row
+    (read from the device after a step)."""
+    V = layer.view
+    n_rows = int(V("expert_offset")[-1].item())
+    n_active = int((V("expert_count").cpu().numpy() > 0).sum())
+    if w.routing == W.EXPERT_CHOICE:
+        t_used = int((V("tok_ptr").diff() > 0).sum().item())
+    else:
+        t_used = int((V("slot_row") >= 0).any(dim=1).sum().item())
+    return n_rows, n_active, t_used
+
+
+def stage_rates(w, work, ms, peak_flops, peak_hbm):
+    """Per-stage algorithmic rates from stage durations (ms)."""
+    out = {}
+    for n, t in ms.items():
+        kind = work[n][0]
+        sec = t / 1e3
+        ent = {"median_ms": round(t, 4)}
+        if kind == "bytes":
+            ent["GB/s"] = round(work[n][1] / sec / 1e9, 1)
+            ent["hbm_frac"] = round(work[n][1] / sec / 1e9 / peak_hbm, 4)
+        else:
+            ent["TFLOP/s"] = round(work[n][1] / sec / 1e12, 1)
+            ent["mfma_frac"] = round(work[n][1] / sec / 1e12 / peak_flops, 4)
+            if len(work[n]) > 2:
+                ent["GB/s"] = round(work[n][2] / sec / 1e9, 1)
+                ent["hbm_frac"] = round(work[n][2] / sec / 1e9 / peak_hbm, 4)
+        out[n] = ent
+    return out
+
+
+def measure_workload(name, steps, warmup, moe, W, torch):
+    """One workload besides the headline one: the median moe_layer_fwd time
+    (HIP events around each of `steps` calls), tokens/s at that median, the
+    median of every stage of the step-by-step path, and the FFN's roofline
+    fraction (MFMA or HBM, by its intensity).  Outputs of the two paths must
+    agree bit for bit."""
+    w = W.WORKLOADS[name]
+    t_gen = time.time()
+    inp = W.make_inputs(w, seed=0)
+    t_gen = time.time() - t_gen
+    cfg = moe.make_config(w)
+    dev = moe.upload(inp)
+    del inp
+    layer = moe.MoELayer(cfg, dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        layer.forward()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        layer.forward()
+        b.record(stream)
+    torch.cuda.synchronize()
+    layer_ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    y_layer = layer.y.clone()
+    names, fns = stage_functions(w, cfg, dev, layer, moe, W, torch)
+    for _ in range(min(warmup, 3)):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        for j, fn in enumerate(fns):
+            evs[i][j].record(stream)
+            fn()
+        evs[i][len(fns)].record(stream)
+    torch.cuda.synchronize()
+    med = {n: float(np.median([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+           for j, n in enumerate(names)}
+    bits = (lambda t: t.view(torch.int16)) if w.dtype == W.BF16 else (lambda t: t)
+    same = bool(torch.equal(bits(y_layer), bits(layer.y)))
+    n_rows, n_active, t_used = kept_counts(w, layer, W)
+    work = algorithmic(w, n_rows, n_active, t_used)
+    peak = PEAK_BF16_TFLOPS if w.dtype == W.BF16 else PEAK_F32_TFLOPS
+    st = stage_rates(w, work, med, peak, PEAK_HBM_GBS)
+    flops, fbytes = work["expert_ffn"][1], work["expert_ffn"][2]
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ffn = st["expert_ffn"]
+    out = {"T": w.T, "d_model": w.d, "num_experts": w.E, "top_k": w.k, "d_ff": w.d_ff, "d_ff_shared": w.d_ff_shared,
+           "routing": w.routing, "dtype": "bf16" if w.dtype == W.BF16 else "f32", "kept_rows": n_rows,
+           "active_experts": n_active, "tokens_with_kept_rows": t_used,
+           "layer_fwd_median_ms": round(layer_ms, 4), "tokens_per_s": round(w.T / (layer_ms / 1e3), 1),
+           "ffn_roofline": ({"bound": "mfma", "frac": ffn["mfma_frac"]} if flops / fbytes >= ridge
+                            else {"bound": "hbm", "frac": ffn["hbm_frac"]}),
+           "stages": st, "layer_fwd_matches_steps": same, "input_gen_s": round(t_gen, 1)}
+    del layer, dev
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU exchange is not built",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_layer_topkrouter_amd import moe
+    from mixture_experts_layer_topkrouter_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+    t_gen = time.time()
+    inp = W.make_inputs(w, seed=0)
+    t_gen = time.time() - t_gen
+    cfg = moe.make_config(w)
+    dev = moe.upload(inp)
+    layer = moe.MoELayer(cfg, dev)  # owns the workspace and y; its views are the intermediates
+    T, E, d = w.T, w.E, w.d
+    ec = w.routing == W.EXPERT_CHOICE
+    k = 0 if ec else w.k
+    names, fns = stage_functions(w, cfg, dev, layer, moe, W, torch)
+    stream = torch.cuda.current_stream()
+    ec = w.routing == W.EXPERT_CHOICE
+    V = layer.view
+    off, cnt = V("expert_offset"), V("expert_count")
 
     def step(ev=None):
         for i, fn in enumerate(fns):
@@ -315,15 +432,18 @@ def main():
                "train_step_tokens_per_s": round(T / ((ms_train_fwd + ms_saved) / 1e3), 1)}
 
     # Practical HBM stream rates of this device, for reading the HBM-bound
-    # stages against: a device-to-device copy (read + write) and a fill
-    # (write), each over 1 GiB, median of 5 event-timed runs.
+    # stages against: the library's own read, write and copy kernels
+    # (moe_stream_probe: 16-B accesses, 32 waves per CU), plain and
+    # non-temporal, each over 1 GiB, median of 5 event-timed runs.
     hbm_probe = None
     if args.hbm_probe:
         nbytes = 1 << 30
         src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
 
-        def rate(fn, moved):
+        def rate(kind, nt, moved):
+            fn = lambda: moe.stream_probe(kind, src, dst, nbytes, nontemporal=nt, sink=sink)
             fn()
             torch.cuda.synchronize()
             ts = []
@@ -336,22 +456,26 @@ def main():
                 ts.append(a.elapsed_time(b))
             return round(moved / (float(np.median(ts)) / 1e3) / 1e9, 1)
 
-        hbm_probe = {"copy_GB/s": rate(lambda: dst.copy_(src), 2 * nbytes),
-                     "fill_GB/s": rate(lambda: dst.fill_(1.0), nbytes), "bytes": nbytes}
+        hbm_probe = {"bytes": nbytes, "kernel": "moe_stream_probe (16-B accesses, 2048 x 256 threads)"}
+        for nt in (False, True):
+            tag = "_nt" if nt else ""
+            hbm_probe["read" + tag + "_GB/s"] = rate("read", nt, nbytes)
+            hbm_probe["write" + tag + "_GB/s"] = rate("write", nt, nbytes)
+            hbm_probe["copy" + tag + "_GB/s"] = rate("copy", nt, 2 * nbytes)
         del src, dst
 
     if args.copy_probe_mib:
-        a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        # one known-size copy through the library's copy kernel (calibrates
+        # the HBM byte counters of a profiler run)
+        a = torch.ones((args.copy_probe_mib << 20) // 2, dtype=torch.bfloat16, device="cuda")
         b = torch.empty_like(a)
         torch.cuda.synchronize()
-        b.copy_(a)
+        moe.stream_probe("copy", a, b, args.copy_probe_mib << 20)
         torch.cuda.synchronize()
         del a, b
 
-    n_rows = int(off[-1].item())
-    counts = cnt.cpu().numpy()
-    n_active = int((counts > 0).sum())
-    work = algorithmic(w, n_rows, n_active)
+    n_rows, n_active, t_used = kept_counts(w, layer, W)
+    work = algorithmic(w, n_rows, n_active, t_used)
     stages = {}
     for n in names:
         kind = work[n][0]
@@ -439,6 +563,15 @@ def main():
         y = layer.y.float().cpu().numpy().astype(np.float64)[toks]
         parity = float(np.max(np.abs(y - ref.y)) / np.max(np.abs(ref.y)))
 
+    # Every other workload, measured after the headline's timed regions: the
+    # layer at its median, the stage breakdown and the FFN's roofline.
+    others = None
+    if args.workloads:
+        others = {}
+        for name in W.WORKLOADS:
+            if name != w.name:
+                others[name] = measure_workload(name, args.steps, args.warmup, moe, W, torch)
+
     out = {
         "metric": METRIC,
         "value": round(T * args.steps / elapsed, 1),
@@ -454,7 +587,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": T, "d_model": d, "num_experts": E, "top_k": w.k, "d_ff": w.d_ff,
                    "d_ff_shared": w.d_ff_shared, "capacity_factor": w.cf, "routing": w.routing, "act": w.act,
-                   "kept_rows": n_rows, "active_experts": n_active},
+                   "kept_rows": n_rows, "active_experts": n_active, "tokens_with_kept_rows": t_used},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
@@ -468,6 +601,7 @@ def main():
         "parity_max_rel_err_sampled": parity,
         "device": dev_name,
         "input_gen_s": round(t_gen, 1),
+        "workloads": others,
     }
     print(json.dumps(out), flush=True)
 

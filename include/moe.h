@@ -110,9 +110,10 @@ int64_t moe_capacity(const moe_config *cfg);
  *   the j-th best, equal logits going to the lower expert index (IEEE
  *   equality, -0 == +0); topk_w [T,k] fp32 gets the gate weights (see
  *   moe_routing).  scores/ec_token/ec_w are ignored and may be NULL.
- * ExpertChoice: scores [T,E] fp32 = softmax over E per token; expert e keeps
- *   the ec_capacity tokens with the largest score in its column (equal scores
- *   to the lower token), stored in ascending token order in ec_token [E,C];
+ * ExpertChoice: scores [E,T] fp32, expert-major (row e holds expert e's
+ *   score of every token) = softmax over E per token; expert e keeps the
+ *   ec_capacity tokens with the largest score in its row (equal scores to
+ *   the lower token), stored in ascending token order in ec_token [E,C];
  *   ec_w [E,C] fp32 = their scores.  Requires T <= 16384.  topk_* ignored.
  * ------------------------------------------------------------------------ */
 moe_status moe_route(const moe_config *cfg, const void *x, const void *w_router,

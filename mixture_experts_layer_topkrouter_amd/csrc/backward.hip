@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void router_bwd_kernel(RouterBwdArgs a) {
   if (a.routing == 2) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (in[q]) v[q] = a.scores[static_cast<int64_t>(t) * E + l + kWave * q];
+      if (in[q]) v[q] = a.scores[static_cast<int64_t>(l + kWave * q) * a.T + t];  // expert-major
   } else {
     float m = -INFINITY;
 #pragma unroll

@@ -36,7 +36,7 @@ __device__ __forceinline__ void st16_stream(void *p, u32x4 v) {
 }
 constexpr int kTokens = kThreads / kWave;
 
-template <bool BF16, int CPL>
+template <bool BF16, int CPL, int TPW>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restrict__ y_perm_,
                                                            const int32_t *__restrict__ tok_ptr,
                                                            const int32_t *__restrict__ slot_row,
@@ -47,20 +47,26 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
                                                            int32_t stamp_val) {
   constexpr int kElems = BF16 ? 8 : 4;  // elements per 16-byte chunk
   if (stamp && blockIdx.x == 0 && threadIdx.x == 0) *stamp = stamp_val;
-  const int t = blockIdx.x * kTokens + wave_id();
-  if (t >= T) return;
+  const int tw0 = (blockIdx.x * kTokens + wave_id()) * TPW;  // this wave's first token
+  if (tw0 >= T) return;
   const int l = lane_id();
-  // slot ranges and rows come from device memory: clamp them to the buffers
-  int64_t s0 = tok_ptr ? min(max(static_cast<int64_t>(tok_ptr[t]), static_cast<int64_t>(0)), nslots)
-                       : static_cast<int64_t>(t) * k;
-  int64_t s1 = tok_ptr ? min(max(static_cast<int64_t>(tok_ptr[t + 1]), s0), nslots) : static_cast<int64_t>(t) * k + k;
-  s0 = uniform64(s0);
-  s1 = uniform64(s1);
   const size_t row_bytes = static_cast<size_t>(d) * (BF16 ? 2 : 4);
   const uint8_t *y_perm = static_cast<const uint8_t *>(y_perm_);
   const uint8_t *y_shared = static_cast<const uint8_t *>(y_shared_);
   uint8_t *y = static_cast<uint8_t *>(y_);
   const int nchunk = d / kElems;
+  // top-k with several tokens per wave: the slots of all of them (TPW * k <=
+  // 64) are loaded at once, lane i holding slot tw0 * k + i, and read back
+  // with readlane, so the wave waits on one round of index loads
+  int my_row = -1;
+  float my_w = 0.f;
+  if (!tok_ptr && TPW > 1) {
+    const int64_t s = static_cast<int64_t>(tw0) * k + l;
+    if (l < TPW * k && s < nslots) {
+      my_row = slot_row[s];
+      my_w = slot_w[s];
+    }
+  }
   auto add = [&](float (&acc)[CPL][kElems], const u32x4 (&v)[CPL], float w) {
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
@@ -84,86 +90,128 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void *__restric
       v[u] = c < nchunk ? ld16_stream(src + static_cast<size_t>(c) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  for (int c0 = 0; c0 < nchunk; c0 += CPL * kWave) {
-    float acc[CPL][kElems];
-#pragma unroll
-    for (int u = 0; u < CPL; ++u)
-#pragma unroll
-      for (int i = 0; i < kElems; ++i) acc[u][i] = 0.f;
-    for (int64_t s = s0; s < s1; s += 2) {
-      const bool two = s + 1 < s1;
-      const int ra = __builtin_amdgcn_readfirstlane(slot_row[s]);
-      const float wa = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(slot_w[s])));
-      const int rb = two ? __builtin_amdgcn_readfirstlane(slot_row[s + 1]) : -1;
-      const float wb = two ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(slot_w[s + 1]))) : 0.f;
-      const bool va = ra >= 0 && ra < rows, vb = rb >= 0 && rb < rows;
-      u32x4 xa[CPL], xb[CPL];
-      if (va) load(xa, ra, c0);
-      if (vb) load(xb, rb, c0);
-      if (va) add(acc, xa, wa);
-      if (vb) add(acc, xb, wb);
+  for (int ti = 0; ti < TPW; ++ti) {
+    const int t = tw0 + ti;
+    if (t >= T) break;
+    // slot ranges and rows come from device memory: clamp them to the buffers
+    int64_t s0, s1;
+    if (tok_ptr) {
+      s0 = min(max(static_cast<int64_t>(tok_ptr[t]), static_cast<int64_t>(0)), nslots);
+      s1 = min(max(static_cast<int64_t>(tok_ptr[t + 1]), s0), nslots);
+    } else {
+      s0 = static_cast<int64_t>(t) * k;
+      s1 = min(s0 + k, nslots);
     }
+    s0 = uniform64(s0);
+    s1 = uniform64(s1);
+    for (int c0 = 0; c0 < nchunk; c0 += CPL * kWave) {
+      float acc[CPL][kElems];
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int c = c0 + u * kWave + l;
-      if (c >= nchunk) continue;
-      const size_t off = static_cast<size_t>(t) * row_bytes + static_cast<size_t>(c) * 16;
-      if (y_shared) {
-        const u32x4 v = ld16(y_shared + off);
-        if (BF16) {
+      for (int u = 0; u < CPL; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[u][2 * i] += __uint_as_float(v[i] << 16);
-            acc[u][2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+        for (int i = 0; i < kElems; ++i) acc[u][i] = 0.f;
+      for (int64_t s = s0; s < s1; s += 2) {
+        const bool two = s + 1 < s1;
+        int ra, rb = -1;
+        float wa, wb = 0.f;
+        if (!tok_ptr && TPW > 1) {
+          const int q = static_cast<int>(s - static_cast<int64_t>(tw0) * k);  // lane holding slot s
+          ra = __builtin_amdgcn_readlane(my_row, q);
+          wa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), q));
+          if (two) {
+            rb = __builtin_amdgcn_readlane(my_row, q + 1);
+            wb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), q + 1));
           }
         } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[u][i] += __uint_as_float(v[i]);
+          ra = __builtin_amdgcn_readfirstlane(slot_row[s]);
+          wa = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(slot_w[s])));
+          if (two) {
+            rb = __builtin_amdgcn_readfirstlane(slot_row[s + 1]);
+            wb = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(slot_w[s + 1])));
+          }
         }
+        const bool va = ra >= 0 && ra < rows, vb = rb >= 0 && rb < rows;
+        u32x4 xa[CPL], xb[CPL];
+        if (va) load(xa, ra, c0);
+        if (vb) load(xb, rb, c0);
+        if (va) add(acc, xa, wa);
+        if (vb) add(acc, xb, wb);
       }
-      u32x4 o;
-      if (BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[i] = static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i])) |
-                 (static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i + 1])) << 16);
-      } else {
+      for (int u = 0; u < CPL; ++u) {
+        const int c = c0 + u * kWave + l;
+        if (c >= nchunk) continue;
+        const size_t off = static_cast<size_t>(t) * row_bytes + static_cast<size_t>(c) * 16;
+        if (y_shared) {
+          const u32x4 v = ld16(y_shared + off);
+          if (BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[u][i]);
+            for (int i = 0; i < 4; ++i) {
+              acc[u][2 * i] += __uint_as_float(v[i] << 16);
+              acc[u][2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[u][i] += __uint_as_float(v[i]);
+          }
+        }
+        u32x4 o;
+        if (BF16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o[i] = static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i])) |
+                   (static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i + 1])) << 16);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[u][i]);
+        }
+        st16_stream(y + off, o);
       }
-      st16_stream(y + off, o);
     }
   }
 }
 
 // Rows of up to 8 chunks per lane take two passes of 4 (84 instead of 160
 // VGPRs: every wave of a 4096-token batch is resident at once, measured 12 %
-// faster for d = 4096 bf16); longer rows take passes of 8.
+// faster for d = 4096 bf16); longer rows take passes of 8.  Top-k rows of at
+// most 2 KB take 4 tokens per wave and rows of at most 4 KB 2, their slot
+// indices loaded in one round: fewer waves, each waiting on one index load.
 template <bool BF16>
-void launch(const CombineArgs &a, int blocks, hipStream_t st) {
+void launch(const CombineArgs &a, hipStream_t st) {
   const int nchunk = a.d / (BF16 ? 8 : 4);
   const int per_lane = (nchunk + kWave - 1) / kWave;
-  if (per_lane <= 1)
-    combine_kernel<BF16, 1><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots, a.stamp, a.stamp_val);
-  else if (per_lane <= 2)
-    combine_kernel<BF16, 2><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots, a.stamp, a.stamp_val);
-  else if (per_lane <= 8)
-    combine_kernel<BF16, 4><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots, a.stamp, a.stamp_val);
-  else
-    combine_kernel<BF16, 8><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w, a.y_shared,
-                                                         a.y, a.T, a.d, a.k, a.rows, a.nslots, a.stamp, a.stamp_val);
+  int tpw = 1;
+  if (!a.tok_ptr && per_lane <= 2) tpw = 4;
+  else if (!a.tok_ptr && per_lane <= 4) tpw = 2;
+  while (tpw > 1 && tpw * a.k > kWave) tpw >>= 1;
+  const int blocks = (a.T + kTokens * tpw - 1) / (kTokens * tpw);
+#define MOE_COMBINE(CPL, TPW)                                                                              \
+  combine_kernel<BF16, CPL, TPW><<<blocks, kThreads, 0, st>>>(a.y_perm, a.tok_ptr, a.slot_row, a.slot_w,   \
+                                                              a.y_shared, a.y, a.T, a.d, a.k, a.rows,      \
+                                                              a.nslots, a.stamp, a.stamp_val)
+  if (per_lane <= 1) {
+    if (tpw == 4) MOE_COMBINE(1, 4);
+    else if (tpw == 2) MOE_COMBINE(1, 2);
+    else MOE_COMBINE(1, 1);
+  } else if (per_lane <= 2) {
+    if (tpw == 4) MOE_COMBINE(2, 4);
+    else if (tpw == 2) MOE_COMBINE(2, 2);
+    else MOE_COMBINE(2, 1);
+  } else if (per_lane <= 8) {
+    if (tpw == 2) MOE_COMBINE(4, 2);
+    else MOE_COMBINE(4, 1);
+  } else {
+    MOE_COMBINE(8, 1);
+  }
+#undef MOE_COMBINE
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
-  const int blocks = (a.T + kTokens - 1) / kTokens;
-  if (a.dtype == 1) launch<true>(a, blocks, st);
-  else launch<false>(a, blocks, st);
+  if (a.dtype == 1) launch<true>(a, st);
+  else launch<false>(a, st);
   return hipGetLastError();
 }
 

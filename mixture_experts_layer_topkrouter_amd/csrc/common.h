@@ -102,6 +102,42 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
   return r;
 }
 
+// the direct-to-LDS loads name M0, which the compiler reserves (it uses M0
+// nowhere else in these kernels)
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds_addr + 16 * lane.  Written as inline asm so the compiler's wait-count
+// pass does not see it: that pass cannot always tell which ring slot an LDS
+// read touches and would then drain every load in flight before the read.
+// The kernel orders these loads itself (explicit vmcnt waits + barriers).
+// The instruction has no register result; M0 carries the LDS address and
+// needs one wait state after it is written.  The global address is a
+// wave-uniform base in SGPRs plus a 32-bit per-lane byte offset, so advancing
+// a stage is scalar arithmetic and each lane keeps one VGPR per load stream.
+__device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  // the LDS address is wave-uniform; readfirstlane puts it in an SGPR for M0
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0v)
+               : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)p));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+}  // namespace
+
 // 16-byte global load/store helpers.
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }

@@ -127,6 +127,7 @@ template <int CPL>
 __device__ __forceinline__ void copy_row(const uint8_t *__restrict__ x, size_t row_bytes, int t, int k, int row,
                                          uint8_t *__restrict__ x_perm, int c_begin = 0) {
   const int l = lane_id();
+  if (__ballot(row >= 0) == 0) return;  // every slot dropped: the row is not read
   const int nchunk = static_cast<int>(row_bytes / 16);
   const uint8_t *src = x + static_cast<size_t>(t) * row_bytes;
   for (int c0 = c_begin; c0 < nchunk; c0 += CPL * kWave) {
@@ -263,15 +264,19 @@ __global__ __launch_bounds__(kFusedThreads) void count_scatter_kernel(
   const int t = blockIdx.x * kFusedTokens + w;
   const bool has_t = t < T;
   const int nchunk = static_cast<int>(row_bytes / 16);
+  // dropless: every token's row is written, so it is requested before the
+  // counting; with a capacity the row is read only if a slot is kept
+  const bool pre = cap < 0;
   u32x4 v[CPL];
-  {
+  auto load_first = [&]() {
     const uint8_t *src = x + static_cast<size_t>(has_t ? t : 0) * row_bytes;
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
       const int c = u * kWave + l;
       v[u] = (has_t && c < nchunk) ? ld16_stream(src + static_cast<size_t>(c) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
-  }
+  };
+  if (pre) load_first();
   for (int e = tid; e < E; e += kFusedThreads) {
     base[e] = 0;
     total[e] = 0;
@@ -338,6 +343,8 @@ __global__ __launch_bounds__(kFusedThreads) void count_scatter_kernel(
     }
     slot_row[static_cast<int64_t>(t) * k + l] = row;
   }
+  if (__ballot(row >= 0) == 0) return;  // every slot dropped: the row is not read
+  if (!pre) load_first();
   for (int j = 0; j < k; ++j) {
     const int rj = __shfl(row, j, kWave);
     if (rj < 0) continue;
@@ -353,18 +360,45 @@ __global__ __launch_bounds__(kFusedThreads) void count_scatter_kernel(
 
 // ---------------------------------------------------------------- ExpertChoice
 
-// Row copy for ExpertChoice: row r = e*C + i holds token ec_token[r].
-__global__ __launch_bounds__(kThreads) void ec_rows_kernel(const uint8_t *__restrict__ x, size_t row_bytes,
-                                                           const int32_t *__restrict__ ec_token, int64_t rows,
-                                                           int E, int C, uint8_t *__restrict__ x_perm,
-                                                           int32_t *__restrict__ row_token,
-                                                           int32_t *__restrict__ expert_count,
-                                                           int32_t *__restrict__ expert_load,
-                                                           int32_t *__restrict__ expert_offset) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * kScatterTokens + wave_id();
-  const int l = lane_id();
+// ExpertChoice permutation in one launch, token-major.  Row e*C + i holds
+// token ec_token[e, i]; each expert's list ascends, so a workgroup that owns
+// tokens [t0, t0 + 16) finds, per expert, the run of list entries that fall in
+// its range by two binary searches (lower bounds of t0 and t0 + 16), and the
+// number of selections before t0 (the CSR base of its first token) is the sum
+// of the first lower bounds over the experts.  A per-token bit mask of the
+// experts holding it (LDS integer ORs, order-independent) gives each entry
+// its place in its token's list (ascending expert); then every token's row is
+// read once and written to each of its rows.
+constexpr int kEcPermTokens = kFusedTokens;  // 16 tokens, one wave each for the copy
+constexpr int kEcMaskWords = kMaxExperts / 32;
+
+__device__ __forceinline__ int ec_lower_bound(const int32_t *__restrict__ list, int C, int t) {
+  int lo = 0, hi = C;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] < t) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kFusedThreads) void ec_permute_kernel(
+    const uint8_t *__restrict__ x, size_t row_bytes, const int32_t *__restrict__ ec_token,
+    const float *__restrict__ ec_w, int T, int E, int C, uint8_t *__restrict__ x_perm,
+    int32_t *__restrict__ row_token, int32_t *__restrict__ slot_row, float *__restrict__ slot_w,
+    int32_t *__restrict__ tok_ptr, int32_t *__restrict__ expert_count, int32_t *__restrict__ expert_load,
+    int32_t *__restrict__ expert_offset) {
+  __shared__ int p0[kMaxExperts], p1[kMaxExperts];
+  __shared__ uint32_t mask[kEcPermTokens][kEcMaskWords];
+  __shared__ int tok_off[kEcPermTokens + 1];
+  __shared__ int rows_of[kEcPermTokens][kMaxExperts];
+  __shared__ int tmp[kFusedThreads / kWave + 1];
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const int t0 = blockIdx.x * kEcPermTokens;
+  const int t1 = min(T, t0 + kEcPermTokens);
   if (blockIdx.x == 0) {
-    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+    for (int e = tid; e <= E; e += kFusedThreads) {
       if (e < E) {
         expert_count[e] = C;
         expert_load[e] = C;
@@ -372,85 +406,91 @@ __global__ __launch_bounds__(kThreads) void ec_rows_kernel(const uint8_t *__rest
       expert_offset[e] = e * C;
     }
   }
-  if (r >= rows) return;
-  const int t = ec_token[r];
-  if (l == 0) row_token[r] = t;
+  // the first pass of this wave's token row is requested before the searches
+  const int t = t0 + w;
+  const bool has_t = t < T;
   const int nchunk = static_cast<int>(row_bytes / 16);
-  const uint8_t *src = x + static_cast<size_t>(t) * row_bytes;
-  uint8_t *dst = x_perm + static_cast<size_t>(r) * row_bytes;
-  for (int c = l; c < nchunk; c += kWave) st16(dst + static_cast<size_t>(c) * 16, ld16(src + static_cast<size_t>(c) * 16));
-}
-
-// Position of token t in expert e's ascending list, or -1.
-__device__ __forceinline__ int ec_find(const int32_t *__restrict__ list, int C, int t) {
-  int lo = 0, hi = C;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (list[mid] < t) lo = mid + 1;
-    else hi = mid;
-  }
-  return (lo < C && list[lo] == t) ? lo : -1;
-}
-
-// Per token: how many experts hold it (written to tok_ptr[t+1]).
-__global__ __launch_bounds__(kThreads) void ec_count_kernel(const int32_t *__restrict__ ec_token, int T, int E,
-                                                            int C, int32_t *__restrict__ tok_ptr) {
-  const int t = blockIdx.x * kScatterTokens + wave_id();
-  if (t >= T) return;
-  const int l = lane_id();
-  int n = 0;
-  for (int e = l; e < E; e += kWave) n += ec_find(ec_token + static_cast<int64_t>(e) * C, C, t) >= 0;
+  u32x4 v[CPL];
+  {
+    const uint8_t *src = x + static_cast<size_t>(has_t ? t : 0) * row_bytes;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, kWave);
-  if (l == 0) tok_ptr[t + 1] = n;
-  if (t == 0 && l == 0) tok_ptr[0] = 0;
-}
-
-constexpr int kPtrThreads = 1024;
-
-// In-place inclusive scan of tok_ptr[1..T] (single workgroup).  The counts
-// pass through LDS so that global loads and stores are coalesced; each
-// thread scans a contiguous run there.
-__global__ __launch_bounds__(kPtrThreads) void ec_ptr_scan_kernel(int32_t *__restrict__ tok_ptr, int T) {
-  __shared__ int tmp[kPtrThreads / kWave + 1];
-  __shared__ int vals[kEcMaxTokens];
-  for (int i = threadIdx.x; i < T; i += kPtrThreads) vals[i] = tok_ptr[i + 1];
+    for (int u = 0; u < CPL; ++u) {
+      const int c = u * kWave + l;
+      v[u] = (has_t && c < nchunk) ? ld16_stream(src + static_cast<size_t>(c) * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  for (int i = tid; i < kEcPermTokens * kEcMaskWords; i += kFusedThreads) (&mask[0][0])[i] = 0u;
+  int before = 0;  // selections of expert `tid` before t0
+  if (tid < E) {
+    const int32_t *list = ec_token + static_cast<int64_t>(tid) * C;
+    p0[tid] = before = ec_lower_bound(list, C, t0);
+    p1[tid] = ec_lower_bound(list, C, t1);
+  }
+  int base_total;
+  block_excl_scan(before, tmp, &base_total);  // base_total = selections before t0
+  // (block_excl_scan ends with a barrier: p0, p1 and the cleared masks are visible)
+  for (int e = tid; e < E; e += kFusedThreads)
+    for (int p = p0[e]; p < p1[e]; ++p) {
+      const int tl = ec_token[static_cast<int64_t>(e) * C + p] - t0;
+      if (tl >= 0 && tl < kEcPermTokens) atomicOr(&mask[tl][e >> 5], 1u << (e & 31));
+    }
   __syncthreads();
-  const int per = (T + kPtrThreads - 1) / kPtrThreads;
-  const int b0 = min(T, static_cast<int>(threadIdx.x) * per), b1 = min(T, b0 + per);
-  int s = 0;
-  for (int i = b0; i < b1; ++i) s += vals[i];
-  int tot;
-  int run = block_excl_scan(s, tmp, &tot);
-  for (int i = b0; i < b1; ++i) {
-    run += vals[i];
-    vals[i] = run;
+  if (w == 0) {  // per-token counts, their scan, the CSR pointers
+    int cnt = 0;
+    if (l < kEcPermTokens)
+      for (int q = 0; q < kEcMaskWords; ++q) cnt += __popc(mask[l][q]);
+    const int incl = wave_incl_scan(cnt);
+    if (l < kEcPermTokens) {
+      tok_off[l] = base_total + incl - cnt;
+      if (t0 + l < T) tok_ptr[t0 + l] = base_total + incl - cnt;
+      if (t0 + l == T - 1) tok_ptr[T] = base_total + incl;
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < T; i += kPtrThreads) tok_ptr[i + 1] = vals[i];
-}
-
-// Per token: its rows and weights in ascending expert order.
-__global__ __launch_bounds__(kThreads) void ec_fill_kernel(const int32_t *__restrict__ ec_token,
-                                                           const float *__restrict__ ec_w, int T, int E, int C,
-                                                           const int32_t *__restrict__ tok_ptr,
-                                                           int32_t *__restrict__ slot_row,
-                                                           float *__restrict__ slot_w) {
-  const int t = blockIdx.x * kScatterTokens + wave_id();
-  if (t >= T) return;
-  const int l = lane_id();
-  int base = tok_ptr[t];
-  for (int e0 = 0; e0 < E; e0 += kWave) {
-    const int e = e0 + l;
-    const int pos = (e < E) ? ec_find(ec_token + static_cast<int64_t>(e) * C, C, t) : -1;
-    const uint64_t hit = __ballot(pos >= 0);
-    if (pos >= 0) {
-      const int s = base + __popcll(hit & lanemask_lt());
-      const int64_t r = static_cast<int64_t>(e) * C + pos;
-      slot_row[s] = static_cast<int32_t>(r);
-      slot_w[s] = ec_w[r];
+  for (int e = tid; e < E; e += kFusedThreads)
+    for (int p = p0[e]; p < p1[e]; ++p) {
+      const int64_t r = static_cast<int64_t>(e) * C + p;
+      const int tl = ec_token[r] - t0;
+      if (tl < 0 || tl >= kEcPermTokens) continue;  // only an unsorted list gets here
+      int rank = 0;  // experts below e that hold this token
+      for (int q = 0; q < (e >> 5); ++q) rank += __popc(mask[tl][q]);
+      rank += __popc(mask[tl][e >> 5] & ((1u << (e & 31)) - 1u));
+      const int slot = tok_off[tl] + rank;
+      slot_row[slot] = static_cast<int32_t>(r);
+      slot_w[slot] = ec_w[r];
+      row_token[r] = t0 + tl;
+      rows_of[tl][rank] = static_cast<int32_t>(r);
     }
-    base += __popcll(hit);
+  __syncthreads();
+  if (!has_t) return;
+  int cnt = 0;
+  for (int q = 0; q < kEcMaskWords; ++q) cnt += __popc(mask[w][q]);
+  for (int j = 0; j < cnt; ++j) {
+    uint8_t *dst = x_perm + static_cast<size_t>(rows_of[w][j]) * row_bytes;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = u * kWave + l;
+      if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
+    }
+  }
+  if (nchunk > CPL * kWave) {
+    // rows longer than one pass: the rest, read once per pass
+    const uint8_t *src = x + static_cast<size_t>(t) * row_bytes;
+    for (int c0 = CPL * kWave; c0 < nchunk; c0 += CPL * kWave) {
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int c = c0 + u * kWave + l;
+        if (c < nchunk) v[u] = ld16_stream(src + static_cast<size_t>(c) * 16);
+      }
+      for (int j = 0; j < cnt; ++j) {
+        uint8_t *dst = x_perm + static_cast<size_t>(rows_of[w][j]) * row_bytes;
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+          const int c = c0 + u * kWave + l;
+          if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
+        }
+      }
+    }
   }
 }
 
@@ -515,16 +555,18 @@ hipError_t launch_permute_topk(const PermuteArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_permute_ec(const PermuteEcArgs &a, hipStream_t st) {
-  const int64_t rows = static_cast<int64_t>(a.E) * a.C;
-  const int rblocks = static_cast<int>((rows + kScatterTokens - 1) / kScatterTokens);
-  ec_rows_kernel<<<rblocks > 0 ? rblocks : 1, kThreads, 0, st>>>(
-      static_cast<const uint8_t *>(a.x), a.row_bytes, a.ec_token, rows, a.E, a.C,
-      static_cast<uint8_t *>(a.x_perm), a.row_token, a.expert_count, a.expert_load, a.expert_offset);
-  const int tblocks = (a.T + kScatterTokens - 1) / kScatterTokens;
-  ec_count_kernel<<<tblocks, kThreads, 0, st>>>(a.ec_token, a.T, a.E, a.C, a.tok_ptr);
-  ec_ptr_scan_kernel<<<1, kPtrThreads, 0, st>>>(a.tok_ptr, a.T);
-  ec_fill_kernel<<<tblocks, kThreads, 0, st>>>(a.ec_token, a.ec_w, a.T, a.E, a.C, a.tok_ptr, a.slot_row,
-                                              a.slot_w);
+  const int blocks = (a.T + kEcPermTokens - 1) / kEcPermTokens;
+  const int per_lane = static_cast<int>((a.row_bytes / 16 + kWave - 1) / kWave);  // 16-B chunks per lane
+  const uint8_t *x = static_cast<const uint8_t *>(a.x);
+  uint8_t *xp = static_cast<uint8_t *>(a.x_perm);
+#define MOE_EC_PERMUTE(CPL)                                                                                     \
+  ec_permute_kernel<CPL><<<blocks > 0 ? blocks : 1, kFusedThreads, 0, st>>>(                                   \
+      x, a.row_bytes, a.ec_token, a.ec_w, a.T, a.E, a.C, xp, a.row_token, a.slot_row, a.slot_w, a.tok_ptr,     \
+      a.expert_count, a.expert_load, a.expert_offset)
+  if (per_lane <= 2) MOE_EC_PERMUTE(2);
+  else if (per_lane <= 4) MOE_EC_PERMUTE(4);
+  else MOE_EC_PERMUTE(8);
+#undef MOE_EC_PERMUTE
   return hipGetLastError();
 }
 

@@ -8,25 +8,24 @@
 // ExpertChoiceRouter lets each expert choose its tokens by routing score.
 //
 // gfx950 design:
-// * logits: bf16 MFMA 16x16x32 with fp32 accumulation.  A block owns 16*MT
-//   tokens and all E (padded to 16*NT) experts; its eight waves split the
-//   contraction over d by interleaved 32-wide steps, each with several steps
-//   of loads in flight, and their partial tiles are summed in LDS in a fixed
-//   wave order, so results are deterministic.
-//   The router weight is tiny and stays in L2; x is streamed once from HBM.
-// * the gate runs on the logits tile while it is still in LDS: one wave per
-//   token, lane l holds experts l, l+64, l+128, l+192; each of the k picks is a
-//   wave arg-max under the order (value desc, index asc) with IEEE comparisons
-//   (so -0 == +0), a strict total order.  The wave reductions (arg-max, max,
-//   sum) run on DPP lane shifts inside rows of 16 lanes plus two row
-//   broadcasts, a few cycles per step instead of an LDS-crossbar round trip
-//   per butterfly level; lane 63 ends with the result, which readlane makes
-//   wave-uniform.  The order of the steps is fixed, so sums are
-//   deterministic.
-// * ExpertChoice: one workgroup per expert keeps its score column in LDS,
-//   finds the C-th largest score by an 8-bit radix select (scores are >= 0,
-//   so their bit patterns order like the values), then compacts the chosen
-//   tokens in ascending order with block prefix sums.
+// * logits: bf16 MFMA 16x16x32 with fp32 accumulation.  A workgroup of four
+//   waves owns 16*MT tokens and all E experts (padded to 16*NT); K advances in
+//   64-wide stages that direct-to-LDS loads copy into a deep LDS ring as whole
+//   128-B lines, so x streams from HBM once in full lines with tens of KB in
+//   flight per CU, and the small router weight comes from L2 the same way.
+//   The output tiles are dealt to the waves (when there are fewer than four,
+//   the waves split the stages as well and add their partials in a fixed
+//   order), so results are deterministic.
+// * the gate runs on the logits tile while it is still in LDS, 16 lanes per
+//   token (a DPP row), so a wave gates four tokens at once: each of the k
+//   picks is a row arg-max under the order (value desc, index asc) with IEEE
+//   comparisons (so -0 == +0), a strict total order, taken by four row
+//   rotations; softmax sums are added in a fixed order and broadcast.
+// * ExpertChoice: the scores are stored expert-major, so one workgroup per
+//   expert reads its contiguous score row into LDS and finds the C-th largest
+//   score by a radix select (scores are >= 0, so their bit patterns order
+//   like the values) that skips the bits all keys share, then compacts the
+//   chosen tokens in ascending order with block prefix sums.
 #include "common.h"
 #include "kernels.h"
 
@@ -54,45 +53,47 @@ __device__ __forceinline__ bool ranks_before(float vb, int ib, float va, int ia)
   return vb > va || (vb == va && ib < ia);
 }
 
-// Wave arg-max of (v, i) under ranks_before; returns it wave-uniform.  Row
-// shifts 1, 2, 4, 8 leave each row's best in its lane 15, the two row
-// broadcasts carry rows 0 and 2 into rows 1 and 3, then row 1 into 2 and 3.
-__device__ __forceinline__ void wave_argmax(float &v, int &i) {
-#define MOE_ARGMAX_STEP(C, R)                   \
-  {                                             \
-    const float ov = dpp_f<C, R>(v);            \
-    const int oi = dpp_i<C, R>(i);              \
-    if (ranks_before(ov, oi, v, i)) {           \
-      v = ov;                                   \
-      i = oi;                                   \
-    }                                           \
+// Gate over a tile of logits in LDS (row r = token t0 + r, row stride ld
+// floats), 16 lanes per token: lane j of a DPP row (16 lanes) holds experts
+// j, j+16, ..., so a wave gates four tokens at once.  Each of the k picks is
+// an arg-max under (value desc, index asc) with IEEE comparisons (so
+// -0 == +0), a strict total order: every lane offers its best untaken
+// candidate and four row rotations (8, 4, 2, 1) leave the row's best in every
+// lane of the row.  Lane j of the row keeps pick j.  Sums (softmax
+// denominators) are taken in a fixed order (row shifts into lane 15) and
+// broadcast from lane 15, so every slot of a token divides by the same sum.
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+__device__ __forceinline__ void row_argmax(float &v, int &i) {
+#define MOE_ROW_ARGMAX_STEP(C)            \
+  {                                       \
+    const float ov = dpp_f<C, 0xf>(v);    \
+    const int oi = dpp_i<C, 0xf>(i);      \
+    if (ranks_before(ov, oi, v, i)) {     \
+      v = ov;                             \
+      i = oi;                             \
+    }                                     \
   }
-  MOE_ARGMAX_STEP(kRowShr1, 0xf)
-  MOE_ARGMAX_STEP(kRowShr2, 0xf)
-  MOE_ARGMAX_STEP(kRowShr4, 0xf)
-  MOE_ARGMAX_STEP(kRowShr8, 0xf)
-  MOE_ARGMAX_STEP(kRowBcast15, 0xa)
-  MOE_ARGMAX_STEP(kRowBcast31, 0xc)
-#undef MOE_ARGMAX_STEP
-  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  i = __builtin_amdgcn_readlane(i, 63);
+  MOE_ROW_ARGMAX_STEP(kRowRor8)
+  MOE_ROW_ARGMAX_STEP(kRowRor4)
+  MOE_ROW_ARGMAX_STEP(kRowRor2)
+  MOE_ROW_ARGMAX_STEP(kRowRor1)
+#undef MOE_ROW_ARGMAX_STEP
 }
 
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, dpp_f<kRowShr1, 0xf>(v));
-  v = fmaxf(v, dpp_f<kRowShr2, 0xf>(v));
-  v = fmaxf(v, dpp_f<kRowShr4, 0xf>(v));
-  v = fmaxf(v, dpp_f<kRowShr8, 0xf>(v));
-  v = fmaxf(v, dpp_f<kRowBcast15, 0xa>(v));
-  v = fmaxf(v, dpp_f<kRowBcast31, 0xc>(v));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp_f<kRowRor8, 0xf>(v));
+  v = fmaxf(v, dpp_f<kRowRor4, 0xf>(v));
+  v = fmaxf(v, dpp_f<kRowRor2, 0xf>(v));
+  v = fmaxf(v, dpp_f<kRowRor1, 0xf>(v));
+  return v;
 }
 
-// Wave sum in a fixed order.  A shifted-in value is added only where the
-// source lane exists (the DPP keeps the lane's own value elsewhere, which
-// must not be added twice).
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  const int l = lane_id() & 15, row = lane_id() >> 4;
+// Sum over the 16 lanes of each row in a fixed order (row shifts 1, 2, 4, 8
+// into lane 15), then lane 15's value to every lane of its row (ds_swizzle,
+// bit mode: lane = (lane & 0x10) | 0xf inside each half-wave).
+__device__ __forceinline__ float row_sum(float v) {
+  const int l = lane_id() & 15;
   float o;
   o = dpp_f<kRowShr1, 0xf>(v);
   if (l >= 1) v += o;
@@ -102,69 +103,68 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   if (l >= 4) v += o;
   o = dpp_f<kRowShr8, 0xf>(v);
   if (l >= 8) v += o;
-  o = dpp_f<kRowBcast15, 0xa>(v);
-  if (row & 1) v += o;
-  o = dpp_f<kRowBcast31, 0xc>(v);
-  if (row >= 2) v += o;
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  constexpr int kBcast15 = (0x10 << 0) | (0x0f << 5);  // and_mask 0x10, or_mask 0x0f, xor_mask 0
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kBcast15));
 }
 
-// Gate for `rows` tokens whose logits sit in LDS (row stride ld).
-__device__ void gate_rows(const float *tile, int ld, int rows, int t0, int T, int E, int k,
-                          int routing, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
-                          float *__restrict__ scores) {
-  const int l = lane_id();
-  const int nw = blockDim.x / kWave;
-  for (int r = wave_id(); r < rows; r += nw) {
+// NT: values per lane (experts padded to 16 * NT).  rows tokens of the tile.
+template <int NT>
+__device__ __forceinline__ void gate_tile(float *tile, int ld, int rows, int t0, int T, int E, int k, int routing,
+                          int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ scores) {
+  const int j = lane_id() & 15;
+  const int rw = wave_id() * 4 + (lane_id() >> 4);  // row of this lane group
+  const int groups = (blockDim.x / kWave) * 4;
+  for (int r = rw; r < rows; r += groups) {
     const int t = t0 + r;
-    if (t >= T) break;
-    const float *row = tile + r * ld;
-    float v[4];
-    bool valid[4], taken[4];
+    if (t >= T) break;  // rows ascend with r: the rest of this lane group's rows are past T too
+    float *row = tile + r * ld;
+    float v[NT];
+    uint32_t taken = 0;  // bit q: expert j + 16q is taken (or past E)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = l + kWave * q;
-      valid[q] = e < E;
-      v[q] = valid[q] ? row[e] : 0.f;
-      taken[q] = !valid[q];
+    for (int q = 0; q < NT; ++q) {
+      const int e = j + 16 * q;
+      v[q] = e < E ? row[e] : 0.f;
+      if (e >= E) taken |= 1u << q;
     }
     if (routing == 2) {  // ExpertChoice scores: softmax over E
       float m = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (valid[q]) m = fmaxf(m, v[q]);
-      m = wave_max_dpp(m);
+      for (int q = 0; q < NT; ++q)
+        if (!(taken >> q & 1u)) m = fmaxf(m, v[q]);
+      m = row_max(m);
       float s = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (valid[q]) s += expf(v[q] - m);
-      s = wave_sum_dpp(s);
+      for (int q = 0; q < NT; ++q) {
+        v[q] = (taken >> q & 1u) ? 0.f : expf(v[q] - m);
+        s += v[q];
+      }
+      s = row_sum(s);
+      // into the tile in place of the logits; store_scores_t writes them out
+      // expert-major
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (valid[q]) scores[(int64_t)t * E + l + kWave * q] = expf(v[q] - m) / s;
+      for (int q = 0; q < NT; ++q)
+        if (!(taken >> q & 1u)) row[j + 16 * q] = v[q] / s;
       continue;
     }
     int my_idx = -1;
     float my_val = 0.f, top = 0.f;
-    for (int j = 0; j < k; ++j) {
-      // this lane's best untaken candidate; lanes without one offer
+    for (int p = 0; p < k; ++p) {
+      // this lane's best untaken candidate; a lane without one offers
       // (-inf, INT_MAX), which every real candidate ranks before
       float bv = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < NT; ++q) {
         // q ascending is index ascending: a strict '>' keeps the lower index on ties
-        if (!taken[q] && (bi == 0x7fffffff || v[q] > bv)) {
+        if (!(taken >> q & 1u) && (bi == 0x7fffffff || v[q] > bv)) {
           bv = v[q];
-          bi = l + kWave * q;
+          bi = j + 16 * q;
         }
       }
-      wave_argmax(bv, bi);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (bi == l + kWave * q) taken[q] = true;
-      if (j == 0) top = bv;
-      if (l == j) {
+      row_argmax(bv, bi);
+      if ((bi & 15) == j && bi < 16 * NT) taken |= 1u << (bi >> 4);
+      if (p == 0) top = bv;
+      if (j == p) {
         my_idx = bi;
         my_val = bv;
       }
@@ -173,142 +173,229 @@ __device__ void gate_rows(const float *tile, int ld, int rows, int t0, int T, in
     if (routing == 0) {  // softmax over all E, read at the chosen experts
       float s = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (valid[q]) s += expf(v[q] - top);
-      s = wave_sum_dpp(s);
+      for (int q = 0; q < NT; ++q)
+        if (j + 16 * q < E) s += expf(v[q] - top);
+      s = row_sum(s);
       w = expf(my_val - top) / s;
-    } else {  // softmax over the k chosen logits, added in slot order
-      const float ex = (l < k) ? expf(my_val - top) : 0.f;
-      float s = 0.f;
-      for (int jj = 0; jj < k; ++jj) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), jj));
-      w = ex / s;
+    } else {  // softmax over the k chosen logits
+      const float ex = (j < k) ? expf(my_val - top) : 0.f;
+      w = ex / row_sum(ex);
     }
-    if (l < k) {
-      topk_idx[(int64_t)t * k + l] = my_idx;
-      topk_w[(int64_t)t * k + l] = w;
+    if (j < k) {
+      topk_idx[(int64_t)t * k + j] = my_idx;
+      topk_w[(int64_t)t * k + j] = w;
     }
+  }
+}
+
+// ExpertChoice scores of a tile (rows tokens, in LDS after gate_tile) to
+// scores[e, t] (expert-major): consecutive threads take consecutive tokens of
+// one expert, so each expert's run of the tile is one contiguous store.
+template <int ROWS>
+__device__ __forceinline__ void store_scores_t(const float *tile, int ld, int t0, int T, int E,
+                                               float *__restrict__ scores) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < ROWS * E; i += blockDim.x) {
+    const int e = i / ROWS, r = i - (i / ROWS) * ROWS;
+    if (t0 + r < T) scores[(int64_t)e * T + t0 + r] = tile[r * ld + e];
   }
 }
 
 // Adds the bias, writes the logits and leaves them in LDS for the gate.
-__device__ void finish_logits(float *tile, int ld, int rows, int t0, int T, int E, const float *bias,
-                              int64_t bias_stride, float *logits) {
-  for (int i = threadIdx.x; i < rows * E; i += blockDim.x) {
-    const int r = i / E, e = i - (i / E) * E;
-    const int t = t0 + r;
-    if (t >= T) continue;
-    float v = tile[r * ld + e];
-    if (bias) v += bias[(int64_t)t * bias_stride + e];
-    tile[r * ld + e] = v;
-    logits[(int64_t)t * E + e] = v;
+// Thread i takes expert e = i % E of rows i / E, i / E + blockDim / E, ...
+// when E divides the block (one bias load per row step, no division in the
+// loop); otherwise a plain flat loop.
+__device__ __forceinline__ void finish_logits(float *tile, int ld, int rows, int t0, int T, int E, const float *bias,
+                                              int64_t bias_stride, float *logits) {
+  const int nthr = blockDim.x;
+  if (nthr % E == 0) {
+    const int e = threadIdx.x % E, rstep = nthr / E;
+    const float b0 = (bias && bias_stride == 0) ? bias[e] : 0.f;
+    for (int r = threadIdx.x / E; r < rows; r += rstep) {
+      const int t = t0 + r;
+      if (t >= T) break;
+      float v = tile[r * ld + e];
+      if (bias) v += bias_stride == 0 ? b0 : bias[(int64_t)t * bias_stride + e];
+      tile[r * ld + e] = v;
+      logits[(int64_t)t * E + e] = v;
+    }
+  } else {
+    for (int i = threadIdx.x; i < rows * E; i += nthr) {
+      const int r = i / E, e = i - (i / E) * E;
+      const int t = t0 + r;
+      if (t >= T) continue;
+      float v = tile[r * ld + e];
+      if (bias) v += bias[(int64_t)t * bias_stride + e];
+      tile[r * ld + e] = v;
+      logits[(int64_t)t * E + e] = v;
+    }
   }
   __syncthreads();
 }
 
-// Logits: 8 waves per block split the contraction over d by interleaved
-// 32-wide steps (wave w takes steps w, w+8, ...).  Each wave keeps D steps of
-// operand fragments in flight in a register ring (load step j+D, then
-// multiply step j), so a CU holds tens of KB of x loads in flight: enough to
-// stream x at HBM speed instead of waiting on one step at a time.
-constexpr int kRouteBf16Threads = 512;
-
-template <int MT, int NT>
-__global__ __launch_bounds__(kRouteBf16Threads) void route_bf16_kernel(
+// ---------------------------------------------------------------------------
+// bf16 logits.  A workgroup of NW waves owns BT = 16*MT tokens and all E
+// experts, padded to EP = 16*NT rows of W_r (padding rows repeat row E-1;
+// their logits are never read).  K advances in stages of KB bytes per row
+// (64 or 128 elements): a stage holds the BT x rows and the EP W_r rows,
+// copied into an LDS ring of NS stages by direct-to-LDS loads
+// (global_load_lds_dwordx4).  One load instruction fills 64/(KB/16) rows
+// with whole 128-B lines, so the token rows stream from HBM in full lines;
+// the stage for step s + NS - 1 is requested as step s starts, which keeps
+// NS - 1 stages in flight per CU.  The 16-B chunk c of row r is stored at
+// c ^ ((r >> 1) & 7) (128-B rows) or c ^ (r & 15) (256-B rows), so the 16
+// rows a ds_read_b128 serves together fall on 16 distinct 16-B bank slots.
+// MFMA 16x16x32 (bf16, fp32 accumulation): the MT x NT output tiles are
+// dealt to the waves; when there are fewer tiles than waves, the waves also
+// split the K stages (stage s to wave group s % KS) and their partial tiles
+// are added in a fixed order.  The logits tile then goes through the bias,
+// the global store and the gate while it sits in LDS.
+template <int MT, int NT, int NS, int NW, int KB>
+__global__ __launch_bounds__(NW * kWave) void route_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, const float *__restrict__ bias,
     int64_t bias_stride, int T, int d, int E, int k, int routing, float *__restrict__ logits,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ scores) {
+  static_assert(KB == 128 || KB == 256, "128- or 256-byte rows");
+  constexpr int KC = KB / 2;                        // K elements per stage
+  constexpr int CPR = KB / 16;                      // 16-B chunks per row
+  constexpr int RPI = kWave / CPR;                  // rows per load instruction
   constexpr int BT = 16 * MT, EP = 16 * NT;
-  constexpr int NW = kRouteBf16Threads / kWave;
-  // logits tile row pitch: 4 rows apart (the row groups of a 16x16 MFMA
-  // result) land 16 banks apart, so the tile write is conflict-free
-  constexpr int LD = EP + 4;
-  constexpr int RED = (NW / 2) * MT * NT * kWave;  // float4s of the reduction buffer
-  static_assert(BT * LD <= RED * 4 || RED == 0, "logits tile fits in the reduction buffer");
-  // steps in flight per wave: as many as fit next to the accumulators in
-  // about 192 registers (4 per fragment), at most 16 (with 16 tokens, 16
-  // experts and d = 4096, every load of a wave is in flight at once)
-  constexpr int D_FIT = (192 - 4 * MT * NT) / (4 * (MT + NT));
-  constexpr int D = D_FIT < 1 ? 1 : (D_FIT > 16 ? 16 : D_FIT);
-  __shared__ f32x4 red[RED];  // partial tiles, then the logits tile
-  float *tile = reinterpret_cast<float *>(red);
+  constexpr int ROWS = BT + EP;                     // staged rows per stage
+  static_assert(BT % RPI == 0 && EP % RPI == 0, "an instruction stays inside x or W_r");
+  constexpr int NI = ROWS / RPI;                    // load instructions per stage
+  constexpr int LPW_LO = NI / NW, NHI = NI % NW;    // waves w < NHI issue LPW_LO + 1
+  constexpr int LPW = LPW_LO + (NHI ? 1 : 0);
+  static_assert((NS - 2) * LPW <= 63, "vmcnt range");
+  constexpr int SB = ROWS * KB;                     // stage bytes
+  constexpr int TILES = MT * NT;
+  constexpr int KS = TILES >= NW ? 1 : NW / TILES;  // waves sharing a tile (K split)
+  constexpr int TPW = TILES * KS / NW;              // tiles per wave
+  constexpr int WG = NW / KS;                       // waves per K slice
+  constexpr int LD = EP + 4;                        // logits tile row pitch (floats)
+  static_assert(BT * LD * 4 <= NS * SB, "logits tile fits in the ring");
+  static_assert(KS == 1 || (KS - 1) * WG * TPW * kWave * 16 <= NS * SB, "partials fit in the ring");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * SB];
+
   const int l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const int t0 = blockIdx.x * BT;
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int S = (d + KC - 1) / KC;                   // stages
+  const int nchunk = d / 8;                          // 16-B chunks per row (d is a multiple of 8)
+  const int nld = LPW_LO + (w < NHI ? 1 : 0);        // this wave's loads per stage (wave-uniform)
+  auto swz = [](int r) { return KB == 128 ? (r >> 1) & 7 : r & 15; };
 
-  const int ksteps = (d + 31) / 32;
-  const int nsteps = ksteps > w ? (ksteps - w + NW - 1) / NW : 0;  // this wave's steps
-  const bf16x8 zero = {};
-  bf16x8 a[D][MT], b[D][NT];
-  // fragments of this wave's step j (zero past the end of d or of the rows)
-  auto load = [&](bf16x8 (&fa)[MT], bf16x8 (&fb)[NT], int j) {
-    const int kk = (w + j * NW) * 32 + (l >> 4) * 8;
-    const bool kin = j < nsteps && kk < d;
+  // instruction i = w + NW*j covers staged rows RPI*i .. +RPI-1; lane l ->
+  // row RPI*i + l/CPR, stored chunk l%CPR, which holds logical chunk
+  // (l%CPR) ^ swz(row)
+  const uint32_t ring_lds = lds_addr_of(ring);
+  uint32_t voff[LPW];
+  bool is_x[LPW];
+  int lchunk[LPW];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int row = t0 + m * 16 + (l & 15);
-      fa[m] = (kin && row < T) ? *reinterpret_cast<const bf16x8 *>(x + (int64_t)row * d + kk) : zero;
-    }
+  for (int jj = 0; jj < LPW; ++jj) {
+    const int i = min(w + NW * jj, NI - 1);
+    const int r = RPI * i + l / CPR;
+    const int c = (l % CPR) ^ swz(r);
+    lchunk[jj] = c;
+    is_x[jj] = i < BT / RPI;  // wave-uniform: x rows come first
+    if (r < BT) voff[jj] = static_cast<uint32_t>((min(t0 + r, T - 1) - t0) * static_cast<int64_t>(d) * 2 + c * 16);
+    else voff[jj] = static_cast<uint32_t>(min(r - BT, E - 1) * static_cast<int64_t>(d) * 2 + c * 16);
+  }
+  const char *xb = reinterpret_cast<const char *>(x) + static_cast<int64_t>(t0) * d * 2;
+  const char *wb = reinterpret_cast<const char *>(wr);
+  // stage s -> ring slot s % NS; a stage whose chunks run past d (the last one
+  // when d % KC != 0) reads a clamped chunk there, whose products are zeroed
+  // below
+  auto issue = [&](int s) {
+    const uint32_t slot = ring_lds + static_cast<uint32_t>((s % NS) * SB);
+    const bool tail = (s + 1) * KC > d;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int e = n * 16 + (l & 15);
-      fb[n] = (kin && e < E) ? *reinterpret_cast<const bf16x8 *>(wr + (int64_t)e * d + kk) : zero;
+    for (int jj = 0; jj < LPW; ++jj) {
+      if (jj == LPW - 1 && NHI && w >= NHI) break;  // wave-uniform
+      const int i = w + NW * jj;
+      uint32_t off = voff[jj];
+      if (tail) {
+        const int over = s * CPR + lchunk[jj] - (nchunk - 1);  // chunks past the last real one
+        if (over > 0) off -= static_cast<uint32_t>(over * 16);
+      }
+      dma16(off, (is_x[jj] ? xb : wb) + static_cast<int64_t>(s) * KB, slot + i * 1024);
     }
   };
+
+  const int kslice = w / WG;
+  f32x4 acc[TPW];
 #pragma unroll
-  for (int i = 0; i < D; ++i) load(a[i], b[i], i);
-  for (int j0 = 0; j0 < nsteps; j0 += D) {
+  for (int jj = 0; jj < TPW; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int frow = l & 15;
+  auto frag = [&](const uint8_t *slot, int row, int ks) -> bf16x8 {
+    const int c = ks * 4 + (l >> 4);
+    return *reinterpret_cast<const bf16x8 *>(slot + row * KB + ((c ^ swz(row)) << 4));
+  };
+
+  for (int s = 0; s < NS - 1 && s < S; ++s) issue(s);
+  for (int s = 0; s < S; ++s) {
+    if (s + NS - 2 < S) {
+      if (NHI == 0 || nld == LPW) wait_vm<(NS - 2) * LPW>();
+      else wait_vm<(NS - 2) * LPW_LO>();
+    } else {
+      wait_vm<0>();
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s + NS - 1 < S) issue(s + NS - 1);  // refills slot (s-1) % NS: every wave is past reading it
+    if (KS > 1 && s % KS != kslice) continue;
+    const uint8_t *slot = ring + (s % NS) * SB;
+    const bool tail = (s + 1) * KC > d;
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      if (j0 + i < nsteps) {
+    for (int ks = 0; ks < KC / 32; ++ks) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int n = 0; n < NT; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][m], b[i][n], acc[m][n], 0, 0, 0);
-        load(a[i], b[i], j0 + i + D);
+      for (int jj = 0; jj < TPW; ++jj) {
+        const int q = (w % WG) + WG * jj;
+        const int m = q / NT, n = q - (q / NT) * NT;
+        bf16x8 a = frag(slot, m * 16 + frow, ks);
+        const bf16x8 b = frag(slot, BT + n * 16 + frow, ks);
+        if (tail && s * KC + (ks * 4 + (l >> 4)) * 8 >= d) a = bf16x8{};
+        acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[jj], 0, 0, 0);
       }
     }
   }
-  // Sum of the waves' partial tiles by a fixed tree (waves h..2h-1 hand
-  // theirs to waves 0..h-1, h = 4, 2, 1), so the result is deterministic.
-  // Partials travel in accumulator order: each lane moves whole float4s to
-  // consecutive addresses.
+  __syncthreads();  // the ring is free: partial tiles, then the logits tile
+  float *red = reinterpret_cast<float *>(ring);
+  if constexpr (KS > 1) {
+    // K slices 1..KS-1 hand their partial tiles over; slice 0 adds them in
+    // slice order (accumulator layout, one float4 per lane)
+    if (kslice > 0) {
 #pragma unroll
-  for (int h = NW / 2; h >= 1; h >>= 1) {
-    if (w >= h && w < 2 * h) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int n = 0; n < NT; ++n) red[((w - h) * MT * NT + m * NT + n) * kWave + l] = acc[m][n];
+      for (int jj = 0; jj < TPW; ++jj)
+        reinterpret_cast<f32x4 *>(red)[(((kslice - 1) * WG + (w % WG)) * TPW + jj) * kWave + l] = acc[jj];
     }
     __syncthreads();
-    if (w < h) {
+    if (kslice == 0) {
+      for (int ksl = 1; ksl < KS; ++ksl)
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[m][n] += red[(w * MT * NT + m * NT + n) * kWave + l];
+        for (int jj = 0; jj < TPW; ++jj)
+          acc[jj] += reinterpret_cast<const f32x4 *>(red)[(((ksl - 1) * WG + w) * TPW + jj) * kWave + l];
     }
     __syncthreads();
   }
-  if (w == 0) {
+  float *tile = red;
+  if (kslice == 0) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int jj = 0; jj < TPW; ++jj) {
+      const int q = (w % WG) + WG * jj;
+      const int m = q / NT, n = q - (q / NT) * NT;
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tile[(m * 16 + (l >> 4) * 4 + r) * LD + n * 16 + (l & 15)] = acc[m][n][r];
+      for (int r = 0; r < 4; ++r) tile[(m * 16 + (l >> 4) * 4 + r) * LD + n * 16 + (l & 15)] = acc[jj][r];
+    }
   }
   __syncthreads();
   finish_logits(tile, LD, BT, t0, T, E, bias, bias_stride, logits);
-  gate_rows(tile, LD, BT, t0, T, E, k, routing, topk_idx, topk_w, scores);
+  gate_tile<NT>(tile, LD, BT, t0, T, E, k, routing, topk_idx, topk_w, scores);
+  if (routing == 2) store_scores_t<BT>(tile, LD, t0, T, E, scores);
 }
 
 constexpr int kF32Rows = 16;
 
+template <int NT>
 __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
     int64_t bias_stride, int T, int d, int E, int k, int routing, float *__restrict__ logits,
@@ -325,10 +412,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(
   }
   __syncthreads();
   finish_logits(tile, E, kF32Rows, t0, T, E, bias, bias_stride, logits);
-  gate_rows(tile, E, kF32Rows, t0, T, E, k, routing, topk_idx, topk_w, scores);
+  gate_tile<NT>(tile, E, kF32Rows, t0, T, E, k, routing, topk_idx, topk_w, scores);
+  if (routing == 2) store_scores_t<kF32Rows>(tile, E, t0, T, E, scores);
 }
 
 // Gate only: the logits are an input.
+template <int NT>
 __global__ __launch_bounds__(kRouteThreads) void gate_only_kernel(
     const float *__restrict__ logits, int T, int E, int k, int routing, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, float *__restrict__ scores) {
@@ -340,76 +429,142 @@ __global__ __launch_bounds__(kRouteThreads) void gate_only_kernel(
     tile[r * E + e] = (t < T) ? logits[(int64_t)t * E + e] : 0.f;
   }
   __syncthreads();
-  gate_rows(tile, E, kF32Rows, t0, T, E, k, routing, topk_idx, topk_w, scores);
+  gate_tile<NT>(tile, E, kF32Rows, t0, T, E, k, routing, topk_idx, topk_w, scores);
+  if (routing == 2) store_scores_t<kF32Rows>(tile, E, t0, T, E, scores);
 }
 
 constexpr int kEcThreads = 1024;
 
-// ExpertChoice selection: expert e (one workgroup) keeps the C tokens with the
-// largest scores[t,e] (equal scores: lower token), in ascending token order.
+// ExpertChoice selection, one workgroup per expert e: the C tokens with the
+// largest scores[e, t] (equal scores: lower token), in ascending token order.
+// The expert's score row is contiguous (expert-major scores) and is read
+// once into LDS as 32-bit keys; scores are >= 0, so their bit patterns order
+// like the values.  The C-th largest key is found by a radix select from the
+// top: the bits every key shares (block-wide AND and OR of the keys) are
+// taken at once, then up to 11 bits per pass.  The first pass histograms
+// every key; the keys of its threshold digit are then copied to a candidate
+// list (keys above it are selected outright), so the later passes only see
+// those.  Finally the tokens whose key is above the threshold, and the
+// lowest tokens whose key equals it, are compacted in ascending token order.
+constexpr int kEcDigitBits = 11;
+constexpr int kEcBins = 1 << kEcDigitBits;
+
+// The digit (of `bins` bins, histogram in LDS) that holds the need-th
+// largest key, searched from the top by wave 0: lane l holds the 32 bins
+// bins-1-32l .. bins-32-32l.  Writes the digit and the rank of the wanted key
+// inside it to state[0], state[1].
+__device__ __forceinline__ void ec_find_digit(const int *hist, int need, uint32_t *state) {
+  const int l = lane_id();
+  int sum = 0;
+  for (int q = 0; q < 32; ++q) sum += hist[kEcBins - 1 - (32 * l + q)];
+  const int incl = wave_incl_scan(sum);
+  const int excl = incl - sum;
+  const uint64_t hit = __ballot(excl < need && need <= incl);
+  const int src = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave - 1;
+  if (l == src) {
+    int cum = excl, q = 0;
+    for (; q < 31; ++q) {
+      const int h = hist[kEcBins - 1 - (32 * l + q)];
+      if (cum + h >= need) break;
+      cum += h;
+    }
+    state[0] = static_cast<uint32_t>(kEcBins - 1 - (32 * l + q));
+    state[1] = static_cast<uint32_t>(need - cum);
+  }
+}
+
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__restrict__ scores, int T,
                                                                int E, int C, int32_t *__restrict__ ec_token,
                                                                float *__restrict__ ec_w) {
   __shared__ uint32_t key[kEcMaxTokens];
-  __shared__ int hist[256];
+  __shared__ uint32_t cand[kEcMaxTokens];
+  __shared__ int hist[kEcBins];
   __shared__ int scan_tmp[kEcThreads / kWave + 1];
+  __shared__ uint32_t red[2][kEcThreads / kWave];
   __shared__ uint32_t sel_state[2];
+  __shared__ int ncand;
   const int e = blockIdx.x;
-  for (int t = threadIdx.x; t < T; t += blockDim.x) key[t] = __float_as_uint(scores[(int64_t)t * E + e]);
-  uint32_t prefix = 0, pmask = 0;
+  const int nw = kEcThreads / kWave;
+  const float *row = scores + (int64_t)e * T;
+  uint32_t kand = ~0u, kor = 0u;
+  if ((T & 3) == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+    for (int i = threadIdx.x; i < T / 4; i += kEcThreads) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(row + 4 * i);
+      *reinterpret_cast<u32x4 *>(key + 4 * i) = v;
+      kand &= v[0] & v[1] & v[2] & v[3];
+      kor |= v[0] | v[1] | v[2] | v[3];
+    }
+  } else {
+    for (int t = threadIdx.x; t < T; t += kEcThreads) {
+      const uint32_t v = __float_as_uint(row[t]);
+      key[t] = v;
+      kand &= v;
+      kor |= v;
+    }
+  }
+  for (int i = threadIdx.x; i < kEcBins; i += kEcThreads) hist[i] = 0;
+  if (threadIdx.x == 0) ncand = 0;
+  // block-wide AND / OR (exact in any order)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kand &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(kand), o, kWave));
+    kor |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(kor), o, kWave));
+  }
+  if (lane_id() == 0) {
+    red[0][wave_id()] = kand;
+    red[1][wave_id()] = kor;
+  }
+  __syncthreads();
+  kand = ~0u;
+  kor = 0u;
+  for (int i = 0; i < nw; ++i) {
+    kand &= red[0][i];
+    kor |= red[1][i];
+  }
+  const uint32_t diff = kand ^ kor;  // bits where keys differ
+  // bits at and above `pos` are shared by every key (and already in `prefix`)
+  int pos = diff ? 32 - __clz(static_cast<int>(diff)) : 0;
+  uint32_t prefix = pos >= 32 ? 0u : (kand >> pos) << pos;
   int need = C;  // rank (1-based, from the top) of the wanted key among those matching the prefix
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+  bool first = true;
+  while (pos > 0) {
+    const int wbits = pos < kEcDigitBits ? pos : kEcDigitBits;
+    const int shift = pos - wbits;
+    const uint32_t dmask = (1u << wbits) - 1u;
+    // histogram of the digit: every key in the first pass (they all share
+    // the bits above pos), the candidates afterwards (integer LDS adds,
+    // order-independent)
+    const uint32_t *src = first ? key : cand;
+    const int n = first ? T : ncand;
+    for (int i = threadIdx.x; i < n; i += kEcThreads) atomicAdd(&hist[(src[i] >> shift) & dmask], 1);
     __syncthreads();
-    // Softmax scores of one expert share their top bits, so most lanes hit
-    // the same bin: the lanes of a wave with equal bins are found with one
-    // ballot per bin bit and only the lowest of them adds the group's count.
-    for (int t0 = 0; t0 < T; t0 += blockDim.x) {
-      const int t = t0 + threadIdx.x;
-      const uint32_t kv = t < T ? key[t] : 0u;
-      const bool match = t < T && (kv & pmask) == prefix;
-      const uint32_t bin = (kv >> shift) & 255u;
-      uint64_t peers = __ballot(match);
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const bool bit = (bin >> b) & 1u;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
-      }
-      if (match && (peers & lanemask_lt()) == 0) atomicAdd(&hist[bin], __popcll(peers));
-    }
+    if (wave_id() == 0) ec_find_digit(hist, need, sel_state);
     __syncthreads();
-    if (wave_id() == 0) {
-      // bins from the top: lane l holds bins 255-4l .. 252-4l; a suffix
-      // count over them finds the bin that holds the need-th largest key
-      const int l = lane_id();
-      int h[4], sum = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        h[q] = hist[255 - (4 * l + q)];
-        sum += h[q];
-      }
-      const int incl = wave_incl_scan(sum);
-      const int excl = incl - sum;
-      const uint64_t hit = __ballot(excl < need && need <= incl);
-      // every key matching the prefix is in some bin and at least `need` of
-      // them do, so one lane is hit; without a hit bin 0 is taken, as the
-      // sequential search did
-      const int src = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave - 1;
-      if (l == src) {
-        int cum = excl, q = 0;
-        for (; q < 3; ++q) {
-          if (cum + h[q] >= need) break;
-          cum += h[q];
-        }
-        sel_state[0] = static_cast<uint32_t>(255 - (4 * l + q));
-        sel_state[1] = static_cast<uint32_t>(need - cum);
-      }
-    }
-    __syncthreads();
-    prefix |= sel_state[0] << shift;
-    pmask |= 255u << shift;
+    const uint32_t digit = sel_state[0];
     need = static_cast<int>(sel_state[1]);
+    prefix |= digit << shift;
+    for (int i = threadIdx.x; i < kEcBins; i += kEcThreads) hist[i] = 0;
+    if (shift > 0) {
+      // the keys of the threshold digit become the candidates of the next
+      // pass (in place when they already are candidates: a wave reads its
+      // keys before any lane writes, and writes land at or below them)
+      __syncthreads();
+      if (threadIdx.x == 0 && !first) ncand = 0;
+      __syncthreads();
+      for (int i0 = 0; i0 < n; i0 += kEcThreads) {
+        const int i = i0 + threadIdx.x;
+        const uint32_t kv = i < n ? src[i] : 0u;
+        const bool keep = i < n && ((kv >> shift) & dmask) == digit;
+        __syncthreads();
+        const uint64_t b = __ballot(keep);
+        int base = 0;
+        if (lane_id() == 0 && b) base = atomicAdd(&ncand, __popcll(b));
+        base = __shfl(base, 0, kWave);
+        if (keep) cand[base + __popcll(b & lanemask_lt())] = kv;
+      }
+    }
+    first = false;
+    pos = shift;
     __syncthreads();
   }
   // prefix is the C-th largest key; `need` of the keys equal to it are taken
@@ -429,7 +584,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
       else if (kv == prefix) { if (er < need) ++n_sel; ++er; }
     }
   }
-  int pos = block_excl_scan(n_sel, scan_tmp, &tot);
+  int p = block_excl_scan(n_sel, scan_tmp, &tot);
   {
     int er = eq_rank;
     for (int t = b0; t < b1; ++t) {
@@ -438,9 +593,9 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
       if (kv > prefix) take = true;
       else if (kv == prefix) { take = er < need; ++er; }
       if (take) {
-        ec_token[(int64_t)e * C + pos] = t;
-        ec_w[(int64_t)e * C + pos] = __uint_as_float(kv);
-        ++pos;
+        ec_token[(int64_t)e * C + p] = t;
+        ec_w[(int64_t)e * C + p] = __uint_as_float(kv);
+        ++p;
       }
     }
   }
@@ -450,36 +605,46 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
+  int nt = 1;
+  while (nt * 16 < a.E) nt <<= 1;
   if (a.x == nullptr) {
     const int blocks = (a.T + kF32Rows - 1) / kF32Rows;
-    gate_only_kernel<<<blocks, kRouteThreads, 0, st>>>(a.logits, a.T, a.E, a.k, a.routing, a.topk_idx,
-                                                       a.topk_w, a.scores);
+#define MOE_GATE_CASE(NT_)                                                                                  \
+  if (nt == NT_)                                                                                           \
+    gate_only_kernel<NT_><<<blocks, kRouteThreads, 0, st>>>(a.logits, a.T, a.E, a.k, a.routing, a.topk_idx, \
+                                                             a.topk_w, a.scores);
+    MOE_GATE_CASE(1) MOE_GATE_CASE(2) MOE_GATE_CASE(4) MOE_GATE_CASE(8) MOE_GATE_CASE(16)
+#undef MOE_GATE_CASE
   } else if (a.dtype == 0) {
     const int blocks = (a.T + kF32Rows - 1) / kF32Rows;
-    route_f32_kernel<<<blocks, kRouteThreads, 0, st>>>(
-        static_cast<const float *>(a.x), static_cast<const float *>(a.wr), a.bias, a.bias_stride, a.T,
+#define MOE_F32_CASE(NT_)                                                                              \
+  if (nt == NT_)                                                                                      \
+    route_f32_kernel<NT_><<<blocks, kRouteThreads, 0, st>>>(                                          \
+        static_cast<const float *>(a.x), static_cast<const float *>(a.wr), a.bias, a.bias_stride, a.T, \
         a.d, a.E, a.k, a.routing, a.logits, a.topk_idx, a.topk_w, a.scores);
+    MOE_F32_CASE(1) MOE_F32_CASE(2) MOE_F32_CASE(4) MOE_F32_CASE(8) MOE_F32_CASE(16)
+#undef MOE_F32_CASE
   } else {
-    int nt = 1;
-    while (nt * 16 < a.E) nt <<= 1;
-    // 16*mt tokens per block: larger token tiles re-read the router weight
-    // (all E rows, from L2) fewer times, as long as 256 blocks remain
-    int mt = 1;
-    if ((a.T + 63) / 64 >= 256 && nt <= 8) mt = 4;
-    else if ((a.T + 31) / 32 >= 256 && nt <= 16) mt = 2;
+    // 16*mt tokens per workgroup; 64 when that still gives a workgroup to
+    // every CU, since each workgroup streams all of W_r once
+    int mt = nt == 1 ? 1 : 2;
+    if (nt >= 2 && nt <= 8 && (a.T + 63) / 64 >= 256) mt = 4;
     const int blocks = (a.T + 16 * mt - 1) / (16 * mt);
     const uint16_t *x = static_cast<const uint16_t *>(a.x);
     const uint16_t *wr = static_cast<const uint16_t *>(a.wr);
-#define MOE_ROUTE_CASE(MT_, NT_)                                                                     \
-  if (mt == MT_ && nt == NT_) {                                                                      \
-    route_bf16_kernel<MT_, NT_><<<blocks, kRouteBf16Threads, 0, st>>>(x, wr, a.bias, a.bias_stride, a.T, \
-                                                                  a.d, a.E, a.k, a.routing,          \
-                                                                  a.logits, a.topk_idx, a.topk_w,    \
-                                                                  a.scores);                         \
+    // 8 waves, 256-B staged rows (measured on the 8-, 64- and 128-expert
+    // workloads: 12.7 / 12.1 / 14.7 us against 15.2 / 17.2 / 18.0 us with 4
+    // waves and 128-B rows); 64-token tiles over 128 experts keep 128-B rows,
+    // whose deeper ring measured faster there (14.0 us); the ring holds
+    // 128-144 KB of LDS (one workgroup per CU)
+#define MOE_ROUTE_CASE(MT_, NT_, NS_, KB_)                                                                   \
+  if (mt == MT_ && nt == NT_) {                                                                             \
+    route_bf16_kernel<MT_, NT_, NS_, 8, KB_><<<blocks, 8 * kWave, 0, st>>>(                                 \
+        x, wr, a.bias, a.bias_stride, a.T, a.d, a.E, a.k, a.routing, a.logits, a.topk_idx, a.topk_w, a.scores); \
   }
-    MOE_ROUTE_CASE(1, 1) MOE_ROUTE_CASE(1, 2) MOE_ROUTE_CASE(1, 4) MOE_ROUTE_CASE(1, 8) MOE_ROUTE_CASE(1, 16)
-    MOE_ROUTE_CASE(2, 1) MOE_ROUTE_CASE(2, 2) MOE_ROUTE_CASE(2, 4) MOE_ROUTE_CASE(2, 8) MOE_ROUTE_CASE(2, 16)
-    MOE_ROUTE_CASE(4, 1) MOE_ROUTE_CASE(4, 2) MOE_ROUTE_CASE(4, 4) MOE_ROUTE_CASE(4, 8)
+    MOE_ROUTE_CASE(1, 1, 16, 256) MOE_ROUTE_CASE(2, 2, 8, 256) MOE_ROUTE_CASE(2, 4, 6, 256)
+    MOE_ROUTE_CASE(2, 8, 3, 256) MOE_ROUTE_CASE(2, 16, 2, 256) MOE_ROUTE_CASE(4, 2, 6, 256)
+    MOE_ROUTE_CASE(4, 4, 4, 256) MOE_ROUTE_CASE(4, 8, 6, 128)
 #undef MOE_ROUTE_CASE
   }
   hipError_t err = hipGetLastError();

@@ -1,0 +1,85 @@
+// HBM stream kernels: a plain read, write and copy of a device buffer.  They
+// measure the rates the device sustains for the access patterns of the
+// HBM-bound stages (route, permute and combine are reads, writes or both of
+// contiguous rows), which those stages are read against, and they are the
+// known-size copy that calibrates the HBM byte counters.
+//
+// gfx950 design: 16-byte accesses, each thread keeps four of them in flight
+// per step (64 B) and strides the grid through the buffer, so every wave
+// instruction covers 1 KB of consecutive bytes; 2048 workgroups of 256
+// threads (8 per CU) keep 32 waves per CU issuing.  Non-temporal accesses
+// are an option (streaming data that is not reused).
+#include "../../include/moe_probe.h"
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 4;
+
+template <bool NT>
+__device__ __forceinline__ u32x4 sload(const u32x4 *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void sstore(u32x4 *p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// KIND 0: read src (an XOR of every word is kept so the loads are not dead;
+// it is written to sink only if it equals a value random data never gives);
+// 1: write a pattern to dst; 2: copy src to dst.
+template <int KIND, bool NT>
+__global__ __launch_bounds__(kStreamThreads) void stream_kernel(const u32x4 *__restrict__ src,
+                                                                u32x4 *__restrict__ dst, size_t n16,
+                                                                uint32_t *__restrict__ sink) {
+  const size_t nthr = static_cast<size_t>(gridDim.x) * kStreamThreads;
+  size_t i = static_cast<size_t>(blockIdx.x) * kStreamThreads + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const u32x4 pat = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, static_cast<uint32_t>(i)};
+  for (; i + (kStreamUnroll - 1) * nthr < n16; i += kStreamUnroll * nthr) {
+    u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u)
+      if (KIND != 1) v[u] = sload<NT>(src + i + u * nthr);
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      if (KIND == 0) acc ^= v[u];
+      else if (KIND == 1) sstore<NT>(dst + i + u * nthr, pat);
+      else sstore<NT>(dst + i + u * nthr, v[u]);
+    }
+  }
+  for (; i < n16; i += nthr) {
+    if (KIND == 0) acc ^= sload<NT>(src + i);
+    else if (KIND == 1) sstore<NT>(dst + i, pat);
+    else sstore<NT>(dst + i, sload<NT>(src + i));
+  }
+  if (KIND == 0 && acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u && sink) sink[0] = acc[2];
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_stream_probe(int32_t kind, int32_t nontemporal, const void *src, void *dst,
+                                       size_t bytes, void *sink, void *stream) {
+  if (kind < 0 || kind > 2 || (bytes & 15) != 0) return MOE_ERR_INVALID_ARG;
+  if ((kind != 1 && !src) || (kind != 0 && !dst)) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(dst) & 15)) return MOE_ERR_INVALID_ARG;
+  if (bytes == 0) return MOE_OK;
+  using namespace moe;
+  const size_t n16 = bytes / 16;
+  const int blocks = 2048;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const u32x4 *s = static_cast<const u32x4 *>(src);
+  u32x4 *d = static_cast<u32x4 *>(dst);
+  uint32_t *k = static_cast<uint32_t *>(sink);
+#define MOE_STREAM(K, N) stream_kernel<K, N><<<blocks, kStreamThreads, 0, st>>>(s, d, n16, k)
+  if (kind == 0) { if (nontemporal) MOE_STREAM(0, true); else MOE_STREAM(0, false); }
+  else if (kind == 1) { if (nontemporal) MOE_STREAM(1, true); else MOE_STREAM(1, false); }
+  else { if (nontemporal) MOE_STREAM(2, true); else MOE_STREAM(2, false); }
+#undef MOE_STREAM
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}

@@ -106,6 +106,7 @@ def load_library() -> ctypes.CDLL:
         "moe_layer_bwd_workspace": ([CP, ctypes.POINTER(BwdLayout)], ctypes.c_int),
         "moe_layer_fwd_train": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_layer_bwd": ([CP, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, ctypes.c_int32, P, sz, P], ctypes.c_int),
+        "moe_stream_probe": ([ctypes.c_int32, ctypes.c_int32, P, P, sz, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -116,10 +117,14 @@ def load_library() -> ctypes.CDLL:
 
 
 def header_symbols() -> list:
-    """Names of the functions declared in include/moe.h."""
-    with open(HEADER_PATH) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(moe_\w+)\s*\(", text, re.M)))
+    """Names of the functions declared in include/*.h."""
+    import glob
+    names = set()
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(HEADER_PATH), "*.h"))):
+        with open(path) as f:
+            text = f.read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(moe_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 # ----------------------------------------------------------------- helpers --
@@ -320,6 +325,15 @@ def layer_bwd(cfg: MoeConfig, x, w_router, w1, w2, fwd_workspace, dy, dx, dw_rou
         "moe_layer_bwd")
 
 
+def stream_probe(kind: str, src, dst, nbytes: int, nontemporal: bool = False, sink=None, stream=None):
+    """moe_stream_probe: kind "read", "write" or "copy" over nbytes of
+    contiguous device buffers (include/moe_probe.h)."""
+    k = {"read": 0, "write": 1, "copy": 2}[kind]
+    _check(load_library().moe_stream_probe(k, int(bool(nontemporal)), _arg(src, "src", None, 0),
+                                           _arg(dst, "dst", None, 0), nbytes, _arg(sink, "sink", None, 0),
+                                           _stream(stream)), "moe_stream_probe")
+
+
 # ------------------------------------------------ allocation conveniences --
 
 def alloc_workspace(cfg: MoeConfig, device="cuda") -> torch.Tensor:
@@ -416,7 +430,7 @@ class MoELayer:
             "y_perm": (dt, (rows, d)),
         }
         if ec:
-            s.update({"scores": (f32, (T, E)), "ec_token": (i32, (E, C)), "ec_w": (f32, (E, C)),
+            s.update({"scores": (f32, (E, T)), "ec_token": (i32, (E, C)), "ec_w": (f32, (E, C)),
                       "slot_row": (i32, (E * C,)), "slot_w": (f32, (E * C,)), "tok_ptr": (i32, (T + 1,))})
         else:
             s.update({"topk_idx": (i32, (T, k)), "topk_w": (f32, (T, k)), "slot_row": (i32, (T, k))})

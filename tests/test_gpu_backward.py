@@ -58,7 +58,7 @@ def _run(w: W.Workload, seed: int = 0, recompute: bool = True):
 
 def _oracle_fwd(w, layer, inp):
     lg = layer.view("logits").cpu().numpy()
-    sc = layer.view("scores").cpu().numpy() if w.routing == W.EXPERT_CHOICE else None
+    sc = layer.view("scores").cpu().numpy().T if w.routing == W.EXPERT_CHOICE else None
     return oracle.layer(inp["x"], inp["wr"], inp["w1"], inp["w2"], k=w.k, routing=w.routing, act=w.act, cf=w.cf,
                         ec_capacity=w.ec_capacity, bias=inp["bias"], bias_stride=inp["bias_stride"],
                         ws1=inp["ws1"], ws2=inp["ws2"], given_logits=lg, given_scores=sc, toks=np.zeros(0, np.int32))
@@ -120,7 +120,7 @@ def test_backward_parity_small(name, recompute):
         ref = oracle.layer(inp["x"], inp["wr"], inp["w1"], inp["w2"], k=w.k, routing=w.routing, act=w.act, cf=w.cf,
                            ec_capacity=w.ec_capacity, bias=inp["bias"], bias_stride=inp["bias_stride"],
                            ws1=inp["ws1"], ws2=inp["ws2"], given_logits=layer.view("logits").cpu().numpy(),
-                           given_scores=(layer.view("scores").cpu().numpy() if w.routing == W.EXPERT_CHOICE
+                           given_scores=(layer.view("scores").cpu().numpy().T if w.routing == W.EXPERT_CHOICE
                                          else None))
         _check("y (training forward)", host_float(layer.y), ref.y, TOL_Y[w.dtype])
     _check_layout(w, layer, inp)
@@ -202,7 +202,7 @@ def test_backward_parity_full_size(name):
     tol = TOL_Y[w.dtype]
     _check_layout(w, layer, inp)
     lg = layer.view("logits").cpu().numpy()
-    sc = layer.view("scores").cpu().numpy() if w.routing == W.EXPERT_CHOICE else None
+    sc = layer.view("scores").cpu().numpy().T if w.routing == W.EXPERT_CHOICE else None
     rng = np.random.default_rng(3)
     toks = np.array(sorted({0, w.T - 1, *rng.choice(w.T, size=min(24, w.T), replace=False).tolist()}), np.int32)
     fwd = oracle.layer(inp["x"], inp["wr"], inp["w1"], inp["w2"], k=w.k, routing=w.routing, act=w.act, cf=w.cf,

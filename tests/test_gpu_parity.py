@@ -47,6 +47,11 @@ SMALL = {
     "correlated_small": W.small_variant(WL["correlated_top2_bf16"], T=1500, d=256, E=16, d_ff=200),
     "correlated_ec_small": W.small_variant(WL["correlated_ec_bf16"], T=1500, d=256, E=16, d_ff=200,
                                            ec_capacity=187),
+    # d_model not a multiple of the router's 64-wide K stages (its last stage
+    # holds 8 columns), 24 experts padded to 32, 6 slots, 333 tokens (a
+    # partial token tile)
+    "route_ktail_small": W.small_variant(WL["finegrained_shared_bf16"], T=333, d=200, E=24, d_ff=136,
+                                         d_ff_shared=0, wr_std=1.0 / np.sqrt(200.0)),
 }
 
 
@@ -177,6 +182,36 @@ def test_gate_tie_heavy_logits_match_oracle(E, k, mode):
     assert np.array_equal(idx.cpu().numpy(), ref)
     np.testing.assert_allclose(tw.cpu().numpy(), oracle.gate_weights(lg.astype(np.float64), ref, mode),
                                rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T,E,C,vals", [
+    (777, 8, 100, (-2.0, -0.0, 0.0, 0.5, 1.0, 3.0)),   # many exact score ties across tokens
+    (2048, 64, 32, (0.0,)),                             # every score equal: the lowest C tokens
+    (4000, 16, 4000, (-1.0, 0.0, 1.0)),                 # C = T: every token
+    (16384, 128, 2, (0.0, 0.25, 0.5)),                  # the largest T, tiny C
+    (300, 5, 299, (-3.0, 2.0)),                         # two score levels, C one short of T
+])
+def test_expert_choice_selection_ties_match_oracle(T, E, C, vals):
+    """ExpertChoice selection on given fp32 logits with heavy ties: the
+    softmax scores repeat exactly, so the C-th largest score is shared by many
+    tokens and the lowest of them must be taken; selections bit-exact against
+    the oracle run on the GPU's scores, weights equal the chosen scores."""
+    rng = np.random.default_rng(T + E * 7 + C)
+    lg = np.asarray(vals, np.float32)[rng.integers(0, len(vals), size=(T, E))]
+    cfg = moe.MoeConfig(T, 8, E, 0, 8, 0, 0.0, C, W.F32, W.GELU, W.EXPERT_CHOICE)
+    d_lg = torch.from_numpy(lg).cuda()
+    sc = torch.empty((E, T), dtype=torch.float32, device="cuda")
+    ect = torch.empty((E, C), dtype=torch.int32, device="cuda")
+    ecw = torch.empty((E, C), dtype=torch.float32, device="cuda")
+    moe.route(cfg, None, None, d_lg, scores=sc, ec_token=ect, ec_w=ecw)
+    torch.cuda.synchronize()
+    scores = sc.cpu().numpy().T
+    np.testing.assert_allclose(scores, oracle.softmax(lg.astype(np.float64)), rtol=2e-6, atol=1e-9)
+    ref = oracle.ec_select(scores.astype(np.float64), C)
+    got = ect.cpu().numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(ecw.cpu().numpy(), scores[ref, np.arange(E)[:, None]])
 
 
 @pytest.mark.gpu
