@@ -23,7 +23,11 @@ workload on the host cores.  ``backward`` times moe_layer_bwd (the layer's
 backward pass for a seeded upstream gradient) in a region of its own after
 the forward regions, in both modes: after a plain forward with the expert
 pre-activations recomputed, and after the training forward that keeps them
-(whose time is reported as ``train_fwd_ms``).
+(whose time is reported as ``train_fwd_ms``).  ``hbm_probe`` gives the
+device's read, write and copy rates from the library's own stream kernels.
+``workloads`` then measures every other workload the same way (median layer
+time, tokens/s, stage medians with their algorithmic rates, the FFN's
+roofline fraction), after the headline's timed regions.
 """
 from __future__ import annotations
 

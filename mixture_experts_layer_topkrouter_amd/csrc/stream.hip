@@ -4,11 +4,11 @@
 // contiguous rows), which those stages are read against, and they are the
 // known-size copy that calibrates the HBM byte counters.
 //
-// gfx950 design: 16-byte accesses, each thread keeps four of them in flight
-// per step (64 B) and strides the grid through the buffer, so every wave
-// instruction covers 1 KB of consecutive bytes; 2048 workgroups of 256
-// threads (8 per CU) keep 32 waves per CU issuing.  Non-temporal accesses
-// are an option (streaming data that is not reused).
+// gfx950 design: 16-byte accesses, four in flight per thread; one workgroup
+// per 16 KB of buffer, so the grid is large and each wave streams contiguous
+// bytes.  Non-temporal accesses are an option (streaming data that is not
+// reused); measured on one MI355X over 1 GiB: read 7.0, write 6.1, copy 6.1
+// TB/s (non-temporal read and copy, plain write).
 #include "../../include/moe_probe.h"
 #include "common.h"
 
@@ -31,31 +31,28 @@ __device__ __forceinline__ void sstore(u32x4 *p, u32x4 v) {
 
 // KIND 0: read src (an XOR of every word is kept so the loads are not dead;
 // it is written to sink only if it equals a value random data never gives);
-// 1: write a pattern to dst; 2: copy src to dst.
+// 1: write a pattern to dst; 2: copy src to dst.  Each workgroup takes one
+// 16-KB run of the buffer (256 threads x 4 x 16 B, consecutive lanes on
+// consecutive 16-B pieces), so every wave streams whole contiguous KB: a
+// grid-stride loop over the whole buffer measured 15-25 % slower here.
 template <int KIND, bool NT>
 __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const u32x4 *__restrict__ src,
                                                                 u32x4 *__restrict__ dst, size_t n16,
                                                                 uint32_t *__restrict__ sink) {
-  const size_t nthr = static_cast<size_t>(gridDim.x) * kStreamThreads;
-  size_t i = static_cast<size_t>(blockIdx.x) * kStreamThreads + threadIdx.x;
+  const size_t i = static_cast<size_t>(blockIdx.x) * kStreamThreads * kStreamUnroll + threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
   const u32x4 pat = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, static_cast<uint32_t>(i)};
-  for (; i + (kStreamUnroll - 1) * nthr < n16; i += kStreamUnroll * nthr) {
-    u32x4 v[kStreamUnroll];
+  u32x4 v[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u)
-      if (KIND != 1) v[u] = sload<NT>(src + i + u * nthr);
+  for (int u = 0; u < kStreamUnroll; ++u)
+    if (KIND != 1 && i + u * kStreamThreads < n16) v[u] = sload<NT>(src + i + u * kStreamThreads);
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) {
-      if (KIND == 0) acc ^= v[u];
-      else if (KIND == 1) sstore<NT>(dst + i + u * nthr, pat);
-      else sstore<NT>(dst + i + u * nthr, v[u]);
-    }
-  }
-  for (; i < n16; i += nthr) {
-    if (KIND == 0) acc ^= sload<NT>(src + i);
-    else if (KIND == 1) sstore<NT>(dst + i, pat);
-    else sstore<NT>(dst + i, sload<NT>(src + i));
+  for (int u = 0; u < kStreamUnroll; ++u) {
+    const size_t j = i + u * kStreamThreads;
+    if (j >= n16) break;
+    if (KIND == 0) acc ^= v[u];
+    else if (KIND == 1) sstore<NT>(dst + j, pat);
+    else sstore<NT>(dst + j, v[u]);
   }
   if (KIND == 0 && acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u && sink) sink[0] = acc[2];
 }
@@ -71,7 +68,10 @@ extern "C" moe_status moe_stream_probe(int32_t kind, int32_t nontemporal, const 
   if (bytes == 0) return MOE_OK;
   using namespace moe;
   const size_t n16 = bytes / 16;
-  const int blocks = 2048;
+  const size_t per_block = static_cast<size_t>(kStreamThreads) * kStreamUnroll;
+  const size_t nblk = (n16 + per_block - 1) / per_block;
+  if (nblk > 0x7fffffffu) return MOE_ERR_UNSUPPORTED;
+  const int blocks = static_cast<int>(nblk);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const u32x4 *s = static_cast<const u32x4 *>(src);
   u32x4 *d = static_cast<u32x4 *>(dst);

@@ -19,7 +19,9 @@ import torch
 from . import workloads as W
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+# a sanitizer build of the same sources (tests/test_sanitizers.py) is loaded
+# in place of the in-tree one when MOE_HIP_LIB names it
+LIB_PATH = os.environ.get("MOE_HIP_LIB") or os.path.join(_HERE, "libmoe_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 F32, BF16 = 0, 1

@@ -25,6 +25,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# a sanitizer build of the same source (tests/test_sanitizers.py) is loaded
+# in place of the default one when this names it
+_LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB")
 
 SOFTMAX_ALL = 0
 SOFTMAX_TOPK = 1
@@ -50,9 +53,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
     lib.orc_logits.argtypes = [i32, i32, i32, i32, P, P, P, i64, P]

@@ -32,6 +32,32 @@ def inputs(w: W.Workload, seed: int = 0):
     return W.make_inputs(w, seed)
 
 
+def elem_rel_err(y, ref, floor: float = 1e-3) -> float:
+    """Largest element-wise relative error, each element's |ref| floored at
+    floor * max |ref| (relative error is undefined near zero)."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.maximum(np.abs(ref), floor * max(np.max(np.abs(ref)), 1e-300))
+    return float(np.max(np.abs(y - ref) / den))
+
+
+def tile_cover_tokens(w: W.Workload, layer, bm: int = None) -> np.ndarray:
+    """Tokens whose rows include the first and the last row of every
+    (expert, row tile) of the grouped GEMM: bm = 256 when the experts average
+    at least 192 rows (the 256-row kernel), else 64 (the weight-streaming
+    kernel's tiles).  Checking these tokens' full output rows covers every
+    tile of both GEMMs, including tiles whose K range is cut into pieces."""
+    off = layer.view("expert_offset").cpu().numpy().astype(np.int64)
+    rt = layer.view("row_token").cpu().numpy()
+    if bm is None:
+        bm = 256 if moe.max_rows(layer.cfg) // w.E >= 192 else 64
+    rows = []
+    for e in range(w.E):
+        for r0 in range(off[e], off[e + 1], bm):
+            rows += [r0, min(r0 + bm, off[e + 1]) - 1]
+    return np.unique(rt[np.asarray(rows, np.int64)]).astype(np.int32) if rows else np.zeros(0, np.int32)
+
+
 def max_rel_err(y, ref) -> float:
     y = np.asarray(y, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -93,7 +119,8 @@ def check_output_topk(w: W.Workload, layer, inp, lg, toks):
                        given_logits=lg, toks=toks)
     y = host_float(layer.y)[toks]
     err = max_rel_err(y, ref.y)
-    say(f"  {w.name}: output max rel err {err:.3e} over {len(toks)} tokens (tol {TOL_Y[w.dtype]})")
+    say(f"  {w.name}: output max rel err {err:.3e} over {len(toks)} tokens (tol {TOL_Y[w.dtype]}); "
+        f"element-wise {elem_rel_err(y, ref.y):.3e} (floor 1e-3 max|ref|)")
     assert err <= TOL_Y[w.dtype]
     return err
 
@@ -138,6 +165,7 @@ def check_output_ec(w: W.Workload, layer, inp, lg, sc, toks):
                        ws1=inp["ws1"], ws2=inp["ws2"], given_logits=lg, given_scores=sc, toks=toks)
     y = host_float(layer.y)[toks]
     err = max_rel_err(y, ref.y)
-    say(f"  {w.name}: output max rel err {err:.3e} over {len(toks)} tokens (tol {TOL_Y[w.dtype]})")
+    say(f"  {w.name}: output max rel err {err:.3e} over {len(toks)} tokens (tol {TOL_Y[w.dtype]}); "
+        f"element-wise {elem_rel_err(y, ref.y):.3e} (floor 1e-3 max|ref|)")
     assert err <= TOL_Y[w.dtype]
     return err

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from _parity import (TOL_Y, check_output_ec, check_output_topk, check_routing_ec, check_routing_topk, host_float,
-                     inputs, max_rel_err, run_layer, sample_tokens, say)
+                     inputs, max_rel_err, run_layer, sample_tokens, say, tile_cover_tokens)
 from mixture_experts_layer_topkrouter_amd import moe
 from mixture_experts_layer_topkrouter_amd import workloads as W
 
@@ -85,10 +85,13 @@ def test_layer_parity_full_size(name):
     w = WL[name]
     say(f"[parity full] {name}: T={w.T} d={w.d} E={w.E} d_ff={w.d_ff}")
     layer, inp = run_layer(w)
+    # sampled tokens: random ones, plus the tokens of the first and last row
+    # of every (expert, row tile), so every tile of both GEMMs is checked
+    cover = tile_cover_tokens(w, layer)
     if w.routing == W.EXPERT_CHOICE:
         lg, sc, ec = check_routing_ec(w, layer, inp)
         uncovered = np.setdiff1d(np.arange(w.T), ec.ravel())[:2]
-        toks = sample_tokens(w, 12, extra=list(uncovered))
+        toks = sample_tokens(w, 12, extra=list(uncovered) + list(cover))
         check_output_ec(w, layer, inp, lg, sc, toks)
         if len(uncovered):
             y = host_float(layer.y)[uncovered]
@@ -98,7 +101,7 @@ def test_layer_parity_full_size(name):
         dropped = np.flatnonzero((d.slot_row < 0).any(1))[:3]
         hot = int(np.argmax(d.expert_count))
         on_hot = d.row_token[d.expert_offset[hot]:d.expert_offset[hot] + 2]
-        toks = sample_tokens(w, 12, extra=list(dropped) + list(on_hot))
+        toks = sample_tokens(w, 12, extra=list(dropped) + list(on_hot) + list(cover))
         check_output_topk(w, layer, inp, lg, toks)
 
 
