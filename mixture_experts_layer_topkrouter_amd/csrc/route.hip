@@ -546,58 +546,62 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
     for (int i = threadIdx.x; i < kEcBins; i += kEcThreads) hist[i] = 0;
     if (shift > 0) {
       // the keys of the threshold digit become the candidates of the next
-      // pass (in place when they already are candidates: a wave reads its
-      // keys before any lane writes, and writes land at or below them)
-      __syncthreads();
-      if (threadIdx.x == 0 && !first) ncand = 0;
-      __syncthreads();
-      for (int i0 = 0; i0 < n; i0 += kEcThreads) {
-        const int i = i0 + threadIdx.x;
-        const uint32_t kv = i < n ? src[i] : 0u;
-        const bool keep = i < n && ((kv >> shift) & dmask) == digit;
-        __syncthreads();
-        const uint64_t b = __ballot(keep);
-        int base = 0;
-        if (lane_id() == 0 && b) base = atomicAdd(&ncand, __popcll(b));
-        base = __shfl(base, 0, kWave);
-        if (keep) cand[base + __popcll(b & lanemask_lt())] = kv;
+      // pass: each thread reads a run of consecutive entries into registers,
+      // one block scan of the kept counts places them, then they are written
+      // (in place when they already are candidates: the scan's barriers put
+      // every read before any write)
+      constexpr int kPer = kEcMaxTokens / kEcThreads;
+      const int per = (n + kEcThreads - 1) / kEcThreads;  // <= kPer
+      const int b0 = min(n, static_cast<int>(threadIdx.x) * per), b1 = min(n, b0 + per);
+      uint32_t mine[kPer];
+      int kept = 0;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        mine[q] = b0 + q < b1 ? src[b0 + q] : 0u;
+        kept += (b0 + q < b1 && ((mine[q] >> shift) & dmask) == digit);
       }
+      int total;
+      int o = block_excl_scan(kept, scan_tmp, &total);
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (b0 + q < b1 && ((mine[q] >> shift) & dmask) == digit) cand[o++] = mine[q];
+      if (threadIdx.x == 0) ncand = total;
     }
     first = false;
     pos = shift;
     __syncthreads();
   }
   // prefix is the C-th largest key; `need` of the keys equal to it are taken
-  // (the lowest tokens), every key above it is taken.
+  // (the lowest tokens), every key above it is taken.  Each thread takes a
+  // run of consecutive tokens; one block scan of the packed pair (keys above,
+  // keys equal) gives every selected token its position: the keys above
+  // before it plus min(keys equal before it, need).
   const int per = (T + kEcThreads - 1) / kEcThreads;
   const int b0 = min(T, static_cast<int>(threadIdx.x) * per), b1 = min(T, b0 + per);
-  int n_eq = 0;
-  for (int t = b0; t < b1; ++t) n_eq += (key[t] == prefix);
-  int tot;
-  int eq_rank = block_excl_scan(n_eq, scan_tmp, &tot);
-  int n_sel = 0;
-  {
-    int er = eq_rank;
-    for (int t = b0; t < b1; ++t) {
-      const uint32_t kv = key[t];
-      if (kv > prefix) ++n_sel;
-      else if (kv == prefix) { if (er < need) ++n_sel; ++er; }
-    }
+  int n_gt = 0, n_eq = 0;
+  for (int t = b0; t < b1; ++t) {
+    const uint32_t kv = key[t];
+    n_gt += kv > prefix;
+    n_eq += kv == prefix;
   }
-  int p = block_excl_scan(n_sel, scan_tmp, &tot);
-  {
-    int er = eq_rank;
-    for (int t = b0; t < b1; ++t) {
-      const uint32_t kv = key[t];
-      bool take = false;
-      if (kv > prefix) take = true;
-      else if (kv == prefix) { take = er < need; ++er; }
-      if (take) {
-        ec_token[(int64_t)e * C + p] = t;
-        ec_w[(int64_t)e * C + p] = __uint_as_float(kv);
-        ++p;
-      }
+  int tot;
+  const int packed = block_excl_scan((n_gt << 16) | n_eq, scan_tmp, &tot);  // T <= 16384 < 2^16
+  int gt = packed >> 16, eq = packed & 0xffff;
+  for (int t = b0; t < b1; ++t) {
+    const uint32_t kv = key[t];
+    bool take = false;
+    if (kv > prefix) {
+      take = true;
+    } else if (kv == prefix) {
+      take = eq < need;
+      ++eq;
     }
+    if (take) {
+      const int p = gt + min(eq - (kv == prefix ? 1 : 0), need);
+      ec_token[(int64_t)e * C + p] = t;
+      ec_w[(int64_t)e * C + p] = __uint_as_float(kv);
+    }
+    if (kv > prefix) ++gt;
   }
 }
 
