@@ -83,23 +83,17 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 // exclusive prefix; *total gets the block sum.
 __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
   const int nw = blockDim.x / kWave;
-  int inc = wave_incl_scan(v);
+  const int inc = wave_incl_scan(v);
   if (lane_id() == kWave - 1) tmp[wave_id()] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) {
-      int c = tmp[w];
-      tmp[w] = run;
-      run += c;
-    }
-    tmp[nw] = run;
-  }
-  __syncthreads();
-  int r = tmp[wave_id()] + inc - v;
-  *total = tmp[nw];
-  __syncthreads();
-  return r;
+  // every wave scans the per-wave totals itself (lane w holds wave w's)
+  const int l = lane_id();
+  const int wt = l < nw ? tmp[l] : 0;
+  const int wi = wave_incl_scan(wt);
+  const int before = __builtin_amdgcn_readlane(wi - wt, __builtin_amdgcn_readfirstlane(wave_id()));
+  *total = __builtin_amdgcn_readlane(wi, nw - 1);
+  __syncthreads();  // tmp may be reused at once
+  return before + inc - v;
 }
 
 // the direct-to-LDS loads name M0, which the compiler reserves (it uses M0

@@ -440,59 +440,107 @@ constexpr int kEcThreads = 1024;
 // The expert's score row is contiguous (expert-major scores) and is read
 // once into LDS as 32-bit keys; scores are >= 0, so their bit patterns order
 // like the values.  The C-th largest key is found by a radix select from the
-// top: the bits every key shares (block-wide AND and OR of the keys) are
-// taken at once, then up to 11 bits per pass.  The first pass histograms
-// every key; the keys of its threshold digit are then copied to a candidate
-// list (keys above it are selected outright), so the later passes only see
-// those.  Finally the tokens whose key is above the threshold, and the
-// lowest tokens whose key equals it, are compacted in ascending token order.
+// top, up to 11 bits per pass.  While the row is read, every key already
+// goes into the histogram of bits [19, 30) (the first digit when every key
+// is below 2.0, i.e. bit 30 and up are clear, as for softmax scores, and
+// the keys differ in a bit at or above 22); otherwise the bits every key
+// shares (block-wide AND and OR) are skipped and the first digit is
+// histogrammed again below them.  The keys of the first pass's threshold
+// digit are copied to a candidate list (keys above it are selected
+// outright), in any order, since the later passes only count them; those
+// passes, over the candidates only, run in wave 0 alone (no workgroup
+// barriers) while the list fits kEcWaveCand entries.
+// Finally the tokens whose key is above the threshold, and the lowest tokens
+// whose key equals it, are compacted in ascending token order.
 constexpr int kEcDigitBits = 11;
 constexpr int kEcBins = 1 << kEcDigitBits;
+constexpr int kEcFusedShift = 19;      // the histogram taken while reading: bits [19, 30)
+constexpr int kEcWaveCand = 4096;      // later passes in one wave up to this many candidates
 
-// The digit (of `bins` bins, histogram in LDS) that holds the need-th
-// largest key, searched from the top by wave 0: lane l holds the 32 bins
-// bins-1-32l .. bins-32-32l.  Writes the digit and the rank of the wanted key
-// inside it to state[0], state[1].
-__device__ __forceinline__ void ec_find_digit(const int *hist, int need, uint32_t *state) {
+// The digit (histogram of kEcBins bins in LDS) that holds the need-th
+// largest key, found by one wave from the top: lane l first sums the 32 bins
+// bins-1-32l .. bins-32-32l (eight 16-B reads), a wave scan of the sums
+// picks the lane whose group holds it, then lane q (< 32) takes bin
+// bins-1-32src-q of that group and a second scan picks the bin.  Returns the
+// digit and the rank of the wanted key inside it (every lane).
+__device__ __forceinline__ void ec_find_digit(const int *hist, int need, int *digit, int *rank) {
   const int l = lane_id();
+  const int lo = kEcBins - 32 * (l + 1);  // this lane's group: bins lo .. lo+31
   int sum = 0;
-  for (int q = 0; q < 32; ++q) sum += hist[kEcBins - 1 - (32 * l + q)];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int4 v = *reinterpret_cast<const int4 *>(hist + lo + 4 * q);
+    sum += v.x + v.y + v.z + v.w;
+  }
   const int incl = wave_incl_scan(sum);
   const int excl = incl - sum;
   const uint64_t hit = __ballot(excl < need && need <= incl);
   const int src = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave - 1;
-  if (l == src) {
-    int cum = excl, q = 0;
-    for (; q < 31; ++q) {
-      const int h = hist[kEcBins - 1 - (32 * l + q)];
-      if (cum + h >= need) break;
-      cum += h;
+  const int base = __builtin_amdgcn_readlane(excl, src);
+  const int bin = kEcBins - 1 - 32 * src - l;  // lanes 0..31: the group's bins from the top
+  const int h = l < 32 ? hist[bin] : 0;
+  const int c = wave_incl_scan(h) + base;
+  const uint64_t hit2 = __ballot(l < 32 && c - h < need && need <= c);
+  const int q = hit2 ? __ffsll(static_cast<unsigned long long>(hit2)) - 1 : 31;
+  *digit = __builtin_amdgcn_readlane(bin, q);
+  *rank = need - __builtin_amdgcn_readlane(c - h, q);
+}
+
+// Thread i's run of entries [b0, b1) of src[0, n), runs of a multiple of 4
+// entries (at most kEcPer), read with 16-B LDS loads into v (entries past
+// the run hold whatever follows in the array, which the kEcMaxTokens bound
+// keeps inside it).
+constexpr int kEcPer = kEcMaxTokens / kEcThreads;
+static_assert(kEcPer % 4 == 0, "runs of whole 16-B loads");
+__device__ __forceinline__ void load_run(const uint32_t *src, int n, uint32_t (&v)[kEcPer], int *b0, int *b1) {
+  const int per = ((n + kEcThreads - 1) / kEcThreads + 3) & ~3;
+  *b0 = min(n, static_cast<int>(threadIdx.x) * per);
+  *b1 = min(n, *b0 + per);
+  const int at = static_cast<int>(threadIdx.x) * per;  // at + per <= kEcMaxTokens
+#pragma unroll
+  for (int q = 0; q < kEcPer; q += 4) {
+    if (q < per) {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(src + at + q);
+      v[q] = w[0];
+      v[q + 1] = w[1];
+      v[q + 2] = w[2];
+      v[q + 3] = w[3];
+    } else {
+      v[q] = v[q + 1] = v[q + 2] = v[q + 3] = 0u;
     }
-    state[0] = static_cast<uint32_t>(kEcBins - 1 - (32 * l + q));
-    state[1] = static_cast<uint32_t>(need - cum);
   }
 }
+
+// LDS operations of one wave complete in order; this makes the compiler keep
+// them in order too and waits for them (a wave-only "barrier").
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__restrict__ scores, int T,
                                                                int E, int C, int32_t *__restrict__ ec_token,
                                                                float *__restrict__ ec_w) {
-  __shared__ uint32_t key[kEcMaxTokens];
-  __shared__ uint32_t cand[kEcMaxTokens];
-  __shared__ int hist[kEcBins];
+  __shared__ __attribute__((aligned(16))) uint32_t key[kEcMaxTokens];
+  __shared__ __attribute__((aligned(16))) uint32_t cand[kEcMaxTokens];
+  __shared__ __attribute__((aligned(16))) int hist[kEcBins];
   __shared__ int scan_tmp[kEcThreads / kWave + 1];
   __shared__ uint32_t red[2][kEcThreads / kWave];
-  __shared__ uint32_t sel_state[2];
+  __shared__ uint32_t sel_state[3];
   __shared__ int ncand;
   const int e = blockIdx.x;
   const int nw = kEcThreads / kWave;
   const float *row = scores + (int64_t)e * T;
+  for (int i = threadIdx.x; i < kEcBins; i += kEcThreads) hist[i] = 0;
+  if (threadIdx.x == 0) ncand = 0;
+  __syncthreads();  // the histogram is clear before the first key goes in
   uint32_t kand = ~0u, kor = 0u;
+  constexpr uint32_t kFusedMask = kEcBins - 1;
   if ((T & 3) == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
     for (int i = threadIdx.x; i < T / 4; i += kEcThreads) {
       const u32x4 v = *reinterpret_cast<const u32x4 *>(row + 4 * i);
       *reinterpret_cast<u32x4 *>(key + 4 * i) = v;
       kand &= v[0] & v[1] & v[2] & v[3];
       kor |= v[0] | v[1] | v[2] | v[3];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) atomicAdd(&hist[(v[q] >> kEcFusedShift) & kFusedMask], 1);
     }
   } else {
     for (int t = threadIdx.x; t < T; t += kEcThreads) {
@@ -500,10 +548,9 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
       key[t] = v;
       kand &= v;
       kor |= v;
+      atomicAdd(&hist[(v >> kEcFusedShift) & kFusedMask], 1);
     }
   }
-  for (int i = threadIdx.x; i < kEcBins; i += kEcThreads) hist[i] = 0;
-  if (threadIdx.x == 0) ncand = 0;
   // block-wide AND / OR (exact in any order)
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -524,84 +571,176 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float *__re
   const uint32_t diff = kand ^ kor;  // bits where keys differ
   // bits at and above `pos` are shared by every key (and already in `prefix`)
   int pos = diff ? 32 - __clz(static_cast<int>(diff)) : 0;
+  const bool fused = (kor >> (kEcFusedShift + kEcDigitBits)) == 0 && pos > kEcFusedShift + 3;
+  if (fused) pos = kEcFusedShift + kEcDigitBits;
   uint32_t prefix = pos >= 32 ? 0u : (kand >> pos) << pos;
   int need = C;  // rank (1-based, from the top) of the wanted key among those matching the prefix
-  bool first = true;
-  while (pos > 0) {
+  if (!fused) {
+    for (int i = threadIdx.x; i < kEcBins; i += kEcThreads) hist[i] = 0;
+    __syncthreads();
+  }
+  // first pass over every key (its histogram already taken when fused)
+  if (pos > 0) {
     const int wbits = pos < kEcDigitBits ? pos : kEcDigitBits;
     const int shift = pos - wbits;
     const uint32_t dmask = (1u << wbits) - 1u;
-    // histogram of the digit: every key in the first pass (they all share
-    // the bits above pos), the candidates afterwards (integer LDS adds,
-    // order-independent)
-    const uint32_t *src = first ? key : cand;
-    const int n = first ? T : ncand;
-    for (int i = threadIdx.x; i < n; i += kEcThreads) atomicAdd(&hist[(src[i] >> shift) & dmask], 1);
-    __syncthreads();
-    if (wave_id() == 0) ec_find_digit(hist, need, sel_state);
+    if (!fused) {
+      for (int i = threadIdx.x; i < T; i += kEcThreads) atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
+      __syncthreads();
+    }
+    if (wave_id() == 0) {
+      int digit, rank;
+      ec_find_digit(hist, need, &digit, &rank);
+      if (lane_id() == 0) {
+        sel_state[0] = static_cast<uint32_t>(digit);
+        sel_state[1] = static_cast<uint32_t>(rank);
+      }
+    }
     __syncthreads();
     const uint32_t digit = sel_state[0];
     need = static_cast<int>(sel_state[1]);
     prefix |= digit << shift;
     for (int i = threadIdx.x; i < kEcBins; i += kEcThreads) hist[i] = 0;
     if (shift > 0) {
-      // the keys of the threshold digit become the candidates of the next
-      // pass: each thread reads a run of consecutive entries into registers,
-      // one block scan of the kept counts places them, then they are written
-      // (in place when they already are candidates: the scan's barriers put
-      // every read before any write)
-      constexpr int kPer = kEcMaxTokens / kEcThreads;
-      const int per = (n + kEcThreads - 1) / kEcThreads;  // <= kPer
-      const int b0 = min(n, static_cast<int>(threadIdx.x) * per), b1 = min(n, b0 + per);
-      uint32_t mine[kPer];
-      int kept = 0;
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        mine[q] = b0 + q < b1 ? src[b0 + q] : 0u;
-        kept += (b0 + q < b1 && ((mine[q] >> shift) & dmask) == digit);
+      // the keys of the threshold digit become the candidates, in any order
+      // (the later passes only count them): each wave appends its kept keys
+      // at a place taken with one LDS atomic
+      for (int i0 = 0; i0 < T; i0 += kEcThreads) {
+        const int i = i0 + static_cast<int>(threadIdx.x);
+        const uint32_t kv = i < T ? key[i] : 0u;
+        const bool keep = i < T && ((kv >> shift) & dmask) == digit;
+        const uint64_t b = __ballot(keep);
+        if (b) {
+          int base = 0;
+          if (lane_id() == 0) base = atomicAdd(&ncand, __popcll(b));
+          base = __shfl(base, 0, kWave);
+          if (keep) cand[base + __popcll(b & lanemask_lt())] = kv;
+        }
       }
-      int total;
-      int o = block_excl_scan(kept, scan_tmp, &total);
-#pragma unroll
-      for (int q = 0; q < kPer; ++q)
-        if (b0 + q < b1 && ((mine[q] >> shift) & dmask) == digit) cand[o++] = mine[q];
-      if (threadIdx.x == 0) ncand = total;
     }
-    first = false;
     pos = shift;
     __syncthreads();
+  }
+  // later passes over the candidates
+  const int n0 = ncand;
+  if (pos > 0 && n0 <= kEcWaveCand) {
+    // wave 0 alone: LDS histogram, digit search and in-place compaction
+    // (chunks of 64 in order: a chunk's writes land at or below its reads)
+    if (wave_id() == 0) {
+      const int l = lane_id();
+      int n = n0;
+      while (pos > 0) {
+        const int wbits = pos < kEcDigitBits ? pos : kEcDigitBits;
+        const int shift = pos - wbits;
+        const uint32_t dmask = (1u << wbits) - 1u;
+        for (int i = l; i < n; i += kWave) atomicAdd(&hist[(cand[i] >> shift) & dmask], 1);
+        wave_lds_sync();
+        int digit, rank;
+        ec_find_digit(hist, need, &digit, &rank);
+        need = rank;
+        prefix |= static_cast<uint32_t>(digit) << shift;
+        wave_lds_sync();
+        for (int i = l; i < n; i += kWave) hist[(cand[i] >> shift) & dmask] = 0;  // only the bins used
+        if (shift > 0) {
+          int o = 0;
+          for (int i0 = 0; i0 < n; i0 += kWave) {
+            const int i = i0 + l;
+            const uint32_t kv = i < n ? cand[i] : 0u;
+            const bool keep = i < n && ((kv >> shift) & dmask) == static_cast<uint32_t>(digit);
+            const uint64_t b = __ballot(keep);
+            wave_lds_sync();  // every lane has read its entry before any writes
+            if (keep) cand[o + __popcll(b & lanemask_lt())] = kv;
+            o += __popcll(b);
+          }
+          n = o;
+        }
+        wave_lds_sync();
+        pos = shift;
+      }
+      if (l == 0) {
+        sel_state[1] = static_cast<uint32_t>(need);
+        sel_state[2] = prefix;
+      }
+    }
+    __syncthreads();
+    need = static_cast<int>(sel_state[1]);
+    prefix = sel_state[2];
+  } else {
+    bool first = true;
+    while (pos > 0) {
+      const int wbits = pos < kEcDigitBits ? pos : kEcDigitBits;
+      const int shift = pos - wbits;
+      const uint32_t dmask = (1u << wbits) - 1u;
+      const int n = first ? n0 : ncand;
+      for (int i = threadIdx.x; i < n; i += kEcThreads) atomicAdd(&hist[(cand[i] >> shift) & dmask], 1);
+      __syncthreads();
+      if (wave_id() == 0) {
+        int digit, rank;
+        ec_find_digit(hist, need, &digit, &rank);
+        if (lane_id() == 0) {
+          sel_state[0] = static_cast<uint32_t>(digit);
+          sel_state[1] = static_cast<uint32_t>(rank);
+        }
+      }
+      __syncthreads();
+      const uint32_t digit = sel_state[0];
+      need = static_cast<int>(sel_state[1]);
+      prefix |= digit << shift;
+      for (int i = threadIdx.x; i < kEcBins; i += kEcThreads) hist[i] = 0;
+      if (shift > 0) {
+        // in place: the scan's barriers put every read before any write
+        uint32_t mine[kEcPer];
+        int b0, b1;
+        load_run(cand, n, mine, &b0, &b1);
+        int kept = 0;
+#pragma unroll
+        for (int q = 0; q < kEcPer; ++q) kept += (b0 + q < b1 && ((mine[q] >> shift) & dmask) == digit);
+        int total;
+        int o = block_excl_scan(kept, scan_tmp, &total);
+#pragma unroll
+        for (int q = 0; q < kEcPer; ++q)
+          if (b0 + q < b1 && ((mine[q] >> shift) & dmask) == digit) cand[o++] = mine[q];
+        if (threadIdx.x == 0) ncand = total;
+      }
+      first = false;
+      pos = shift;
+      __syncthreads();
+    }
   }
   // prefix is the C-th largest key; `need` of the keys equal to it are taken
   // (the lowest tokens), every key above it is taken.  Each thread takes a
   // run of consecutive tokens; one block scan of the packed pair (keys above,
   // keys equal) gives every selected token its position: the keys above
   // before it plus min(keys equal before it, need).
-  const int per = (T + kEcThreads - 1) / kEcThreads;
-  const int b0 = min(T, static_cast<int>(threadIdx.x) * per), b1 = min(T, b0 + per);
+  uint32_t mine[kEcPer];
+  int b0, b1;
+  load_run(key, T, mine, &b0, &b1);
   int n_gt = 0, n_eq = 0;
-  for (int t = b0; t < b1; ++t) {
-    const uint32_t kv = key[t];
-    n_gt += kv > prefix;
-    n_eq += kv == prefix;
+#pragma unroll
+  for (int q = 0; q < kEcPer; ++q) {
+    n_gt += b0 + q < b1 && mine[q] > prefix;
+    n_eq += b0 + q < b1 && mine[q] == prefix;
   }
   int tot;
   const int packed = block_excl_scan((n_gt << 16) | n_eq, scan_tmp, &tot);  // T <= 16384 < 2^16
   int gt = packed >> 16, eq = packed & 0xffff;
-  for (int t = b0; t < b1; ++t) {
-    const uint32_t kv = key[t];
-    bool take = false;
+#pragma unroll
+  for (int q = 0; q < kEcPer; ++q) {
+    if (b0 + q >= b1) break;
+    const uint32_t kv = mine[q];
     if (kv > prefix) {
-      take = true;
+      const int p = gt + min(eq, need);
+      ec_token[(int64_t)e * C + p] = b0 + q;
+      ec_w[(int64_t)e * C + p] = __uint_as_float(kv);
+      ++gt;
     } else if (kv == prefix) {
-      take = eq < need;
+      if (eq < need) {
+        const int p = gt + eq;
+        ec_token[(int64_t)e * C + p] = b0 + q;
+        ec_w[(int64_t)e * C + p] = __uint_as_float(kv);
+      }
       ++eq;
     }
-    if (take) {
-      const int p = gt + min(eq - (kv == prefix ? 1 : 0), need);
-      ec_token[(int64_t)e * C + p] = t;
-      ec_w[(int64_t)e * C + p] = __uint_as_float(kv);
-    }
-    if (kv > prefix) ++gt;
   }
 }
 

@@ -194,6 +194,8 @@ def test_gate_tie_heavy_logits_match_oracle(E, k, mode):
     (4000, 16, 4000, (-1.0, 0.0, 1.0)),                 # C = T: every token
     (16384, 128, 2, (0.0, 0.25, 0.5)),                  # the largest T, tiny C
     (300, 5, 299, (-3.0, 2.0)),                         # two score levels, C one short of T
+    (16384, 2, 8000, (-5.0, 0.0)),                      # > 4096 keys share the first digit's threshold bin
+    (4096, 48, 100, (0.0, 1e-3, 2e-3, 3e-3)),           # keys share their top 15 bits: digits start lower
 ])
 def test_expert_choice_selection_ties_match_oracle(T, E, C, vals):
     """ExpertChoice selection on given fp32 logits with heavy ties: the
