@@ -71,7 +71,18 @@ def parse():
                          "after the headline's timed regions)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (calibrates HBM byte counters)")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="only the launches a profiler's HBM byte counters are read from: one step through the "
+                         "stage entry points, then each stage again (3 calls of each in all, 5 of the shared "
+                         "expert FFN), then one 1-GiB copy through the library's copy kernel for calibration")
     return ap.parse_args()
+
+
+# Calls of each stage in a --traffic-run (the first within one whole step);
+# the routed and the shared expert FFN run the same kernels, so their counts
+# differ (3 against 5) to tell their dispatches apart.
+TRAFFIC_CALLS = {"route": 3, "permute": 3, "expert_ffn": 3, "shared_ffn": 5, "unpermute": 3}
+TRAFFIC_COPY_BYTES = 1 << 30
 
 
 def algorithmic(w, n_rows: int, n_active: int, t_used: int = None):
@@ -101,28 +112,38 @@ def algorithmic(w, n_rows: int, n_active: int, t_used: int = None):
     return out
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per expert-FFN launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (scaled by a plain-copy calibration), or None when no such
-    measurement exists or the GEMM sources have changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_ffn_traffic.json")
+def measured_traffic(workload: str, stage: str = "expert_ffn"):
+    """HBM bytes (read + written) per call of a stage from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (each scaled by a plain-copy
+    calibration), or None when no such measurement exists or the stage's
+    kernel sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
-    if gemm_sources_sha256() != rec.get("gemm_source_sha256"):
+        rec = json.load(f).get("stages", {}).get(stage)
+    if rec is None or stage_sources_sha256(stage) != rec.get("sources_sha256"):
         return None
-    return int(rec["traffic_bytes_per_launch"])
+    return int(rec["read_bytes"] + rec["write_bytes"])
 
 
-GEMM_SOURCES = ("gemm_common.h", "gemm.hip", "gemm_skinny.hip")
+# The kernel sources of each stage (with the shared device helpers).
+COMMON_SOURCES = ("common.h", "kernels.h")
+STAGE_SOURCES = {
+    "route": ("route.hip",),
+    "permute": ("permute.hip",),
+    "expert_ffn": ("gemm_common.h", "gemm.hip", "gemm_skinny.hip"),
+    "shared_ffn": ("gemm_common.h", "gemm.hip", "gemm_skinny.hip"),
+    "unpermute": ("combine.hip",),
+}
 
 
-def gemm_sources_sha256() -> str:
-    """One hash over the grouped-GEMM sources, in a fixed order."""
+def stage_sources_sha256(stage: str) -> str:
+    """One hash over a stage's kernel sources and the shared helpers, in a
+    fixed order."""
     import hashlib
     h = hashlib.sha256()
-    for name in GEMM_SOURCES:
+    for name in STAGE_SOURCES[stage] + COMMON_SOURCES:
         with open(os.path.join(ROOT, "mixture_experts_layer_topkrouter_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -198,6 +219,20 @@ def kept_counts(w, layer, W):
     return n_rows, n_active, t_used
 
 
+def add_traffic(ent, w, n, work, sec):
+    """The stage's measured HBM bytes per call (profiler counters, while its
+    sources are unchanged), their rate and their ratio to the algorithmic
+    bytes."""
+    tb = measured_traffic(w.name, n)
+    if tb is None:
+        return
+    alg = work[n][1] if work[n][0] == "bytes" else (work[n][2] if len(work[n]) > 2 else None)
+    ent["traffic_bytes"] = tb
+    ent["traffic_GB/s"] = round(tb / sec / 1e9, 1)
+    if alg:
+        ent["traffic_vs_algorithmic"] = round(tb / alg, 3)
+
+
 def stage_rates(w, work, ms, peak_flops, peak_hbm):
     """Per-stage algorithmic rates from stage durations (ms)."""
     out = {}
@@ -214,6 +249,7 @@ def stage_rates(w, work, ms, peak_flops, peak_hbm):
             if len(work[n]) > 2:
                 ent["GB/s"] = round(work[n][2] / sec / 1e9, 1)
                 ent["hbm_frac"] = round(work[n][2] / sec / 1e9 / peak_hbm, 4)
+        add_traffic(ent, w, n, work, sec)
         out[n] = ent
     return out
 
@@ -315,6 +351,29 @@ def main():
             fn()
         if ev is not None:
             ev[len(fns)].record(stream)
+
+    if args.traffic_run:
+        # launches for a profiler's HBM byte counters: one step, then every
+        # stage on its own until it has run TRAFFIC_CALLS times, then a known
+        # copy through the library's stream kernel
+        step()
+        for n, fn in zip(names, fns):
+            for _ in range(TRAFFIC_CALLS[n] - 1):
+                fn()
+        a = torch.ones(TRAFFIC_COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        moe.stream_probe("copy", a, b, TRAFFIC_COPY_BYTES)
+        torch.cuda.synchronize()
+        n_rows, n_active, t_used = kept_counts(w, layer, W)
+        work = algorithmic(w, n_rows, n_active, t_used)
+        print(json.dumps({"traffic_run": w.name, "calls": {n: TRAFFIC_CALLS[n] for n in names},
+                          "copy_bytes": TRAFFIC_COPY_BYTES,
+                          "algorithmic_bytes": {n: int(work[n][2] if work[n][0] == "flops" and len(work[n]) > 2
+                                                       else work[n][1]) for n in names if
+                                                work[n][0] == "bytes" or len(work[n]) > 2},
+                          "sources_sha256": {n: stage_sources_sha256(n) for n in names}}), flush=True)
+        return
 
     # The headline: K calls of moe_layer_fwd (the whole layer, shared expert
     # overlapped on its side stream), between two synchronisations.
@@ -506,6 +565,7 @@ def main():
                 ent["min_bytes"] = int(work[n][2])
                 ent["GB/s"] = round(work[n][2] / sec / 1e9, 1)
                 ent["hbm_frac"] = round(work[n][2] / sec / 1e9 / PEAK_HBM_GBS, 4)
+        add_traffic(ent, w, n, work, sec)
         stages[n] = ent
 
     if bwd is not None:

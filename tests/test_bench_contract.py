@@ -33,14 +33,24 @@ def test_algorithmic_work_of_the_mixtral_slice():
     assert work["unpermute"][1] == 8192 * 4096 * 2 + 4096 * 4096 * 2 + 8192 * 8
 
 
-def test_traffic_records_are_keyed_to_the_gemm_sources():
-    """A record counts only while the grouped-GEMM sources hash to the value it
-    was measured with; otherwise bench.py reports traffic as null."""
-    for name in ("mixtral_top2_bf16", "mixtral_decode_bf16"):
-        with open(os.path.join(ROOT, "profiles", f"{name}_ffn_traffic.json")) as f:
+def test_traffic_records_are_keyed_to_the_stage_sources(monkeypatch):
+    """A stage's counter record counts only while that stage's kernel sources
+    hash to the value it was measured with; otherwise bench.py reports its
+    traffic as null."""
+    import glob
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.json")))
+    assert paths, "no HBM traffic records under profiles/"
+    for path in paths:
+        name = os.path.basename(path)[:-len("_hbm_traffic.json")]
+        with open(path) as f:
             rec = json.load(f)
-        assert rec["traffic_bytes_per_launch"] > 0 and len(rec["gemm_source_sha256"]) == 64
-        fresh = rec["gemm_source_sha256"] == bench.gemm_sources_sha256()
-        expect = int(rec["traffic_bytes_per_launch"]) if fresh else None
-        assert bench.measured_traffic(name) == expect
+        assert rec["copy_probe"]["bytes"] > 0
+        for stage, st in rec["stages"].items():
+            assert st["read_bytes"] >= 0 and st["write_bytes"] >= 0 and len(st["sources_sha256"]) == 64
+            fresh = st["sources_sha256"] == bench.stage_sources_sha256(stage)
+            expect = int(st["read_bytes"] + st["write_bytes"]) if fresh else None
+            assert bench.measured_traffic(name, stage) == expect
+        monkeypatch.setattr(bench, "stage_sources_sha256", lambda stage: "0" * 64)
+        assert all(bench.measured_traffic(name, stage) is None for stage in rec["stages"])
+        monkeypatch.undo()
     assert bench.measured_traffic("no_such_workload") is None
