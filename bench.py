@@ -496,7 +496,7 @@ def main():
 
     # Practical HBM stream rates of this device, for reading the HBM-bound
     # stages against: the library's own read, write and copy kernels
-    # (moe_stream_probe: 16-B accesses, 32 waves per CU), plain and
+    # (moe_stream_probe: 16-B accesses, one 16-KB run per 256-thread workgroup), plain and
     # non-temporal, each over 1 GiB, median of 5 event-timed runs.
     hbm_probe = None
     if args.hbm_probe:
@@ -519,7 +519,7 @@ def main():
                 ts.append(a.elapsed_time(b))
             return round(moved / (float(np.median(ts)) / 1e3) / 1e9, 1)
 
-        hbm_probe = {"bytes": nbytes, "kernel": "moe_stream_probe (16-B accesses, 2048 x 256 threads)"}
+        hbm_probe = {"bytes": nbytes, "kernel": "moe_stream_probe (16-B accesses, one 16-KB run per 256-thread workgroup)"}
         for nt in (False, True):
             tag = "_nt" if nt else ""
             hbm_probe["read" + tag + "_GB/s"] = rate("read", nt, nbytes)
