@@ -24,7 +24,8 @@ backward pass for a seeded upstream gradient) in a region of its own after
 the forward regions, in both modes: after a plain forward with the expert
 pre-activations recomputed, and after the training forward that keeps them
 (whose time is reported as ``train_fwd_ms``).  ``hbm_probe`` gives the
-device's read, write and copy rates from the library's own stream kernels.
+device's read, write and copy rates from the library's own stream kernels, and
+the bf16 MFMA rate of a register-only loop (random and constant operands).
 ``workloads`` then measures every other workload the same way (median layer
 time, tokens/s, stage medians with their algorithmic rates, the FFN's
 roofline fraction), after the headline's timed regions.
@@ -526,6 +527,32 @@ def main():
             hbm_probe["write" + tag + "_GB/s"] = rate("write", nt, nbytes)
             hbm_probe["copy" + tag + "_GB/s"] = rate("copy", nt, 2 * nbytes)
         del src, dst
+        # the bf16 MFMA rate of a register-only loop (moe_mfma_probe: no
+        # memory traffic), on random operands and on constant ones: the
+        # matrix core's power, and so the clock it holds, depends on the data
+        blocks, iters = 512, 4096
+        flops = blocks * 4 * iters * 8 * 32768
+        g = torch.Generator(device="cuda").manual_seed(7)
+        ops = {"random": torch.randn(blocks * 16384, device="cuda", generator=g).to(torch.bfloat16),
+               "constant": torch.full((blocks * 16384,), 0.5, dtype=torch.bfloat16, device="cuda")}
+        mfma = {"kernel": "moe_mfma_probe (8 independent 32x32x16 bf16 MFMA accumulators per wave, 4 waves x "
+                          f"{blocks} workgroups, {iters} rounds)", "flops": flops}
+        for name, op in ops.items():
+            moe.mfma_probe(blocks, iters, op)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                moe.mfma_probe(blocks, iters, op)
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            tf = flops / (float(np.median(ts)) / 1e3) / 1e12
+            mfma[name + "_TFLOP/s"] = round(tf, 1)
+            mfma[name + "_frac_of_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+        hbm_probe["mfma"] = mfma
+        del ops
 
     if args.copy_probe_mib:
         # one known-size copy through the library's copy kernel (calibrates

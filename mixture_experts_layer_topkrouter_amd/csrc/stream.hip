@@ -1,3 +1,5 @@
+// Measurement kernels (include/moe_probe.h).
+//
 // HBM stream kernels: a plain read, write and copy of a device buffer.  They
 // measure the rates the device sustains for the access patterns of the
 // HBM-bound stages (route, permute and combine are reads, writes or both of
@@ -57,8 +59,56 @@ __global__ __launch_bounds__(kStreamThreads) void stream_kernel(const u32x4 *__r
   if (KIND == 0 && acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u && sink) sink[0] = acc[2];
 }
 
+// Register-only matrix-core loop: wave w of workgroup b loads 8 fragments
+// (16 B per lane each) from operands, then runs iters rounds of 8 MFMAs into
+// 8 independent accumulators (a 128 x 64 block of 32 x 32 tiles; each
+// accumulator is reused every 8 MFMAs, far past the MFMA's latency).
+__global__ __launch_bounds__(256) void mfma_probe_kernel(const u32x4 *__restrict__ ops, int iters,
+                                                         float *__restrict__ sink) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  const u32x4 *src = ops + static_cast<size_t>(wave) * 8 * kWave + l;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 va = src[i * kWave], vb = src[(4 + i) * kWave];
+    a[i] = __builtin_bit_cast(bf16x8, va);
+    b[i] = __builtin_bit_cast(bf16x8, vb);
+  }
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[(it & 1) * 2 + j], acc[i][j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+  if (s == 1234.5678f && sink) sink[wave] = s;
+}
+
 }  // namespace
 }  // namespace moe
+
+extern "C" moe_status moe_mfma_probe(int32_t blocks, int32_t iters, const void *operands, void *sink,
+                                     void *stream) {
+  if (blocks <= 0 || iters <= 0 || !operands || (reinterpret_cast<uintptr_t>(operands) & 15))
+    return MOE_ERR_INVALID_ARG;
+  moe::mfma_probe_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const moe::u32x4 *>(operands), iters, static_cast<float *>(sink));
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
 
 extern "C" moe_status moe_stream_probe(int32_t kind, int32_t nontemporal, const void *src, void *dst,
                                        size_t bytes, void *sink, void *stream) {

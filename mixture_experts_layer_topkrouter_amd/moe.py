@@ -109,6 +109,7 @@ def load_library() -> ctypes.CDLL:
         "moe_layer_fwd_train": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_layer_bwd": ([CP, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, ctypes.c_int32, P, sz, P], ctypes.c_int),
         "moe_stream_probe": ([ctypes.c_int32, ctypes.c_int32, P, P, sz, P, P], ctypes.c_int),
+        "moe_mfma_probe": ([ctypes.c_int32, ctypes.c_int32, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -334,6 +335,15 @@ def stream_probe(kind: str, src, dst, nbytes: int, nontemporal: bool = False, si
     _check(load_library().moe_stream_probe(k, int(bool(nontemporal)), _arg(src, "src", None, 0),
                                            _arg(dst, "dst", None, 0), nbytes, _arg(sink, "sink", None, 0),
                                            _stream(stream)), "moe_stream_probe")
+
+
+def mfma_probe(blocks: int, iters: int, operands, sink=None, stream=None):
+    """moe_mfma_probe: a register-only bf16 MFMA loop (include/moe_probe.h);
+    operands: a bf16 device tensor of at least blocks * 16384 elements."""
+    if operands.numel() * operands.element_size() < blocks * 32768:
+        raise ValueError("operands: blocks * 32 KB needed")
+    _check(load_library().moe_mfma_probe(int(blocks), int(iters), _arg(operands, "operands", None, 0),
+                                         _arg(sink, "sink", None, 0), _stream(stream)), "moe_mfma_probe")
 
 
 # ------------------------------------------------ allocation conveniences --
