@@ -35,8 +35,8 @@ moe_status moe_stream_probe(int32_t kind, int32_t nontemporal, const void *src, 
  * matrix core's power and so the clock depend on the data), then issues
  * `iters` rounds of 8 v_mfma_f32_32x32x16_bf16 into 8 independent
  * accumulators (a 128 x 64 block of 32 x 32 tiles; the B operands of
- * alternate rounds differ) and nothing else.  Flops = blocks * 4 * iters *
- * 8 * 32768.  The accumulators
+ * alternate rounds differ) and nothing else; iters is rounded up to an
+ * even count.  Flops = blocks * 4 * iters * 8 * 32768.  The accumulators
  * are summed into one float per wave and written to sink only if that sum
  * is a fixed improbable value (sink may then be NULL).  blocks and iters
  * must be positive and operands 16-byte aligned (else MOE_ERR_INVALID_ARG);

@@ -81,12 +81,17 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(const u32x4 *__restrict
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  for (int it = 0; it < iters; ++it) {
+  // two rounds per trip, the second on the other two B fragments
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[(it & 1) * 2 + j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[2 + j], acc[i][j], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll

@@ -228,3 +228,20 @@ class _NoStream:
     @property
     def cuda_stream(self):
         raise AssertionError("the binding reached the library call")
+
+
+def test_probe_arguments_are_checked_before_launch():
+    """The measurement probes reject bad kinds, sizes, counts and alignments
+    on the host (MOE_ERR_INVALID_ARG = 1), so nothing is launched; zero
+    bytes is a no-op."""
+    lib = moe.load_library()
+    p16, p8 = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x100008)
+    assert lib.moe_stream_probe(3, 0, p16, p16, 16, None, None) == 1        # no such kind
+    assert lib.moe_stream_probe(2, 0, p16, p16, 24, None, None) == 1        # not a multiple of 16
+    assert lib.moe_stream_probe(2, 0, p8, p16, 16, None, None) == 1         # misaligned source
+    assert lib.moe_stream_probe(2, 0, None, p16, 16, None, None) == 1       # copy without a source
+    assert lib.moe_stream_probe(0, 0, p16, None, 0, None, None) == 0        # nothing to read
+    assert lib.moe_mfma_probe(0, 1, p16, None, None) == 1
+    assert lib.moe_mfma_probe(1, 0, p16, None, None) == 1
+    assert lib.moe_mfma_probe(1, 1, p8, None, None) == 1
+    assert lib.moe_mfma_probe(1, 1, None, None, None) == 1
