@@ -120,6 +120,15 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void *sbase, uint32_t
                : "memory", "m0");
 }
 
+// The same with the non-temporal hint: for a stream read once (expert
+// weights no other workgroup shares), which then does not push reused data
+// out of the caches.
+__device__ __forceinline__ void dma16_nt(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(m0v)
+               : "memory", "m0");
+}
+
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)p));

@@ -34,6 +34,9 @@ constexpr int SBN = 256;              // weight rows per tile
 constexpr int kSkinnyTarget = 512;    // workgroups the K split aims for
 constexpr int kPieceStages = 4;       // a K piece keeps at least this many stages
 constexpr int kSkinnyStages = 2;      // LDS ring depth: 2 stages (80 KB), two workgroups per CU
+// Weight loads carry the non-temporal hint when K is at least this long
+// (each weight tile is read by one workgroup only).
+constexpr int kSkinnyNtMinK = 4096;
 static_assert(kSkinnyTarget <= kSkinnyMaxPieces, "partial buffer holds every piece");
 
 template <int BM>
@@ -81,7 +84,7 @@ __device__ __forceinline__ bool skinny_job(const GemmParams &p, int nk, SkJob *j
 // LDS row of 128 B: element offset of logical chunk c of row r
 __device__ __forceinline__ int sk_chunk(int r, int c) { return r * SK + ((c ^ ((r >> 1) & 7)) << 3); }
 
-template <int ACT, int BM, int SST>
+template <int ACT, int BM, int SST, bool BNT>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p) {
   using C = Sk<BM>;
   constexpr int MI = C::MI, NJ = C::NJ;
@@ -126,7 +129,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
     for (int i = 0; i < C::A_INSTR; ++i) dma16(a_off[i], A + st * SK * 2, base + (w + 4 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_INSTR; ++i)
-      dma16(b_off[i], B + st * SK * 2, base + C::A_ELEMS * 2 + (w + 4 * i) * 1024);
+      if constexpr (BNT) dma16_nt(b_off[i], B + st * SK * 2, base + C::A_ELEMS * 2 + (w + 4 * i) * 1024);
+      else dma16(b_off[i], B + st * SK * 2, base + C::A_ELEMS * 2 + (w + 4 * i) * 1024);
   };
 
   // fragment rows: A tile i rows i*32 + l%32; B tile j rows brow[j] + l%32
@@ -277,7 +281,8 @@ int64_t sk_mtile_bound(int64_t rows, int E, int bm) { return rows / bm + std::mi
 
 template <int ACT, int BM>
 void launch_skinny(const GemmParams &p, int64_t blocks, bool reduce, hipStream_t st) {
-  gemm_bf16_skinny_kernel<ACT, BM, kSkinnyStages><<<blocks, kThreads, 0, st>>>(p);
+  if (p.K >= kSkinnyNtMinK) gemm_bf16_skinny_kernel<ACT, BM, kSkinnyStages, true><<<blocks, kThreads, 0, st>>>(p);
+  else gemm_bf16_skinny_kernel<ACT, BM, kSkinnyStages, false><<<blocks, kThreads, 0, st>>>(p);
   if (reduce) skinny_reduce_kernel<ACT, BM><<<1024, kThreads, 0, st>>>(p);
 }
 
