@@ -23,6 +23,8 @@ CASES = [  # T, k, E, capacity factor (0 = dropless), d
     (2731, 3, 256, 1.25, 64),   # 8193, 256 experts, drops
     (1000, 16, 37, 0.5, 40),    # 16 slots per token, heavy drops, single launch
     (3, 2, 4, 0.0, 8),          # fewer tokens than one workgroup takes
+    (12000, 4, 256, 1.25, 8),   # [blocks x E] table past LDS: count, scan, scatter launches; drops
+    (9000, 6, 200, 0.0, 520),   # the same path dropless, 2-KB rows
     (100, 1, 4, 1.2, 8),        # cf * T * k / E = 30 exactly; 1.2 has no exact float32 value
     (1000, 1, 4, 1.1, 16),      # 275 exactly; likewise for 1.1
 ]
