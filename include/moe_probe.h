@@ -37,8 +37,8 @@ moe_status moe_stream_probe(int32_t kind, int32_t nontemporal, const void *src, 
  * accumulators (a 128 x 64 block of 32 x 32 tiles; the B operands of
  * alternate rounds differ) and nothing else; iters is rounded up to an
  * even count.  Flops = blocks * 4 * iters * 8 * 32768.  The accumulators
- * are summed into one float per wave and written to sink only if that sum
- * is a fixed improbable value (sink may then be NULL).  blocks and iters
+ * are summed into one float per wave, which goes to sink[wave] (blocks * 4
+ * floats) only if it equals a fixed improbable value (sink may be NULL).  blocks and iters
  * must be positive and operands 16-byte aligned (else MOE_ERR_INVALID_ARG);
  * the call only enqueues the kernel on `stream`. */
 moe_status moe_mfma_probe(int32_t blocks, int32_t iters, const void *operands, void *sink, void *stream);

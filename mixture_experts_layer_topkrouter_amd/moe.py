@@ -332,6 +332,11 @@ def stream_probe(kind: str, src, dst, nbytes: int, nontemporal: bool = False, si
     """moe_stream_probe: kind "read", "write" or "copy" over nbytes of
     contiguous device buffers (include/moe_probe.h)."""
     k = {"read": 0, "write": 1, "copy": 2}[kind]
+    for t, name, used in ((src, "src", k != 1), (dst, "dst", k != 0)):
+        if used and (t is None or t.numel() * t.element_size() < nbytes):
+            raise ValueError(f"{name}: at least {nbytes} bytes needed")
+    if sink is not None and sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink: one 32-bit word needed")
     _check(load_library().moe_stream_probe(k, int(bool(nontemporal)), _arg(src, "src", None, 0),
                                            _arg(dst, "dst", None, 0), nbytes, _arg(sink, "sink", None, 0),
                                            _stream(stream)), "moe_stream_probe")
@@ -342,6 +347,8 @@ def mfma_probe(blocks: int, iters: int, operands, sink=None, stream=None):
     operands: a bf16 device tensor of at least blocks * 16384 elements."""
     if operands.numel() * operands.element_size() < blocks * 32768:
         raise ValueError("operands: blocks * 32 KB needed")
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() < blocks * 4):
+        raise ValueError("sink: blocks * 4 float32 values needed")
     _check(load_library().moe_mfma_probe(int(blocks), int(iters), _arg(operands, "operands", None, 0),
                                          _arg(sink, "sink", None, 0), _stream(stream)), "moe_mfma_probe")
 

@@ -4,6 +4,7 @@ and rejects invalid arguments on the host before anything reaches a GPU
 import ctypes
 
 import pytest
+import torch
 
 from mixture_experts_layer_topkrouter_amd import moe
 from mixture_experts_layer_topkrouter_amd import workloads as W
@@ -245,3 +246,15 @@ def test_probe_arguments_are_checked_before_launch():
     assert lib.moe_mfma_probe(1, 0, p16, None, None) == 1
     assert lib.moe_mfma_probe(1, 1, p8, None, None) == 1
     assert lib.moe_mfma_probe(1, 1, None, None, None) == 1
+
+
+def test_probe_binding_checks_sizes():
+    """The probe wrappers refuse buffers smaller than the bytes asked for
+    before calling the library (CPU tensors: the checks come first)."""
+    small = torch.empty(8, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        moe.stream_probe("copy", small, small, 16)
+    with pytest.raises(ValueError):
+        moe.stream_probe("write", None, small, 16)
+    with pytest.raises(ValueError):
+        moe.mfma_probe(2, 1, torch.empty(16384, dtype=torch.bfloat16))
