@@ -3,8 +3,14 @@
 
 One step = the whole forward pass of one MoE block (route, permute, grouped
 expert FFN, shared expert when present, unpermute) over one batch of seeded
-synthetic tokens already resident in HBM: one moe_layer_fwd call (the
-shared expert runs beside the rest on its side stream).  ``value`` is the
+synthetic tokens already resident in HBM: one moe_layer_fwd_packed call
+(the shared expert runs beside the rest on its side stream).  The expert
+weights are packed once, before any timed region (moe_pack_weights: the
+tile-major order in which the expert GEMMs stream them); the same layer on
+the unpacked weights (moe_layer_fwd) is timed beside it and must give the
+same bits (``weights``).  ``--unpacked`` times moe_layer_fwd instead; a
+workload whose widths cannot be packed (fp32, or not multiples of 64) runs
+unpacked.  ``value`` is the
 wall-clock rate over the back-to-back calls; the same calls timed one by one
 with HIP events give ``layer_fwd_median_ms``, and the layer captured once
 into a HIP graph and replayed gives ``graph_replay``.  A second timed
@@ -72,6 +78,8 @@ def parse():
                          "after the headline's timed regions)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (calibrates HBM byte counters)")
+    ap.add_argument("--unpacked", dest="packed", action="store_false",
+                    help="run the layer on the unpacked expert weights (moe_layer_fwd)")
     ap.add_argument("--traffic-run", action="store_true",
                     help="only the launches a profiler's HBM byte counters are read from: one step through the "
                          "stage entry points, then each stage again (3 calls of each in all, 5 of the shared "
@@ -150,11 +158,17 @@ def stage_sources_sha256(stage: str) -> str:
     return h.hexdigest()
 
 
-def stage_functions(w, cfg, dev, layer, moe, W, torch):
+def packable(w, W) -> bool:
+    """Expert weights the packed entry points take: bf16, widths multiples of 64."""
+    return w.dtype == W.BF16 and w.d % 64 == 0 and w.d_ff % 64 == 0 and w.d_ff_shared % 64 == 0
+
+
+def stage_functions(w, cfg, dev, layer, moe, W, torch, packed=False):
     """One callable per stage of the step-by-step path (route, permute, routed
     FFN, shared FFN, unpermute), on the intermediates of `layer`'s workspace;
     each rewrites only its own outputs, so any stage can be re-run on its own
-    once a whole step has run."""
+    once a whole step has run.  packed: the FFNs read the weights layer.pack()
+    prepared (moe_expert_ffn_packed)."""
     T, E, d = w.T, w.E, w.d
     ec = w.routing == W.EXPERT_CHOICE
     V = layer.view
@@ -193,9 +207,14 @@ def stage_functions(w, cfg, dev, layer, moe, W, torch):
                                          bias_stride=dev.bias_stride))
             fns.append(lambda: moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off,
                                            topk_idx=topk_idx, scratch=scratch))
-        fns.append(lambda: moe.expert_ffn(cfg, x_perm, off, dev.w1, dev.w2, h, y_perm, ffn_ws))
-        if w.d_ff_shared:
-            fns.append(lambda: moe.expert_ffn(scfg, dev.x, soff, dev.ws1, dev.ws2, hs, ys, sffn_ws))
+        if packed:
+            fns.append(lambda: moe.expert_ffn_packed(cfg, x_perm, off, layer.w1p, layer.w2p, h, y_perm, ffn_ws))
+            if w.d_ff_shared:
+                fns.append(lambda: moe.expert_ffn_packed(scfg, dev.x, soff, layer.ws1p, layer.ws2p, hs, ys, sffn_ws))
+        else:
+            fns.append(lambda: moe.expert_ffn(cfg, x_perm, off, dev.w1, dev.w2, h, y_perm, ffn_ws))
+            if w.d_ff_shared:
+                fns.append(lambda: moe.expert_ffn(scfg, dev.x, soff, dev.ws1, dev.ws2, hs, ys, sffn_ws))
         if ec:
             fns.append(lambda: moe.unpermute(cfg, y_perm, slot_row, slot_w, layer.y, tok_ptr=tok_ptr,
                                              y_shared=ys if w.d_ff_shared else None))
@@ -255,12 +274,13 @@ def stage_rates(w, work, ms, peak_flops, peak_hbm):
     return out
 
 
-def measure_workload(name, steps, warmup, moe, W, torch):
-    """One workload besides the headline one: the median moe_layer_fwd time
-    (HIP events around each of `steps` calls), tokens/s at that median, the
-    median of every stage of the step-by-step path, and the FFN's roofline
-    fraction (MFMA or HBM, by its intensity).  Outputs of the two paths must
-    agree bit for bit."""
+def measure_workload(name, steps, warmup, moe, W, torch, packed=True):
+    """One workload besides the headline one: the median layer forward time
+    (HIP events around each of `steps` calls; packed weights where the
+    workload allows, the unpacked forward's median beside it), tokens/s at
+    that median, the median of every stage of the step-by-step path, and the
+    FFN's roofline fraction (MFMA or HBM, by its intensity).  Outputs of all
+    paths must agree bit for bit."""
     w = W.WORKLOADS[name]
     t_gen = time.time()
     inp = W.make_inputs(w, seed=0)
@@ -270,18 +290,33 @@ def measure_workload(name, steps, warmup, moe, W, torch):
     del inp
     layer = moe.MoELayer(cfg, dev)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        layer.forward()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        a.record(stream)
-        layer.forward()
-        b.record(stream)
-    torch.cuda.synchronize()
-    layer_ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    packed = packed and packable(w, W)
+    if packed:
+        layer.pack()
+
+    def median_fwd(pk):
+        for _ in range(warmup):
+            layer.forward(packed=pk)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            layer.forward(packed=pk)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    bits = (lambda t: t.view(torch.int16)) if w.dtype == W.BF16 else (lambda t: t)
+    unpacked_ms, unpacked_same = None, None
+    if packed:
+        unpacked_ms = median_fwd(False)
+        y_unpacked = layer.y.clone()
+    layer_ms = median_fwd(packed)
     y_layer = layer.y.clone()
-    names, fns = stage_functions(w, cfg, dev, layer, moe, W, torch)
+    if packed:
+        unpacked_same = bool(torch.equal(bits(y_unpacked), bits(y_layer)))
+        del y_unpacked
+    names, fns = stage_functions(w, cfg, dev, layer, moe, W, torch, packed)
     for _ in range(min(warmup, 3)):
         for fn in fns:
             fn()
@@ -295,7 +330,6 @@ def measure_workload(name, steps, warmup, moe, W, torch):
     torch.cuda.synchronize()
     med = {n: float(np.median([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
            for j, n in enumerate(names)}
-    bits = (lambda t: t.view(torch.int16)) if w.dtype == W.BF16 else (lambda t: t)
     same = bool(torch.equal(bits(y_layer), bits(layer.y)))
     n_rows, n_active, t_used = kept_counts(w, layer, W)
     work = algorithmic(w, n_rows, n_active, t_used)
@@ -310,7 +344,10 @@ def measure_workload(name, steps, warmup, moe, W, torch):
            "layer_fwd_median_ms": round(layer_ms, 4), "tokens_per_s": round(w.T / (layer_ms / 1e3), 1),
            "ffn_roofline": ({"bound": "mfma", "frac": ffn["mfma_frac"]} if flops / fbytes >= ridge
                             else {"bound": "hbm", "frac": ffn["hbm_frac"]}),
-           "stages": st, "layer_fwd_matches_steps": same, "input_gen_s": round(t_gen, 1)}
+           "stages": st, "layer_fwd_matches_steps": same, "input_gen_s": round(t_gen, 1),
+           "weights": {"order": "packed" if packed else "unpacked",
+                       "unpacked_layer_fwd_median_ms": None if unpacked_ms is None else round(unpacked_ms, 4),
+                       "unpacked_matches": unpacked_same}}
     del layer, dev
     torch.cuda.empty_cache()
     return out
@@ -339,7 +376,17 @@ def main():
     T, E, d = w.T, w.E, w.d
     ec = w.routing == W.EXPERT_CHOICE
     k = 0 if ec else w.k
-    names, fns = stage_functions(w, cfg, dev, layer, moe, W, torch)
+    # packed expert weights: rearranged once, here, outside every timed region
+    use_packed = args.packed and packable(w, W)
+    pack_ms = None
+    if use_packed:
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        layer.pack()
+        torch.cuda.synchronize()
+        pack_ms = (time.perf_counter() - tp) * 1e3
+    fwd = lambda: layer.forward(packed=use_packed)
+    names, fns = stage_functions(w, cfg, dev, layer, moe, W, torch, use_packed)
     stream = torch.cuda.current_stream()
     ec = w.routing == W.EXPERT_CHOICE
     V = layer.view
@@ -376,14 +423,15 @@ def main():
                           "sources_sha256": {n: stage_sources_sha256(n) for n in names}}), flush=True)
         return
 
-    # The headline: K calls of moe_layer_fwd (the whole layer, shared expert
-    # overlapped on its side stream), between two synchronisations.
+    # The headline: K calls of moe_layer_fwd_packed (moe_layer_fwd with
+    # --unpacked; the whole layer, shared expert overlapped on its side
+    # stream), between two synchronisations.
     for _ in range(args.warmup):
-        layer.forward()
+        fwd()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        layer.forward()
+        fwd()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -393,10 +441,28 @@ def main():
     lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in lev:
         a.record(stream)
-        layer.forward()
+        fwd()
         b.record(stream)
     torch.cuda.synchronize()
     layer_med_ms = float(np.median([a.elapsed_time(b) for a, b in lev]))
+    bits = (lambda t: t.view(torch.int16)) if y_layer.dtype == torch.bfloat16 else (lambda t: t)
+    # the same layer on the unpacked weights (moe_layer_fwd), timed the same
+    # way: what packing saves, and the same bits
+    weights = {"order": "packed" if use_packed else "unpacked"}
+    if use_packed:
+        for _ in range(min(args.warmup, 3)):
+            layer.forward()
+        torch.cuda.synchronize()
+        uev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in uev:
+            a.record(stream)
+            layer.forward()
+            b.record(stream)
+        torch.cuda.synchronize()
+        weights.update({"pack_ms_untimed": round(pack_ms, 2),
+                        "unpacked_layer_fwd_median_ms": round(float(np.median([a.elapsed_time(b) for a, b in uev])), 4),
+                        "unpacked_matches": bool(torch.equal(bits(y_layer), bits(layer.y)))})
     # the same layer captured once into a HIP graph and replayed K times (the
     # launches of one step become one graph launch; the outputs must match)
     graph = None
@@ -404,12 +470,12 @@ def main():
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
-            layer.forward()
+            fwd()
         stream.wait_stream(cap)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            layer.forward()
+            fwd()
         torch.cuda.synchronize()
         for _ in range(min(args.warmup, 3)):
             g.replay()
@@ -485,7 +551,7 @@ def main():
             return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
         # recompute mode: after a plain forward, the backward re-runs GEMM1
-        layer.forward()
+        fwd()
         ms_re = timed(lambda: layer.backward(dy, recompute=True), args.bwd_steps)
         # training mode: the forward keeps the pre-activations, the backward
         # reads them
@@ -616,7 +682,9 @@ def main():
     ffn_s = stage_ms["expert_ffn"] / 1e3
     peak = PEAK_BF16_TFLOPS if w.dtype == W.BF16 else PEAK_F32_TFLOPS
     ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
-    common = {"traffic": measured_traffic(w.name), "kernel": "grouped expert FFN: every kernel of one moe_expert_ffn call",
+    common = {"traffic": measured_traffic(w.name),
+              "kernel": "grouped expert FFN: every kernel of one moe_expert_ffn" + ("_packed" if use_packed else "")
+                        + " call",
               "avg_ms": round(stage_ms["expert_ffn"], 4), "flops_per_launch": int(ffn_flops),
               "bytes_per_launch": int(ffn_bytes), "intensity_flop_per_byte": round(ffn_flops / ffn_bytes, 1)}
     if ffn_flops / ffn_bytes >= ridge:
@@ -661,7 +729,7 @@ def main():
         others = {}
         for name in W.WORKLOADS:
             if name != w.name:
-                others[name] = measure_workload(name, args.steps, args.warmup, moe, W, torch)
+                others[name] = measure_workload(name, args.steps, args.warmup, moe, W, torch, args.packed)
 
     out = {
         "metric": METRIC,
@@ -685,6 +753,7 @@ def main():
         "backward": bwd,
         "event_ms_per_step": round(ev_total_ms, 4),
         "layer_fwd_median_ms": round(layer_med_ms, 4),
+        "weights": weights,
         "graph_replay": graph,
         "hbm_probe": hbm_probe,
         "tokens_per_s_at_median": round(T / (layer_med_ms / 1e3), 1),

@@ -183,7 +183,9 @@ moe_status moe_permute_noalloc(const moe_config *cfg, const void *x, const int32
  *   bf16, <= 128 rows per expert on average, K a multiple of 64: the
  *   weight-streaming kernel cuts its tiles when there are too few to fill
  *   the GPU; 512 tiles of 64 x 256 fp32: 32 MiB.
- * The larger of the two applies; 0 for every other configuration. */
+ * The larger of the two applies; 0 for every other configuration.  When the
+ * configuration also admits packed weights (moe_pack_weights), the figure
+ * covers moe_expert_ffn_packed as well, whose kernel choice can differ. */
 moe_status moe_expert_ffn_workspace_bytes(const moe_config *cfg, size_t *bytes);
 
 /* --------------------------------------------------------------------------
@@ -209,6 +211,50 @@ moe_status moe_expert_ffn_workspace_bytes(const moe_config *cfg, size_t *bytes);
 moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
                           const void *w1, const void *w2, void *h, void *y_perm, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * Packed expert weights for inference: the same computation as
+ * moe_expert_ffn / moe_layer_fwd ([P1] "Core MoE Layer Architecture",
+ * MoELayer step 2), with each weight matrix rearranged once, when it is
+ * loaded, into the order in which the expert GEMMs stream it, so that every
+ * K stage of a weight tile is one contiguous block of memory.
+ *
+ * Packed order of one weight (per expert e, column tile j, K slice s):
+ *   column tiles of 256 weight rows; SwiGLU's W1 tile j holds gate rows
+ *   [128 j, 128 j + 128) then the matching up rows; K slices of 32; each
+ *   (e, j, s) is a block of 256 x 32 bf16 (16 KB) at byte
+ *   ((e * tiles + j) * (K / 32) + s) * 16384, whose 16-B chunk q holds row
+ *   q / 4 of the tile at K elements 32 s + 8 ((q % 4) ^ ((q / 16) % 4)) .. +8.
+ *   Tile rows past the weight's output width are zero.
+ * Requirements: dtype bf16, d_model and the FFN width (d_ff, or d_ff_shared
+ * for the shared expert's weights) multiples of 64; otherwise
+ * MOE_ERR_UNSUPPORTED.  Results are bitwise identical to the unpacked entry
+ * points on the same weights.  Training (moe_layer_fwd_train,
+ * moe_layer_bwd) takes the unpacked weights.
+ * ------------------------------------------------------------------------ */
+typedef enum {
+  MOE_PACK_W1 = 0,        /* w1 [E, n_up*d_ff, d]             */
+  MOE_PACK_W2 = 1,        /* w2 [E, d, d_ff]                  */
+  MOE_PACK_SHARED_W1 = 2, /* ws1 [n_up*d_ff_shared, d]        */
+  MOE_PACK_SHARED_W2 = 3  /* ws2 [d, d_ff_shared]             */
+} moe_pack_which;
+/* Bytes of the packed form of weight `which` (a moe_pack_which):
+ * E * tiles * (K / 32) * 16384 with K its input width and tiles =
+ * ceil(d_ff / 128) for SwiGLU's W1, ceil(output width / 256) otherwise.
+ * MOE_ERR_INVALID_ARG for an unknown `which` or a shared weight when
+ * d_ff_shared == 0. */
+moe_status moe_packed_weight_bytes(const moe_config *cfg, int32_t which, size_t *bytes);
+/* Enqueues the rearrangement of weight `which` from `w` (unpacked layout, as
+ * moe_expert_ffn / moe_layer_fwd take it) into `packed`
+ * (moe_packed_weight_bytes() bytes, caller-owned, 16-byte aligned, not
+ * overlapping w; every byte is written).  w is only read. */
+moe_status moe_pack_weights(const moe_config *cfg, int32_t which, const void *w, void *packed, void *stream);
+/* moe_expert_ffn on packed weights: w1_packed / w2_packed from
+ * moe_pack_weights(MOE_PACK_W1 / MOE_PACK_W2); every other argument, the
+ * workspace size and the results as moe_expert_ffn. */
+moe_status moe_expert_ffn_packed(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
+                                 const void *w1_packed, const void *w2_packed, void *h, void *y_perm,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
  * moe_unpermute -- [P1] "Token Dispatching and Communication"
@@ -263,6 +309,14 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
                          const float *logit_bias, int64_t bias_row_stride, const void *w1,
                          const void *w2, const void *ws1, const void *ws2, void *y,
                          void *workspace, size_t workspace_bytes, void *stream);
+/* moe_layer_fwd on packed expert weights (moe_pack_weights: MOE_PACK_W1,
+ * MOE_PACK_W2, and for a shared expert MOE_PACK_SHARED_W1 / _W2); the router
+ * weights stay unpacked.  Workspace (moe_layer_workspace) and results as
+ * moe_layer_fwd. */
+moe_status moe_layer_fwd_packed(const moe_config *cfg, const void *x, const void *w_router,
+                                const float *logit_bias, int64_t bias_row_stride, const void *w1_packed,
+                                const void *w2_packed, const void *ws1_packed, const void *ws2_packed, void *y,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
  * Backward pass ([P1] "Activation Checkpointing and Constraints": the layer

@@ -184,13 +184,24 @@ void *noalloc_scratch() {
   return addr[dev];
 }
 
+// Packed expert weights: bf16, and every dimension a packed GEMM contracts
+// over or tiles a multiple of 64.
+bool packable(const moe_config *c, int dff) { return c->dtype == MOE_BF16 && c->d_model % 64 == 0 && dff % 64 == 0; }
+
+// The FFN scratch of a configuration covers both weight orders: the packed
+// one may run another kernel (and so need another scratch) than the plain.
 size_t ffn_scratch_of(const moe_config *c) {
-  return moe::ffn_scratch_bytes(c->dtype, c->num_experts, c->d_model, c->d_ff, max_rows_of(c));
+  const int64_t rows = max_rows_of(c);
+  size_t need = moe::ffn_scratch_bytes(c->dtype, c->num_experts, c->d_model, c->d_ff, rows);
+  if (packable(c, c->d_ff))
+    need = std::max(need, moe::ffn_scratch_bytes(c->dtype, c->num_experts, c->d_model, c->d_ff, rows, true));
+  return need;
 }
 
 moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset, const void *w1,
                     const void *w2, void *h, void *y_perm, void *workspace, size_t workspace_bytes,
-                    void *stream, void *z = nullptr) {
+                    void *stream, void *z = nullptr, bool packed = false) {
+  if (packed && (!packable(cfg, cfg->d_ff) || z)) return MOE_ERR_UNSUPPORTED;
   if (max_rows_of(cfg) == 0) return MOE_OK;  // no rows: nothing to compute, empty buffers may be NULL
   if (!x_perm || !expert_offset || !w1 || !w2 || !h || !y_perm) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) || !aligned16(y_perm))
@@ -216,7 +227,27 @@ moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *ex
   a.scratch = workspace;
   a.scratch_bytes = workspace_bytes;
   a.z = z;
+  a.packed = packed;
   return hip_status(moe::launch_expert_ffn(a, static_cast<hipStream_t>(stream)));
+}
+
+// Shapes of the weight that `which` names (moe_pack_which).
+moe_status pack_args(const moe_config *cfg, int32_t which, moe::PackArgs *a) {
+  const bool swiglu = cfg->act == MOE_ACT_SWIGLU;
+  const int d = cfg->d_model;
+  switch (which) {
+    case MOE_PACK_W1: *a = {cfg->num_experts, (swiglu ? 2 : 1) * cfg->d_ff, cfg->d_ff, d, swiglu, nullptr, nullptr}; break;
+    case MOE_PACK_W2: *a = {cfg->num_experts, d, d, cfg->d_ff, false, nullptr, nullptr}; break;
+    case MOE_PACK_SHARED_W1:
+      *a = {1, (swiglu ? 2 : 1) * cfg->d_ff_shared, cfg->d_ff_shared, d, swiglu, nullptr, nullptr};
+      break;
+    case MOE_PACK_SHARED_W2: *a = {1, d, d, cfg->d_ff_shared, false, nullptr, nullptr}; break;
+    default: return MOE_ERR_INVALID_ARG;
+  }
+  const bool shared = which == MOE_PACK_SHARED_W1 || which == MOE_PACK_SHARED_W2;
+  if (shared && cfg->d_ff_shared == 0) return MOE_ERR_INVALID_ARG;
+  if (!packable(cfg, shared ? cfg->d_ff_shared : cfg->d_ff)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
 }
 
 moe_status unpermute_impl(const moe_config *cfg, const void *y_perm, const int32_t *tok_ptr,
@@ -511,9 +542,11 @@ moe_status ffn_bwd_impl(const moe_config *c, int E, int dff, int64_t rows, const
 moe_status layer_fwd_impl(const moe_config *cfg, const void *x, const void *w_router, const float *logit_bias,
                           int64_t bias_row_stride, const void *w1, const void *w2, const void *ws1,
                           const void *ws2, void *y, void *workspace, size_t workspace_bytes, void *stream,
-                          bool train) {
+                          bool train, bool packed = false) {
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
+  if (packed && (!packable(cfg, cfg->d_ff) || (cfg->d_ff_shared > 0 && !packable(cfg, cfg->d_ff_shared))))
+    return MOE_ERR_UNSUPPORTED;
   if (cfg->num_tokens == 0) return MOE_OK;  // empty batch: nothing to do, empty buffers may be NULL
   if (!x || !w_router || !w1 || !w2 || !y || !workspace) return MOE_ERR_INVALID_ARG;
   if (cfg->d_ff_shared > 0 && (!ws1 || !ws2)) return MOE_ERR_INVALID_ARG;
@@ -560,7 +593,7 @@ moe_status layer_fwd_impl(const moe_config *cfg, const void *x, const void *w_ro
     int32_t *so = static_cast<int32_t *>(P(L.shared_offset));
     if (moe::launch_fill_offsets(so, cfg->num_tokens, side->stream) != hipSuccess) return MOE_ERR_HIP;
     s = ffn_impl(&sc, x, so, ws1, ws2, P(L.shared_h), P(L.shared_y), P(L.shared_ffn_scratch),
-                 L.shared_ffn_scratch_bytes, side->stream, train ? P(L.shared_z) : nullptr);
+                 L.shared_ffn_scratch_bytes, side->stream, train ? P(L.shared_z) : nullptr, packed);
     if (s != MOE_OK) return s;
     if (hipEventRecord(side->join, side->stream) != hipSuccess) return MOE_ERR_HIP;
     join = side->join;
@@ -574,7 +607,7 @@ moe_status layer_fwd_impl(const moe_config *cfg, const void *x, const void *w_ro
                    static_cast<int32_t *>(P(L.expert_load)), expert_offset, P(L.scratch), L.scratch_bytes, stream);
   if (s != MOE_OK) return s;
   s = ffn_impl(cfg, P(L.x_perm), expert_offset, w1, w2, P(L.h), P(L.y_perm), P(L.ffn_scratch),
-               L.ffn_scratch_bytes, stream, train ? P(L.z) : nullptr);
+               L.ffn_scratch_bytes, stream, train ? P(L.z) : nullptr, packed);
   if (s != MOE_OK) return s;
   if (join && hipStreamWaitEvent(main_st, join, 0) != hipSuccess) return MOE_ERR_HIP;
   return unpermute_impl(cfg, P(L.y_perm), tok_ptr, slot_row, slot_w, y_shared, y, stream,
@@ -585,7 +618,7 @@ moe_status layer_fwd_impl(const moe_config *cfg, const void *x, const void *w_ro
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 6; }
+int32_t moe_abi_version(void) { return 7; }
 
 const char *moe_status_string(moe_status s) {
   switch (s) {
@@ -670,6 +703,36 @@ moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32
   return ffn_impl(cfg, x_perm, expert_offset, w1, w2, h, y_perm, workspace, workspace_bytes, stream);
 }
 
+moe_status moe_packed_weight_bytes(const moe_config *cfg, int32_t which, size_t *bytes) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe::PackArgs a{};
+  if ((s = pack_args(cfg, which, &a)) != MOE_OK) return s;
+  *bytes = moe::packed_weight_bytes(a.E, a.n_out, a.K, a.swiglu);
+  return MOE_OK;
+}
+
+moe_status moe_pack_weights(const moe_config *cfg, int32_t which, const void *w, void *packed, void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  moe::PackArgs a{};
+  if ((s = pack_args(cfg, which, &a)) != MOE_OK) return s;
+  if (!w || !packed || w == packed || !aligned16(w) || !aligned16(packed)) return MOE_ERR_INVALID_ARG;
+  a.src = w;
+  a.dst = packed;
+  return hip_status(moe::launch_pack_weights(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_ffn_packed(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
+                                 const void *w1_packed, const void *w2_packed, void *h, void *y_perm,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  return ffn_impl(cfg, x_perm, expert_offset, w1_packed, w2_packed, h, y_perm, workspace, workspace_bytes, stream,
+                  nullptr, true);
+}
+
 moe_status moe_unpermute(const moe_config *cfg, const void *y_perm, const int32_t *tok_ptr,
                          const int32_t *slot_row, const float *slot_w, const void *y_shared, void *y,
                          void *stream) {
@@ -691,6 +754,14 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
                          const void *ws2, void *y, void *workspace, size_t workspace_bytes, void *stream) {
   return layer_fwd_impl(cfg, x, w_router, logit_bias, bias_row_stride, w1, w2, ws1, ws2, y, workspace,
                         workspace_bytes, stream, false);
+}
+
+moe_status moe_layer_fwd_packed(const moe_config *cfg, const void *x, const void *w_router,
+                                const float *logit_bias, int64_t bias_row_stride, const void *w1_packed,
+                                const void *w2_packed, const void *ws1_packed, const void *ws2_packed, void *y,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  return layer_fwd_impl(cfg, x, w_router, logit_bias, bias_row_stride, w1_packed, w2_packed, ws1_packed, ws2_packed,
+                        y, workspace, workspace_bytes, stream, false, true);
 }
 
 moe_status moe_layer_fwd_train(const moe_config *cfg, const void *x, const void *w_router, const float *logit_bias,

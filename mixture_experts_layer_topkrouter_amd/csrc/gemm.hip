@@ -385,12 +385,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   const int64_t kfirst = static_cast<int64_t>(job.k0) + static_cast<int64_t>(job.kb) * DK;
   const char *A = static_cast<const char *>(p.A) +
                   (AT ? kfirst * p.lda + row0 : static_cast<int64_t>(row0) * p.lda + job.kb * DK) * 2;
+  // packed B: the stage blocks of column tile nt follow each other, 16 KB
+  // apart, and a stage is read as one contiguous block
+  static_assert(kPackK == DK && kPackBlockBytes == DSTAGE * 2, "a packed block is one B stage");
+  const bool packed = LAY == LAY_NT && p.packed;
   const char *B = static_cast<const char *>(p.B) +
-                  (BT ? (LAY == LAY_TN ? 0 : static_cast<int64_t>(e) * p.b_stride) + kfirst * p.ldb +
-                            static_cast<int64_t>(nt) * BN
-                      : static_cast<int64_t>(e) * p.b_stride + job.kb * DK) * 2;
+                  (packed ? static_cast<int64_t>(e) * p.b_stride * 2 +
+                                (static_cast<int64_t>(nt) * (p.K / DK) + job.kb) * kPackBlockBytes
+                          : (BT ? (LAY == LAY_TN ? 0 : static_cast<int64_t>(e) * p.b_stride) + kfirst * p.ldb +
+                                      static_cast<int64_t>(nt) * BN
+                                : static_cast<int64_t>(e) * p.b_stride + job.kb * DK) * 2);
   const int64_t a_step = AT ? static_cast<int64_t>(DK) * p.lda * 2 : DK * 2;
-  const int64_t b_step = BT ? static_cast<int64_t>(DK) * p.ldb * 2 : DK * 2;
+  const int64_t b_step = packed ? kPackBlockBytes : BT ? static_cast<int64_t>(DK) * p.ldb * 2 : DK * 2;
 
   auto slot = [&](auto S) -> uint16_t * {
     constexpr int s = decltype(S)::value;
@@ -435,7 +441,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
         const int col = nt * BN + r;
         br = col < p.n_out ? col : 0;
       }
-      b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(br) * p.ldb + c * 8) * 2);
+      b_off[i] = packed ? static_cast<uint32_t>(q * 16)
+                        : static_cast<uint32_t>((static_cast<int64_t>(br) * p.ldb + c * 8) * 2);
     }
   }
   // stage st of this piece: K elements [st*DK, st*DK + DK) past A / B
@@ -921,9 +928,20 @@ struct FfnPlan {
 // kernel when K is a multiple of 64.
 constexpr int64_t kSkinnyMaxAvgRows = 128;
 
-FfnPlan plan_ffn(int dtype, int E, int d, int d_ff, int64_t max_rows) {
+FfnPlan plan_ffn(int dtype, int E, int d, int d_ff, int64_t max_rows, bool packed) {
   FfnPlan f{};
   const int64_t avg_rows = max_rows / E;
+  if (packed) {
+    // packed weights (bf16, d and d_ff multiples of 64) are read by the two
+    // kernels that know the packed order: the skinny one up to
+    // kSkinnyMaxAvgRows rows per expert, the 256-row one above
+    f.bm = 256;
+    f.sk1 = f.sk2 = avg_rows <= kSkinnyMaxAvgRows ? 64 : 0;
+    f.dma1 = f.dma2 = f.sk1 == 0;
+    f.split1 = f.dma1 && d / DK >= kSplitMinStages;
+    f.split2 = f.dma2 && d_ff / DK >= kSplitMinStages;
+    return f;
+  }
   f.bm = avg_rows >= kDmaMinAvgRows ? 256 : 128;
   f.dma1 = dtype == 1 && f.bm == 256 && d % DK == 0;
   f.dma2 = dtype == 1 && f.bm == 256 && d_ff % DK == 0;
@@ -959,9 +977,9 @@ int round_units() {
 
 }  // namespace
 
-size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows) {
+size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows, bool packed) {
   if (max_rows == 0) return 0;
-  const FfnPlan f = plan_ffn(dtype, E, d, d_ff, max_rows);
+  const FfnPlan f = plan_ffn(dtype, E, d, d_ff, max_rows, packed);
   size_t need = 0;
   if (f.split1 || f.split2) {
     // the pieces of one round: at most kSplitUnits, and at most kMaxSplit per
@@ -979,9 +997,13 @@ size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows) {
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   if (a.max_rows == 0) return hipSuccess;
   const int n_up = a.act == 1 ? 2 : 1;
-  const FfnPlan f = plan_ffn(a.dtype, a.E, a.d, a.d_ff, a.max_rows);
-  const size_t need = ffn_scratch_bytes(a.dtype, a.E, a.d, a.d_ff, a.max_rows);
+  const FfnPlan f = plan_ffn(a.dtype, a.E, a.d, a.d_ff, a.max_rows, a.packed);
+  const size_t need = ffn_scratch_bytes(a.dtype, a.E, a.d, a.d_ff, a.max_rows, a.packed);
   if (a.scratch_bytes < need || (need > 0 && a.scratch == nullptr)) return hipErrorInvalidValue;
+  // packed weights: bf16 only, no kept pre-activations, both GEMMs on a
+  // kernel that reads the packed order
+  if (a.packed && (a.dtype != 1 || a.z || a.d % 64 || a.d_ff % 64 || !(f.dma1 || f.sk1) || !(f.dma2 || f.sk2)))
+    return hipErrorInvalidValue;
   float *part = static_cast<float *>(a.scratch);
   const int units = round_units();
   const int slots = static_cast<int>(std::min<size_t>(kSplitUnits, need / kPartTileBytes));
@@ -994,7 +1016,9 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   g1.lda = a.d;
   g1.B = a.w1;
   g1.ldb = a.d;
-  g1.b_stride = static_cast<int64_t>(n_up) * a.d_ff * a.d;
+  g1.b_stride = a.packed ? static_cast<int64_t>(packed_weight_bytes(1, a.d_ff, a.d, a.act == 1) / 2)
+                         : static_cast<int64_t>(n_up) * a.d_ff * a.d;
+  g1.packed = a.packed;
   g1.C = a.h;
   g1.ldc = a.d_ff;
   g1.offs = a.expert_offset;
@@ -1037,7 +1061,9 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   g2.lda = a.d_ff;
   g2.B = a.w2;
   g2.ldb = a.d_ff;
-  g2.b_stride = static_cast<int64_t>(a.d) * a.d_ff;
+  g2.b_stride = a.packed ? static_cast<int64_t>(packed_weight_bytes(1, a.d, a.d_ff, false) / 2)
+                         : static_cast<int64_t>(a.d) * a.d_ff;
+  g2.packed = a.packed;
   g2.C = a.y_perm;
   g2.ldc = a.d;
   g2.offs = a.expert_offset;
@@ -1069,6 +1095,57 @@ __global__ void fill_offsets_kernel(int32_t *dst, int32_t t, const int32_t *stam
 
 hipError_t launch_fill_offsets(int32_t *dst, int32_t t, hipStream_t st, const int32_t *stamp) {
   fill_offsets_kernel<<<1, 64, 0, st>>>(dst, t, stamp);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing (the order is described beside kPackBlockBytes): one thread
+// per 16-B chunk of the packed buffer, grid-stride.  Four neighbouring
+// threads read one row's 64 B of a 32-wide K slice; the writes are
+// contiguous.  A one-off transform, run when the weights are loaded.
+namespace {
+
+__global__ __launch_bounds__(256) void pack_weights_kernel(PackArgs a, int64_t chunks, int nk, int n_tiles) {
+  const char *src = static_cast<const char *>(a.src);
+  char *dst = static_cast<char *>(a.dst);
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; g < chunks;
+       g += static_cast<int64_t>(gridDim.x) * 256) {
+    const int q = static_cast<int>(g & 1023);
+    const int64_t blk = g >> 10;  // (e * n_tiles + nt) * nk + kb
+    const int kb = static_cast<int>(blk % nk);
+    const int64_t et = blk / nk;
+    const int nt = static_cast<int>(et % n_tiles);
+    const int64_t e = et / n_tiles;
+    const int r = q >> 2, c = (q & 3) ^ ((r >> 2) & 3);
+    int col, row;
+    if (a.swiglu) {
+      col = nt * (BN / 2) + (r & (BN / 2 - 1));
+      row = col + (r >= BN / 2 ? a.n_out : 0);
+    } else {
+      col = nt * BN + r;
+      row = col;
+    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (col < a.n_out)
+      v = *reinterpret_cast<const u32x4 *>(
+          src + ((e * a.n_rows + row) * static_cast<int64_t>(a.K) + kb * kPackK + c * 8) * 2);
+    *reinterpret_cast<u32x4 *>(dst + g * 16) = v;
+  }
+}
+
+}  // namespace
+
+size_t packed_weight_bytes(int E, int n_out, int K, bool swiglu) {
+  const int64_t n_tiles = swiglu ? (n_out + BN / 2 - 1) / (BN / 2) : (n_out + BN - 1) / BN;
+  return static_cast<size_t>(E) * static_cast<size_t>(n_tiles) * static_cast<size_t>(K / kPackK) * kPackBlockBytes;
+}
+
+hipError_t launch_pack_weights(const PackArgs &a, hipStream_t st) {
+  if (a.E <= 0 || a.n_out <= 0 || a.K <= 0 || a.K % kPackK) return hipErrorInvalidValue;
+  const int n_tiles = a.swiglu ? (a.n_out + BN / 2 - 1) / (BN / 2) : (a.n_out + BN - 1) / BN;
+  const int64_t chunks = static_cast<int64_t>(packed_weight_bytes(a.E, a.n_out, a.K, a.swiglu) / 16);
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 16384);
+  pack_weights_kernel<<<static_cast<unsigned>(blocks), 256, 0, st>>>(a, chunks, a.K / kPackK, n_tiles);
   return hipGetLastError();
 }
 

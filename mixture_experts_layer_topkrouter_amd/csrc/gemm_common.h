@@ -36,7 +36,19 @@ struct GemmParams {
   // elements after group e-1's and has m_rows rows (groups of K)
   int64_t c_stride;
   int m_rows;
+  // forward (NT) only: B is in the packed tile-major order of
+  // launch_pack_weights (b_stride then counts the packed elements of one
+  // expert; ldb and up_off are not used)
+  int packed;
 };
+
+// Packed weights: per expert, per column tile of BN weight rows (SwiGLU: the
+// tile's BN/2 gate rows, then the matching BN/2 up rows), per 32-wide slice
+// of K, one block of BN x 32 bf16 = 16 KB in the order the 256-row kernel's
+// LDS stage holds it (16-B chunk q: row q/4, K chunk (q%4) ^ ((q/16)%4)).
+// Rows past n_out are zero.
+constexpr int kPackK = 32;
+constexpr int kPackBlockBytes = BN * kPackK * 2;
 
 namespace {
 

@@ -95,7 +95,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
   const int rows = job.rows, nt = job.nt;
   const int l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const char *A = static_cast<const char *>(p.A) + (static_cast<int64_t>(job.row0) * p.lda + job.kb * SK) * 2;
-  const char *B = static_cast<const char *>(p.B) + (static_cast<int64_t>(job.e) * p.b_stride + job.kb * SK) * 2;
+  // packed B: a 64-wide stage is the column tile's two consecutive 32-wide
+  // blocks, 32 KB contiguous
+  static_assert(SK == 2 * kPackK && SBN == BN, "a stage is two packed blocks of one column tile");
+  const bool packed = p.packed != 0;
+  const char *B = static_cast<const char *>(p.B) +
+                  (packed ? static_cast<int64_t>(job.e) * p.b_stride * 2 +
+                                (static_cast<int64_t>(nt) * (p.K / kPackK) + 2 * job.kb) * kPackBlockBytes
+                          : (static_cast<int64_t>(job.e) * p.b_stride + job.kb * SK) * 2);
+  const int64_t b_step = packed ? 2 * kPackBlockBytes : SK * 2;
 
   auto slot = [&](auto S) -> uint16_t * { return ring[decltype(S)::value]; };
 
@@ -121,7 +129,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
       const int col = nt * SBN + r;
       br = col < p.n_out ? col : 0;
     }
-    b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(br) * p.ldb + c * 8) * 2);
+    // packed: logical chunk c of row r sits in block c/4 at chunk
+    // 4r + ((c%4) ^ ((r/4)%4))
+    b_off[i] = packed ? static_cast<uint32_t>((c >> 2) * kPackBlockBytes + (4 * r + ((c & 3) ^ ((r >> 2) & 3))) * 16)
+                      : static_cast<uint32_t>((static_cast<int64_t>(br) * p.ldb + c * 8) * 2);
   }
   auto issue = [&](auto S, int st) {
     const uint32_t base = lds_addr_of(slot(S));
@@ -129,8 +140,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
     for (int i = 0; i < C::A_INSTR; ++i) dma16(a_off[i], A + st * SK * 2, base + (w + 4 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_INSTR; ++i)
-      if constexpr (BNT) dma16_nt(b_off[i], B + st * SK * 2, base + C::A_ELEMS * 2 + (w + 4 * i) * 1024);
-      else dma16(b_off[i], B + st * SK * 2, base + C::A_ELEMS * 2 + (w + 4 * i) * 1024);
+      if constexpr (BNT) dma16_nt(b_off[i], B + st * b_step, base + C::A_ELEMS * 2 + (w + 4 * i) * 1024);
+      else dma16(b_off[i], B + st * b_step, base + C::A_ELEMS * 2 + (w + 4 * i) * 1024);
   };
 
   // fragment rows: A tile i rows i*32 + l%32; B tile j rows brow[j] + l%32

@@ -66,9 +66,23 @@ struct FfnArgs {
   void *scratch;  // ffn_scratch_bytes() bytes, 256-B aligned
   size_t scratch_bytes;
   void *z;        // optional [max_rows, n_up*d_ff]: keep the pre-activations
+  bool packed;    // w1 / w2 in the packed order of launch_pack_weights (bf16,
+                  // d and d_ff multiples of 64, no z)
 };
-size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows);
+size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows, bool packed = false);
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st);
+
+// Expert weights [E][n_rows][K] (bf16) -> the packed tile-major order the
+// forward GEMMs read as whole contiguous stages (gemm_common.h describes it).
+// SwiGLU: n_rows = 2 n_out, gate rows first; otherwise n_rows = n_out.
+struct PackArgs {
+  int E, n_rows, n_out, K;
+  bool swiglu;
+  const void *src;
+  void *dst;
+};
+size_t packed_weight_bytes(int E, int n_out, int K, bool swiglu);
+hipError_t launch_pack_weights(const PackArgs &a, hipStream_t st);
 
 struct CombineArgs {
   int dtype;

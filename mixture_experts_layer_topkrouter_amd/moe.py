@@ -25,6 +25,8 @@ LIB_PATH = os.environ.get("MOE_HIP_LIB") or os.path.join(_HERE, "libmoe_mi355x.s
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 F32, BF16 = 0, 1
+# moe_pack_which: the weight moe_pack_weights rearranges
+PACK_W1, PACK_W2, PACK_SHARED_W1, PACK_SHARED_W2 = 0, 1, 2, 3
 GELU, SWIGLU = 0, 1
 SOFTMAX_ALL, SOFTMAX_TOPK, EXPERT_CHOICE = 0, 1, 2
 
@@ -105,6 +107,10 @@ def load_library() -> ctypes.CDLL:
         "moe_unpermute": ([CP, P, P, P, P, P, P, P], ctypes.c_int),
         "moe_layer_workspace": ([CP, ctypes.POINTER(WorkspaceLayout)], ctypes.c_int),
         "moe_layer_fwd": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "moe_packed_weight_bytes": ([CP, ctypes.c_int32, ctypes.POINTER(sz)], ctypes.c_int),
+        "moe_pack_weights": ([CP, ctypes.c_int32, P, P, P], ctypes.c_int),
+        "moe_expert_ffn_packed": ([CP, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "moe_layer_fwd_packed": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_layer_bwd_workspace": ([CP, ctypes.POINTER(BwdLayout)], ctypes.c_int),
         "moe_layer_fwd_train": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_layer_bwd": ([CP, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, ctypes.c_int32, P, sz, P], ctypes.c_int),
@@ -278,6 +284,53 @@ def expert_ffn(cfg: MoeConfig, x_perm, expert_offset, w1, w2, h, y_perm, workspa
         _stream(stream)), "moe_expert_ffn")
 
 
+_PACK_NAMES = {PACK_W1: "w1", PACK_W2: "w2", PACK_SHARED_W1: "ws1", PACK_SHARED_W2: "ws2"}
+
+
+def packed_weight_bytes(cfg: MoeConfig, which: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_packed_weight_bytes(ctypes.byref(cfg), which, ctypes.byref(n)),
+           "moe_packed_weight_bytes")
+    return int(n.value)
+
+
+def _packed_arg(cfg: MoeConfig, t, which: int):
+    """A packed weight: a uint8 device tensor of packed_weight_bytes() bytes."""
+    if t is None:
+        return None
+    return _arg(t, "packed " + _PACK_NAMES[which], torch.uint8, packed_weight_bytes(cfg, which))
+
+
+def pack_weights(cfg: MoeConfig, which: int, w, packed=None, stream=None) -> torch.Tensor:
+    """moe_pack_weights: rearranges weight `which` (PACK_W1, PACK_W2,
+    PACK_SHARED_W1, PACK_SHARED_W2) into `packed` (a uint8 device tensor of
+    packed_weight_bytes(cfg, which) bytes, allocated on w's device when
+    None) and returns it."""
+    if which not in _PACK_NAMES:
+        raise ValueError(f"unknown packed weight {which}")
+    nbytes = packed_weight_bytes(cfg, which)
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    n = _dims(cfg)
+    name = _PACK_NAMES[which]
+    _check(load_library().moe_pack_weights(
+        ctypes.byref(cfg), which, _arg(w, name, torch_dtype(cfg), n[name]), _packed_arg(cfg, packed, which),
+        _stream(stream)), "moe_pack_weights")
+    return packed
+
+
+def expert_ffn_packed(cfg: MoeConfig, x_perm, expert_offset, w1_packed, w2_packed, h, y_perm, workspace=None,
+                      stream=None):
+    """moe_expert_ffn_packed: expert_ffn on weights packed by pack_weights."""
+    n, dt = _dims(cfg), torch_dtype(cfg)
+    rows, d = n["rows"], n["d"]
+    _check(load_library().moe_expert_ffn_packed(
+        ctypes.byref(cfg), _arg(x_perm, "x_perm", dt, rows * d), _arg(expert_offset, "expert_offset", _I32, n["E"] + 1),
+        _packed_arg(cfg, w1_packed, PACK_W1), _packed_arg(cfg, w2_packed, PACK_W2), _arg(h, "h", dt, rows * cfg.d_ff),
+        _arg(y_perm, "y_perm", dt, rows * d), _arg(workspace, "workspace", None, 0), _nbytes(workspace),
+        _stream(stream)), "moe_expert_ffn_packed")
+
+
 def unpermute(cfg: MoeConfig, y_perm, slot_row, slot_w, y, *, tok_ptr=None, y_shared=None, stream=None):
     n, dt = _dims(cfg), torch_dtype(cfg)
     T, d = n["T"], n["d"]
@@ -306,6 +359,21 @@ def layer_fwd(cfg: MoeConfig, x, w_router, w1, w2, y, workspace, *, bias=None, b
               _arg(w1, "w1", dt, n["w1"]), _arg(w2, "w2", dt, n["w2"]), _arg(ws1, "ws1", dt, n["ws1"]),
               _arg(ws2, "ws2", dt, n["ws2"]), _arg(y, "y", dt, T * d), _arg(workspace, "workspace", None, 0),
               _nbytes(workspace), _stream(stream)), "moe_layer_fwd_train" if train else "moe_layer_fwd")
+
+
+def layer_fwd_packed(cfg: MoeConfig, x, w_router, w1_packed, w2_packed, y, workspace, *, bias=None,
+                     bias_stride: int = 0, ws1_packed=None, ws2_packed=None, stream=None):
+    """moe_layer_fwd_packed: layer_fwd on expert weights packed by
+    pack_weights (the router weights stay as they are)."""
+    n, dt = _dims(cfg), torch_dtype(cfg)
+    T, E, d = n["T"], n["E"], n["d"]
+    _check(load_library().moe_layer_fwd_packed(
+        ctypes.byref(cfg), _arg(x, "x", dt, T * d), _arg(w_router, "w_router", dt, E * d),
+        _arg(bias, "logit_bias", _F32, E if bias_stride == 0 else T * E), bias_stride,
+        _packed_arg(cfg, w1_packed, PACK_W1), _packed_arg(cfg, w2_packed, PACK_W2),
+        _packed_arg(cfg, ws1_packed, PACK_SHARED_W1), _packed_arg(cfg, ws2_packed, PACK_SHARED_W2),
+        _arg(y, "y", dt, T * d), _arg(workspace, "workspace", None, 0), _nbytes(workspace), _stream(stream)),
+        "moe_layer_fwd_packed")
 
 
 def layer_bwd_workspace(cfg: MoeConfig) -> Dict[str, int]:
@@ -422,10 +490,28 @@ class MoELayer:
         self.workspace = torch.empty(max(self.layout["total"], 256), dtype=torch.uint8, device=device)
         self.y = torch.empty((cfg.num_tokens, cfg.d_model), dtype=torch_dtype(cfg), device=device)
 
-    def forward(self, stream=None, train: bool = False) -> torch.Tensor:
+    def pack(self, stream=None):
+        """Packs the expert weights once (moe_pack_weights) for
+        forward(packed=True); the unpacked weights stay for training."""
+        c, d = self.cfg, self.dev
+        self.w1p = pack_weights(c, PACK_W1, d.w1, stream=stream)
+        self.w2p = pack_weights(c, PACK_W2, d.w2, stream=stream)
+        self.ws1p = None if d.ws1 is None else pack_weights(c, PACK_SHARED_W1, d.ws1, stream=stream)
+        self.ws2p = None if d.ws2 is None else pack_weights(c, PACK_SHARED_W2, d.ws2, stream=stream)
+
+    def forward(self, stream=None, train: bool = False, packed: bool = False) -> torch.Tensor:
         """moe_layer_fwd (train=True: moe_layer_fwd_train, which keeps the
-        expert pre-activations for backward(recompute=False))."""
+        expert pre-activations for backward(recompute=False); packed=True:
+        moe_layer_fwd_packed on the weights pack() prepared)."""
         d = self.dev
+        if packed:
+            if train:
+                raise ValueError("the training forward takes unpacked weights")
+            if not hasattr(self, "w1p"):
+                raise RuntimeError("forward(packed=True) needs pack() first")
+            layer_fwd_packed(self.cfg, d.x, d.wr, self.w1p, self.w2p, self.y, self.workspace, bias=d.bias,
+                             bias_stride=d.bias_stride, ws1_packed=self.ws1p, ws2_packed=self.ws2p, stream=stream)
+            return self.y
         layer_fwd(self.cfg, d.x, d.wr, d.w1, d.w2, self.y, self.workspace, bias=d.bias, bias_stride=d.bias_stride,
                   ws1=d.ws1, ws2=d.ws2, train=train, stream=stream)
         return self.y

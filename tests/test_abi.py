@@ -23,7 +23,7 @@ def test_library_exports_every_header_symbol():
 
 def test_status_strings_and_version():
     lib = moe.load_library()
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
 
@@ -53,7 +53,9 @@ def expected_ffn_workspace(dtype, avg_rows, d, d_ff):
     """K-split partial tiles: 256 of 256 x 256 fp32 for the 256-row kernel
     (>= 192 rows per expert on average, a reduction length >= 8192); 512 of
     64 x 256 fp32 for the weight-streaming kernel (<= 128 rows per expert on
-    average, K a multiple of 64)."""
+    average, K a multiple of 64).  With packable widths (d and d_ff multiples
+    of 64) the packed FFN's need counts too: it runs the 256-row kernel from
+    129 rows per expert on."""
     if dtype == W.F32:
         return 0
     need = 0
@@ -61,7 +63,70 @@ def expected_ffn_workspace(dtype, avg_rows, d, d_ff):
         need = 256 * 256 * 256 * 4
     if avg_rows <= 128 and (d % 64 == 0 or d_ff % 64 == 0):
         need = max(need, 512 * 64 * 256 * 4)
+    if d % 64 == 0 and d_ff % 64 == 0 and avg_rows > 128 and max(d, d_ff) >= 8192:
+        need = max(need, 256 * 256 * 256 * 4)
     return need
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("act,d,d_ff,dffs,E", [(1, 4096, 14336, 0, 8), (0, 192, 448, 320, 3), (1, 128, 320, 192, 5),
+                                               (0, 64, 64, 64, 1)])
+def test_packed_weight_bytes(act, d, d_ff, dffs, E):
+    """E * column tiles * (K / 32) * 16 KB; SwiGLU's W1 has tiles of 128
+    d_ff columns (gate and up rows together), every other weight tiles of
+    256 output rows."""
+    cfg = _cfg(d_model=d, num_experts=E, top_k=1, d_ff=d_ff, d_ff_shared=dffs, act=act)
+    tw = 128 if act == 1 else 256
+    assert moe.packed_weight_bytes(cfg, moe.PACK_W1) == E * _ceil(d_ff, tw) * (d // 32) * 16384
+    assert moe.packed_weight_bytes(cfg, moe.PACK_W2) == E * _ceil(d, 256) * (d_ff // 32) * 16384
+    if dffs:
+        assert moe.packed_weight_bytes(cfg, moe.PACK_SHARED_W1) == _ceil(dffs, tw) * (d // 32) * 16384
+        assert moe.packed_weight_bytes(cfg, moe.PACK_SHARED_W2) == _ceil(d, 256) * (dffs // 32) * 16384
+
+
+def test_packed_argument_errors():
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(256)
+    n = ctypes.c_size_t(0)
+    cfg = _cfg(d_ff_shared=128)
+    assert lib.moe_packed_weight_bytes(ctypes.byref(cfg), 4, ctypes.byref(n)) == 1  # unknown weight
+    assert lib.moe_packed_weight_bytes(ctypes.byref(_cfg()), moe.PACK_SHARED_W1, ctypes.byref(n)) == 1  # no shared
+    assert lib.moe_packed_weight_bytes(ctypes.byref(cfg), 0, None) == 1
+    # fp32, or a width that is not a multiple of 64: not packable
+    assert lib.moe_packed_weight_bytes(ctypes.byref(_cfg(dtype=0)), 0, ctypes.byref(n)) == 2
+    assert lib.moe_packed_weight_bytes(ctypes.byref(_cfg(d_ff=72)), 0, ctypes.byref(n)) == 2
+    assert lib.moe_packed_weight_bytes(ctypes.byref(_cfg(d_model=96)), 1, ctypes.byref(n)) == 2
+    assert lib.moe_packed_weight_bytes(ctypes.byref(_cfg(d_ff_shared=72)), 2, ctypes.byref(n)) == 2
+    assert lib.moe_packed_weight_bytes(ctypes.byref(_cfg(d_ff_shared=72)), 0, ctypes.byref(n)) == 0
+    # packing: null, aliased or misaligned buffers
+    assert lib.moe_pack_weights(ctypes.byref(cfg), 0, None, fake, None) == 1
+    assert lib.moe_pack_weights(ctypes.byref(cfg), 0, fake, None, None) == 1
+    assert lib.moe_pack_weights(ctypes.byref(cfg), 0, fake, fake, None) == 1
+    assert lib.moe_pack_weights(ctypes.byref(cfg), 0, ctypes.c_void_p(264), ctypes.c_void_p(4096), None) == 1
+    assert lib.moe_pack_weights(ctypes.byref(_cfg(dtype=0)), 0, fake, ctypes.c_void_p(4096), None) == 2
+    # the packed FFN and layer refuse configurations they cannot run
+    st = lib.moe_expert_ffn_packed(ctypes.byref(_cfg(dtype=0)), fake, fake, fake, fake, fake, fake, fake, 1 << 30,
+                                   None)
+    assert st == 2
+    st = lib.moe_expert_ffn_packed(ctypes.byref(_cfg(d_ff=200)), fake, fake, fake, fake, fake, fake, fake, 1 << 30,
+                                   None)
+    assert st == 2
+    st = lib.moe_layer_fwd_packed(ctypes.byref(_cfg(d_ff_shared=72)), fake, fake, None, 0, fake, fake, fake, fake,
+                                  fake, fake, 1 << 30, None)
+    assert st == 2
+    # missing shared-expert weights
+    st = lib.moe_layer_fwd_packed(ctypes.byref(cfg), fake, fake, None, 0, fake, fake, None, None, fake, fake,
+                                  1 << 30, None)
+    assert st == 1
+    # the binding checks the packed buffer's size before the call
+    small = torch.empty(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="needs at least"):
+        moe.expert_ffn_packed(cfg, None, None, small, small, None, None)
+    with pytest.raises(TypeError):
+        moe.pack_weights(cfg, moe.PACK_W1, torch.empty(64 * 128, dtype=torch.float32), small)
 
 
 @pytest.mark.parametrize("T,d,E,k,d_ff", [(64, 512, 8, 2, 1024), (1200, 256, 16, 1, 512), (4096, 256, 8, 2, 8192),
