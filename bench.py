@@ -167,8 +167,9 @@ def stage_functions(w, cfg, dev, layer, moe, W, torch, packed=False):
     """One callable per stage of the step-by-step path (route, permute, routed
     FFN, shared FFN, unpermute), on the intermediates of `layer`'s workspace;
     each rewrites only its own outputs, so any stage can be re-run on its own
-    once a whole step has run.  packed: the FFNs read the weights layer.pack()
-    prepared (moe_expert_ffn_packed)."""
+    once a whole step has run.  packed: the steps of moe_layer_fwd_packed
+    (moe_permute_packed writes x_perm K-blocked; the FFNs read the weights
+    layer.pack() prepared, moe_expert_ffn_packed)."""
     T, E, d = w.T, w.E, w.d
     ec = w.routing == W.EXPERT_CHOICE
     V = layer.view
@@ -201,14 +202,16 @@ def stage_functions(w, cfg, dev, layer, moe, W, torch, packed=False):
             fns.append(lambda: moe.route(cfg, dev.x, dev.wr, logits, bias=dev.bias, bias_stride=dev.bias_stride,
                                          scores=scores, ec_token=ec_token, ec_w=ec_w))
             fns.append(lambda: moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off,
-                                           ec_token=ec_token, ec_w=ec_w, slot_w=slot_w, tok_ptr=tok_ptr))
+                                           ec_token=ec_token, ec_w=ec_w, slot_w=slot_w, tok_ptr=tok_ptr,
+                                           kblocked=packed))
         else:
             fns.append(lambda: moe.route(cfg, dev.x, dev.wr, logits, topk_idx, topk_w, bias=dev.bias,
                                          bias_stride=dev.bias_stride))
             fns.append(lambda: moe.permute(cfg, dev.x, x_perm, row_token, slot_row, cnt, load, off,
-                                           topk_idx=topk_idx, scratch=scratch))
+                                           topk_idx=topk_idx, scratch=scratch, kblocked=packed))
         if packed:
-            fns.append(lambda: moe.expert_ffn_packed(cfg, x_perm, off, layer.w1p, layer.w2p, h, y_perm, ffn_ws))
+            fns.append(lambda: moe.expert_ffn_packed(cfg, x_perm, off, layer.w1p, layer.w2p, h, y_perm, ffn_ws,
+                                                     x_kblocked=True))
             if w.d_ff_shared:
                 fns.append(lambda: moe.expert_ffn_packed(scfg, dev.x, soff, layer.ws1p, layer.ws2p, hs, ys, sffn_ws))
         else:

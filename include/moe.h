@@ -226,11 +226,17 @@ moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32
  *   ((e * tiles + j) * (K / 32) + s) * 16384, whose 16-B chunk q holds row
  *   q / 4 of the tile at K elements 32 s + 8 ((q % 4) ^ ((q / 16) % 4)) .. +8.
  *   Tile rows past the weight's output width are zero.
+ * The packed path also keeps the expert activations K-blocked: a [rows, K]
+ * bf16 matrix is stored as [K/32][rows][32] (row r, column k at element
+ * ((k / 32) * rows + r) * 32 + k % 32), so a K stage of any run of
+ * consecutive rows is one contiguous block too.  moe_permute_packed writes
+ * x_perm in that order (rows = moe_max_rows()), and the packed FFN keeps h in
+ * it ([d_ff/32][rows][32]); y_perm stays row-major for moe_unpermute.
  * Requirements: dtype bf16, d_model and the FFN width (d_ff, or d_ff_shared
  * for the shared expert's weights) multiples of 64; otherwise
  * MOE_ERR_UNSUPPORTED.  Results are bitwise identical to the unpacked entry
- * points on the same weights.  Training (moe_layer_fwd_train,
- * moe_layer_bwd) takes the unpacked weights.
+ * points on the same weights (h and x_perm up to their order).  Training
+ * (moe_layer_fwd_train, moe_layer_bwd) takes the unpacked weights.
  * ------------------------------------------------------------------------ */
 typedef enum {
   MOE_PACK_W1 = 0,        /* w1 [E, n_up*d_ff, d]             */
@@ -249,12 +255,22 @@ moe_status moe_packed_weight_bytes(const moe_config *cfg, int32_t which, size_t 
  * (moe_packed_weight_bytes() bytes, caller-owned, 16-byte aligned, not
  * overlapping w; every byte is written).  w is only read. */
 moe_status moe_pack_weights(const moe_config *cfg, int32_t which, const void *w, void *packed, void *stream);
+/* moe_permute with x_perm written K-blocked ([d/32][moe_max_rows()][32]);
+ * every other output, the arguments and the scratch as moe_permute. */
+moe_status moe_permute_packed(const moe_config *cfg, const void *x, const int32_t *topk_idx,
+                              const int32_t *ec_token, const float *ec_w, void *x_perm, int32_t *row_token,
+                              int32_t *slot_row, float *slot_w, int32_t *tok_ptr, int32_t *expert_count,
+                              int32_t *expert_load, int32_t *expert_offset, void *scratch, size_t scratch_bytes,
+                              void *stream);
 /* moe_expert_ffn on packed weights: w1_packed / w2_packed from
- * moe_pack_weights(MOE_PACK_W1 / MOE_PACK_W2); every other argument, the
- * workspace size and the results as moe_expert_ffn. */
-moe_status moe_expert_ffn_packed(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
-                                 const void *w1_packed, const void *w2_packed, void *h, void *y_perm,
-                                 void *workspace, size_t workspace_bytes, void *stream);
+ * moe_pack_weights(MOE_PACK_W1 / MOE_PACK_W2); x_perm_kblocked = 1 when
+ * x_perm is K-blocked (moe_permute_packed), 0 when it is row-major
+ * [rows, d] (moe_permute, or x itself for the shared expert; other values:
+ * MOE_ERR_INVALID_ARG).  h (same size as for moe_expert_ffn) is written
+ * K-blocked.  y_perm, the workspace size and the results as moe_expert_ffn. */
+moe_status moe_expert_ffn_packed(const moe_config *cfg, const void *x_perm, int32_t x_perm_kblocked,
+                                 const int32_t *expert_offset, const void *w1_packed, const void *w2_packed,
+                                 void *h, void *y_perm, void *workspace, size_t workspace_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
  * moe_unpermute -- [P1] "Token Dispatching and Communication"
@@ -311,8 +327,10 @@ moe_status moe_layer_fwd(const moe_config *cfg, const void *x, const void *w_rou
                          void *workspace, size_t workspace_bytes, void *stream);
 /* moe_layer_fwd on packed expert weights (moe_pack_weights: MOE_PACK_W1,
  * MOE_PACK_W2, and for a shared expert MOE_PACK_SHARED_W1 / _W2); the router
- * weights stay unpacked.  Workspace (moe_layer_workspace) and results as
- * moe_layer_fwd. */
+ * weights stay unpacked.  Its steps are moe_route, moe_permute_packed and
+ * moe_expert_ffn_packed (the workspace's x_perm and h regions then hold
+ * K-blocked matrices), the shared expert's moe_expert_ffn_packed on x and
+ * moe_unpermute.  Workspace (moe_layer_workspace) and y as moe_layer_fwd. */
 moe_status moe_layer_fwd_packed(const moe_config *cfg, const void *x, const void *w_router,
                                 const float *logit_bias, int64_t bias_row_stride, const void *w1_packed,
                                 const void *w2_packed, const void *ws1_packed, const void *ws2_packed, void *y,

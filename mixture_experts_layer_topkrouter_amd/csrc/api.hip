@@ -115,8 +115,9 @@ moe_status route_impl(const moe_config *cfg, const void *x, const void *w_router
 moe_status permute_impl(const moe_config *cfg, const void *x, const int32_t *topk_idx, const int32_t *ec_token,
                         const float *ec_w, void *x_perm, int32_t *row_token, int32_t *slot_row, float *slot_w,
                         int32_t *tok_ptr, int32_t *expert_count, int32_t *expert_load, int32_t *expert_offset,
-                        void *scratch, size_t scratch_bytes, void *stream) {
+                        void *scratch, size_t scratch_bytes, void *stream, bool kblocked = false) {
   if (!expert_count || !expert_load || !expert_offset) return MOE_ERR_INVALID_ARG;
+  const int64_t kb_rows = kblocked ? max_rows_of(cfg) : 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool empty = cfg->num_tokens == 0;  // only the (zero) counts and offsets are written
   if (!empty && (!x || !x_perm || !row_token || !slot_row)) return MOE_ERR_INVALID_ARG;
@@ -139,6 +140,7 @@ moe_status permute_impl(const moe_config *cfg, const void *x, const int32_t *top
     a.expert_load = expert_load;
     a.expert_offset = expert_offset;
     a.slot_w = slot_w;
+    a.kb_rows = kb_rows;
     return hip_status(moe::launch_permute_ec(a, st));
   }
   if (!empty && !topk_idx) return MOE_ERR_INVALID_ARG;
@@ -161,6 +163,7 @@ moe_status permute_impl(const moe_config *cfg, const void *x, const int32_t *top
   a.expert_count = expert_count;
   a.expert_load = expert_load;
   a.expert_offset = expert_offset;
+  a.kb_rows = kb_rows;
   a.blk = static_cast<int32_t *>(scratch);
   a.rank = reinterpret_cast<int32_t *>(static_cast<char *>(scratch) +
                                        align256(static_cast<size_t>(nblk * cfg->num_experts) * 4));
@@ -200,7 +203,7 @@ size_t ffn_scratch_of(const moe_config *c) {
 
 moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset, const void *w1,
                     const void *w2, void *h, void *y_perm, void *workspace, size_t workspace_bytes,
-                    void *stream, void *z = nullptr, bool packed = false) {
+                    void *stream, void *z = nullptr, bool packed = false, bool x_kblocked = false) {
   if (packed && (!packable(cfg, cfg->d_ff) || z)) return MOE_ERR_UNSUPPORTED;
   if (max_rows_of(cfg) == 0) return MOE_OK;  // no rows: nothing to compute, empty buffers may be NULL
   if (!x_perm || !expert_offset || !w1 || !w2 || !h || !y_perm) return MOE_ERR_INVALID_ARG;
@@ -228,6 +231,7 @@ moe_status ffn_impl(const moe_config *cfg, const void *x_perm, const int32_t *ex
   a.scratch_bytes = workspace_bytes;
   a.z = z;
   a.packed = packed;
+  a.x_kb = packed && x_kblocked;
   return hip_status(moe::launch_expert_ffn(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -604,10 +608,11 @@ moe_status layer_fwd_impl(const moe_config *cfg, const void *x, const void *w_ro
   if (s != MOE_OK) return s;
   s = permute_impl(cfg, x, topk_idx, ec_token, ec_w, P(L.x_perm), static_cast<int32_t *>(P(L.row_token)), slot_row,
                    static_cast<float *>(P(L.slot_w)), tok_ptr, static_cast<int32_t *>(P(L.expert_count)),
-                   static_cast<int32_t *>(P(L.expert_load)), expert_offset, P(L.scratch), L.scratch_bytes, stream);
+                   static_cast<int32_t *>(P(L.expert_load)), expert_offset, P(L.scratch), L.scratch_bytes, stream,
+                   packed);
   if (s != MOE_OK) return s;
   s = ffn_impl(cfg, P(L.x_perm), expert_offset, w1, w2, P(L.h), P(L.y_perm), P(L.ffn_scratch),
-               L.ffn_scratch_bytes, stream, train ? P(L.z) : nullptr, packed);
+               L.ffn_scratch_bytes, stream, train ? P(L.z) : nullptr, packed, packed);
   if (s != MOE_OK) return s;
   if (join && hipStreamWaitEvent(main_st, join, 0) != hipSuccess) return MOE_ERR_HIP;
   return unpermute_impl(cfg, P(L.y_perm), tok_ptr, slot_row, slot_w, y_shared, y, stream,
@@ -671,6 +676,17 @@ moe_status moe_permute(const moe_config *cfg, const void *x, const int32_t *topk
                       expert_count, expert_load, expert_offset, scratch, scratch_bytes, stream);
 }
 
+moe_status moe_permute_packed(const moe_config *cfg, const void *x, const int32_t *topk_idx, const int32_t *ec_token,
+                              const float *ec_w, void *x_perm, int32_t *row_token, int32_t *slot_row, float *slot_w,
+                              int32_t *tok_ptr, int32_t *expert_count, int32_t *expert_load, int32_t *expert_offset,
+                              void *scratch, size_t scratch_bytes, void *stream) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if (!packable(cfg, cfg->d_ff)) return MOE_ERR_UNSUPPORTED;
+  return permute_impl(cfg, x, topk_idx, ec_token, ec_w, x_perm, row_token, slot_row, slot_w, tok_ptr,
+                      expert_count, expert_load, expert_offset, scratch, scratch_bytes, stream, true);
+}
+
 moe_status moe_permute_noalloc(const moe_config *cfg, const void *x, const int32_t *topk_idx,
                                const int32_t *ec_token, const float *ec_w, void *x_perm, int32_t *row_token,
                                int32_t *slot_row, float *slot_w, int32_t *tok_ptr, int32_t *expert_count,
@@ -724,13 +740,14 @@ moe_status moe_pack_weights(const moe_config *cfg, int32_t which, const void *w,
   return hip_status(moe::launch_pack_weights(a, static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_expert_ffn_packed(const moe_config *cfg, const void *x_perm, const int32_t *expert_offset,
-                                 const void *w1_packed, const void *w2_packed, void *h, void *y_perm,
-                                 void *workspace, size_t workspace_bytes, void *stream) {
+moe_status moe_expert_ffn_packed(const moe_config *cfg, const void *x_perm, int32_t x_perm_kblocked,
+                                 const int32_t *expert_offset, const void *w1_packed, const void *w2_packed, void *h,
+                                 void *y_perm, void *workspace, size_t workspace_bytes, void *stream) {
   moe_status s = check_config(cfg);
   if (s != MOE_OK) return s;
+  if (x_perm_kblocked != 0 && x_perm_kblocked != 1) return MOE_ERR_INVALID_ARG;
   return ffn_impl(cfg, x_perm, expert_offset, w1_packed, w2_packed, h, y_perm, workspace, workspace_bytes, stream,
-                  nullptr, true);
+                  nullptr, true, x_perm_kblocked == 1);
 }
 
 moe_status moe_unpermute(const moe_config *cfg, const void *y_perm, const int32_t *tok_ptr,

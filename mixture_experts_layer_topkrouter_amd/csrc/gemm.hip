@@ -384,7 +384,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   // tile's first column); a stage advances them by a_step / b_step bytes
   const int64_t kfirst = static_cast<int64_t>(job.k0) + static_cast<int64_t>(job.kb) * DK;
   const char *A = static_cast<const char *>(p.A) +
-                  (AT ? kfirst * p.lda + row0 : static_cast<int64_t>(row0) * p.lda + job.kb * DK) * 2;
+                  (AT ? kfirst * p.lda + row0 : static_cast<int64_t>(row0) * p.lda + job.kb * DK) * 2;  // K-blocked: below
   // packed B: the stage blocks of column tile nt follow each other, 16 KB
   // apart, and a stage is read as one contiguous block
   static_assert(kPackK == DK && kPackBlockBytes == DSTAGE * 2, "a packed block is one B stage");
@@ -395,7 +395,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
                           : (BT ? (LAY == LAY_TN ? 0 : static_cast<int64_t>(e) * p.b_stride) + kfirst * p.ldb +
                                       static_cast<int64_t>(nt) * BN
                                 : static_cast<int64_t>(e) * p.b_stride + job.kb * DK) * 2);
-  const int64_t a_step = AT ? static_cast<int64_t>(DK) * p.lda * 2 : DK * 2;
+  // K-blocked A: the tile's K stage is the 256 row pieces starting at row0
+  // of the stage's 32-wide slice
+  static_assert(kKbRowBytes == DK * 2, "a K-blocked row piece is one stage of one row");
+  const bool a_kb = LAY == LAY_NT && p.a_kb;
+  if (a_kb) A = static_cast<const char *>(p.A) + (static_cast<int64_t>(job.kb) * p.max_rows + row0) * kKbRowBytes;
+  const int64_t a_step = a_kb ? p.max_rows * kKbRowBytes : AT ? static_cast<int64_t>(DK) * p.lda * 2 : DK * 2;
   const int64_t b_step = packed ? kPackBlockBytes : BT ? static_cast<int64_t>(DK) * p.ldb * 2 : DK * 2;
 
   auto slot = [&](auto S) -> uint16_t * {
@@ -427,7 +432,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
       const int col = min(tc * 8, p.m_rows - row0 - 8);
       a_off[i] = static_cast<uint32_t>((static_cast<int64_t>(kk) * p.lda + col) * 2);
     } else {
-      a_off[i] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
+      a_off[i] = a_kb ? static_cast<uint32_t>(min(r, rows - 1) * kKbRowBytes + c * 16)
+                      : static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
     }
     if constexpr (BT) {
       const int col = min(tc * 8, p.n_out - nt * BN - 8);
@@ -729,13 +735,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   constexpr int CHUNKS = OUT_COLS / 8;  // 16-byte chunks per row
   const int col0 = nt * OUT_COLS;
   uint8_t *C = static_cast<uint8_t *>(p.C) + (LAY == LAY_TN ? static_cast<int64_t>(e) * p.c_stride * 2 : 0);
+  // non-temporal stores: the tile is not read again by this kernel, and its
+  // lines would push the operands that the tiles running beside it share out
+  // of L2 (correlated workloads: FFN 4-9 % faster; the others unchanged)
+  if (LAY == LAY_NT && p.c_kb) {
+    // K-blocked output: thread q takes chunk q%4 of row (q/4)%DBM in the
+    // tile's 32-column slice q/(4 DBM), so a wave stores 16 whole row pieces,
+    // 1 KB contiguous
+    for (int q = threadIdx.x; q < DBM * CHUNKS; q += NTH) {
+      const int c4 = q & 3, r = (q >> 2) & (DBM - 1), kbl = q / (4 * DBM);
+      const int col = col0 + kbl * 32 + c4 * 8;
+      if (r >= rows || col >= p.n_out) continue;
+      const u32x4 val = *reinterpret_cast<const u32x4 *>(ep + r * PITCH + (kbl * 4 + c4) * 16);
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(C + c_index(p, row0 + r, col) * 2));
+    }
+    return;
+  }
   for (int q = threadIdx.x; q < DBM * CHUNKS; q += NTH) {
     const int r = q / CHUNKS, c = q - (q / CHUNKS) * CHUNKS;
     if (r >= rows || col0 + c * 8 >= p.n_out) continue;
     const u32x4 val = *reinterpret_cast<const u32x4 *>(ep + r * PITCH + c * 16);
-    // non-temporal: the tile is not read again by this kernel, and its lines
-    // would push the operands that the tiles running beside it share out of
-    // L2 (correlated workloads: FFN 4-9 % faster; the others unchanged)
     __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(C + (static_cast<int64_t>(row0 + r) * p.ldc + col0 + c * 8) * 2));
   }
 }
@@ -781,7 +800,7 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
     for (int r = 0; r < 4; ++r) {
       if (r0 + r >= rows) continue;
       const float v = ACT == ACT_SWIGLU ? silu_fast(a[r]) * u[r] : (ACT == ACT_GELU ? gelu_erf(a[r]) : a[r]);
-      C[static_cast<int64_t>(row0 + r0 + r) * p.ldc + col] = f32_to_bf16(v);
+      C[c_index(p, row0 + r0 + r, col)] = f32_to_bf16(v);
     }
   }
 }
@@ -1004,6 +1023,7 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   // kernel that reads the packed order
   if (a.packed && (a.dtype != 1 || a.z || a.d % 64 || a.d_ff % 64 || !(f.dma1 || f.sk1) || !(f.dma2 || f.sk2)))
     return hipErrorInvalidValue;
+  if (a.x_kb && !a.packed) return hipErrorInvalidValue;
   float *part = static_cast<float *>(a.scratch);
   const int units = round_units();
   const int slots = static_cast<int>(std::min<size_t>(kSplitUnits, need / kPartTileBytes));
@@ -1019,6 +1039,8 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   g1.b_stride = a.packed ? static_cast<int64_t>(packed_weight_bytes(1, a.d_ff, a.d, a.act == 1) / 2)
                          : static_cast<int64_t>(n_up) * a.d_ff * a.d;
   g1.packed = a.packed;
+  g1.a_kb = a.x_kb;
+  g1.c_kb = a.packed;  // h K-blocked: GEMM2 reads its stages contiguously
   g1.C = a.h;
   g1.ldc = a.d_ff;
   g1.offs = a.expert_offset;
@@ -1064,6 +1086,7 @@ hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st) {
   g2.b_stride = a.packed ? static_cast<int64_t>(packed_weight_bytes(1, a.d, a.d_ff, false) / 2)
                          : static_cast<int64_t>(a.d) * a.d_ff;
   g2.packed = a.packed;
+  g2.a_kb = a.packed;
   g2.C = a.y_perm;
   g2.ldc = a.d;
   g2.offs = a.expert_offset;

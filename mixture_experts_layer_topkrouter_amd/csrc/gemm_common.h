@@ -40,7 +40,21 @@ struct GemmParams {
   // launch_pack_weights (b_stride then counts the packed elements of one
   // expert; ldb and up_off are not used)
   int packed;
+  // forward (NT) only, bf16: A is read / C is written K-blocked (row r,
+  // column k at ((k / 32) * max_rows + r) * 32 + k % 32; lda / ldc unused)
+  int a_kb, c_kb;
 };
+
+// Element index of (row, col) in an output: row-major with pitch ldc, or
+// K-blocked over max_rows rows.
+__device__ __forceinline__ int64_t c_index(const GemmParams &p, int64_t row, int col) {
+  return p.c_kb ? (static_cast<int64_t>(col >> 5) * p.max_rows + row) * 32 + (col & 31) : row * p.ldc + col;
+}
+
+// K-blocked activations ([K/32][rows][32] bf16): the 32-wide K slice of
+// consecutive rows is contiguous, so a tile's K stage is one contiguous run
+// of 64-B row pieces whatever row the tile starts on.
+constexpr int kKbRowBytes = 64;
 
 // Packed weights: per expert, per column tile of BN weight rows (SwiGLU: the
 // tile's BN/2 gate rows, then the matching BN/2 up rows), per 32-wide slice

@@ -94,7 +94,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
   if (!skinny_job<BM>(p, p.K / SK, &job)) return;
   const int rows = job.rows, nt = job.nt;
   const int l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
-  const char *A = static_cast<const char *>(p.A) + (static_cast<int64_t>(job.row0) * p.lda + job.kb * SK) * 2;
+  // K-blocked A: a 64-wide stage is two 32-wide slices, max_rows row pieces
+  // apart
+  static_assert(SK * 2 == 2 * kKbRowBytes, "a stage row is two K-blocked row pieces");
+  const bool a_kb = p.a_kb != 0;
+  const int64_t kb_slice = p.max_rows * kKbRowBytes;  // bytes between consecutive 32-wide slices
+  const char *A = static_cast<const char *>(p.A) +
+                  (a_kb ? 2 * job.kb * kb_slice + static_cast<int64_t>(job.row0) * kKbRowBytes
+                        : (static_cast<int64_t>(job.row0) * p.lda + job.kb * SK) * 2);
+  const int64_t a_step = a_kb ? 2 * kb_slice : SK * 2;
   // packed B: a 64-wide stage is the column tile's two consecutive 32-wide
   // blocks, 32 KB contiguous
   static_assert(SK == 2 * kPackK && SBN == BN, "a stage is two packed blocks of one column tile");
@@ -115,7 +123,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
   for (int i = 0; i < C::A_INSTR; ++i) {
     const int r = 8 * (w + 4 * i) + (l >> 3);
     const int c = (l & 7) ^ ((r >> 1) & 7);
-    a_off[i] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
+    a_off[i] = a_kb ? static_cast<uint32_t>((c >> 2) * kb_slice + min(r, rows - 1) * kKbRowBytes + (c & 3) * 16)
+                    : static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
   }
 #pragma unroll
   for (int i = 0; i < C::B_INSTR; ++i) {
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
   auto issue = [&](auto S, int st) {
     const uint32_t base = lds_addr_of(slot(S));
 #pragma unroll
-    for (int i = 0; i < C::A_INSTR; ++i) dma16(a_off[i], A + st * SK * 2, base + (w + 4 * i) * 1024);
+    for (int i = 0; i < C::A_INSTR; ++i) dma16(a_off[i], A + st * a_step, base + (w + 4 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_INSTR; ++i)
       if constexpr (BNT) dma16_nt(b_off[i], B + st * b_step, base + C::A_ELEMS * 2 + (w + 4 * i) * 1024);
@@ -229,16 +238,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
     for (int v = 0; v < 16; ++v) {
       const int r = i * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
       if (r >= rows) continue;
-      uint16_t *crow = Cp + static_cast<int64_t>(job.row0 + r) * p.ldc;
+      const int64_t grow = job.row0 + r;
       if (ACT == ACT_SWIGLU) {
         const int col = nt * (SBN / 2) + w * 32 + (l & 31);
-        if (col < p.n_out) crow[col] = f32_to_bf16(silu_fast(acc[i][0][v]) * acc[i][1][v]);
+        if (col < p.n_out) Cp[c_index(p, grow, col)] = f32_to_bf16(silu_fast(acc[i][0][v]) * acc[i][1][v]);
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const int col = nt * SBN + w * 64 + j * 32 + (l & 31);
           const float x = acc[i][j][v];
-          if (col < p.n_out) crow[col] = f32_to_bf16(ACT == ACT_GELU ? gelu_erf(x) : x);
+          if (col < p.n_out) Cp[c_index(p, grow, col)] = f32_to_bf16(ACT == ACT_GELU ? gelu_erf(x) : x);
         }
       }
     }
@@ -283,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void skinny_reduce_kernel(GemmParams p) {
     for (int r = 0; r < 4; ++r) {
       if (r0 + r >= rows) continue;
       const float v = ACT == ACT_SWIGLU ? silu_fast(a[r]) * u[r] : (ACT == ACT_GELU ? gelu_erf(a[r]) : a[r]);
-      Cp[static_cast<int64_t>(row0 + r0 + r) * p.ldc + col] = f32_to_bf16(v);
+      Cp[c_index(p, row0 + r0 + r, col)] = f32_to_bf16(v);
     }
   }
 }

@@ -39,6 +39,7 @@ struct PermuteArgs {
   int32_t *row_token, *slot_row, *expert_count, *expert_load, *expert_offset;
   int32_t *blk;             // scratch [nblk][E]
   int32_t *rank;            // scratch [T*k]
+  int64_t kb_rows;          // > 0: x_perm K-blocked over this many rows ([d/32][kb_rows][32])
 };
 size_t permute_scratch_bytes(int T, int k, int E);
 hipError_t launch_permute_topk(const PermuteArgs &a, hipStream_t st);
@@ -52,6 +53,7 @@ struct PermuteEcArgs {
   void *x_perm;
   int32_t *row_token, *slot_row, *tok_ptr, *expert_count, *expert_load, *expert_offset;
   float *slot_w;
+  int64_t kb_rows;  // > 0: x_perm K-blocked, as in PermuteArgs
 };
 hipError_t launch_permute_ec(const PermuteEcArgs &a, hipStream_t st);
 
@@ -67,7 +69,9 @@ struct FfnArgs {
   size_t scratch_bytes;
   void *z;        // optional [max_rows, n_up*d_ff]: keep the pre-activations
   bool packed;    // w1 / w2 in the packed order of launch_pack_weights (bf16,
-                  // d and d_ff multiples of 64, no z)
+                  // d and d_ff multiples of 64, no z); h is then K-blocked
+                  // ([d_ff/32][max_rows][32])
+  bool x_kb;      // packed only: x_perm K-blocked ([d/32][max_rows][32])
 };
 size_t ffn_scratch_bytes(int dtype, int E, int d, int d_ff, int64_t max_rows, bool packed = false);
 hipError_t launch_expert_ffn(const FfnArgs &a, hipStream_t st);

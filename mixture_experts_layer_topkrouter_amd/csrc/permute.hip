@@ -46,6 +46,16 @@ __device__ __forceinline__ u32x4 ld16_stream(const void *p) {
 }
 constexpr int kGroups = kPermuteBlock / kWave;  // 16 groups of 64 per block
 
+// Address of 16-B chunk c of permuted row `row`: row-major rows of row_bytes,
+// or (kb_rows > 0, bf16) K-blocked over kb_rows rows, where the four chunks
+// c = 4 s .. 4 s + 3 of every row (its 32-wide K slice s) lie together and
+// the slices of consecutive rows follow each other.
+__device__ __forceinline__ uint8_t *xp_chunk(uint8_t *x_perm, size_t row_bytes, int64_t kb_rows, int64_t row,
+                                             int c) {
+  return kb_rows > 0 ? x_perm + ((static_cast<int64_t>(c >> 2) * kb_rows + row) * 4 + (c & 3)) * 16
+                     : x_perm + static_cast<size_t>(row) * row_bytes + static_cast<size_t>(c) * 16;
+}
+
 __global__ __launch_bounds__(kThreads) void count_kernel(const int32_t *__restrict__ idx, int64_t A, int E,
                                                          int ebits, int32_t *__restrict__ blk,
                                                          int32_t *__restrict__ rank) {
@@ -125,7 +135,7 @@ constexpr int kScatterTokens = kThreads / kWave;  // one wave per token
 // each of the token's kept rows (row of slot j in lane j).
 template <int CPL>
 __device__ __forceinline__ void copy_row(const uint8_t *__restrict__ x, size_t row_bytes, int t, int k, int row,
-                                         uint8_t *__restrict__ x_perm, int c_begin = 0) {
+                                         uint8_t *__restrict__ x_perm, int64_t kb_rows, int c_begin = 0) {
   const int l = lane_id();
   if (__ballot(row >= 0) == 0) return;  // every slot dropped: the row is not read
   const int nchunk = static_cast<int>(row_bytes / 16);
@@ -140,11 +150,10 @@ __device__ __forceinline__ void copy_row(const uint8_t *__restrict__ x, size_t r
     for (int j = 0; j < k; ++j) {
       const int rj = __shfl(row, j, kWave);
       if (rj < 0) continue;
-      uint8_t *dst = x_perm + static_cast<size_t>(rj) * row_bytes;
 #pragma unroll
       for (int u = 0; u < CPL; ++u) {
         const int c = c0 + u * kWave + l;
-        if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
+        if (c < nchunk) st16(xp_chunk(x_perm, row_bytes, kb_rows, rj, c), v[u]);
       }
     }
   }
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
     const uint8_t *__restrict__ x, size_t row_bytes, const int32_t *__restrict__ idx, int T, int k, int E,
     int64_t cap, const int32_t *__restrict__ blk, const int32_t *__restrict__ rank,
     const int32_t *__restrict__ expert_offset, uint8_t *__restrict__ x_perm, int32_t *__restrict__ row_token,
-    int32_t *__restrict__ slot_row) {
+    int32_t *__restrict__ slot_row, int64_t kb_rows) {
   const int t = blockIdx.x * kScatterTokens + wave_id();
   if (t >= T) return;
   const int l = lane_id();
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(
     }
     slot_row[a] = row;
   }
-  copy_row<CPL>(x, row_bytes, t, k, row, x_perm);
+  copy_row<CPL>(x, row_bytes, t, k, row, x_perm, kb_rows);
 }
 
 // Scan and scatter in one launch, for histogram tables of at most
@@ -187,7 +196,8 @@ __global__ __launch_bounds__(kFusedThreads) void scan_scatter_kernel(
     const uint8_t *__restrict__ x, size_t row_bytes, const int32_t *__restrict__ idx, int T, int k, int E,
     int64_t cap, const int32_t *__restrict__ blk, int nblk, const int32_t *__restrict__ rank,
     int32_t *__restrict__ expert_count, int32_t *__restrict__ expert_load, int32_t *__restrict__ expert_offset,
-    uint8_t *__restrict__ x_perm, int32_t *__restrict__ row_token, int32_t *__restrict__ slot_row) {
+    uint8_t *__restrict__ x_perm, int32_t *__restrict__ row_token, int32_t *__restrict__ slot_row,
+    int64_t kb_rows) {
   __shared__ int tab[kFusedTable];
   __shared__ int offs[kMaxExperts + 1];
   __shared__ int tmp[kFusedThreads / kWave + 1];
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(kFusedThreads) void scan_scatter_kernel(
     }
     slot_row[a] = row;
   }
-  copy_row<CPL>(x, row_bytes, t, k, row, x_perm);
+  copy_row<CPL>(x, row_bytes, t, k, row, x_perm, kb_rows);
 }
 
 // One launch for at most kSelfCount assignments: each workgroup (16 tokens,
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(kFusedThreads) void count_scatter_kernel(
     const uint8_t *__restrict__ x, size_t row_bytes, const int32_t *__restrict__ idx, int T, int k, int E,
     int ebits, int64_t cap, int32_t *__restrict__ expert_count, int32_t *__restrict__ expert_load,
     int32_t *__restrict__ expert_offset, uint8_t *__restrict__ x_perm, int32_t *__restrict__ row_token,
-    int32_t *__restrict__ slot_row) {
+    int32_t *__restrict__ slot_row, int64_t kb_rows) {
   __shared__ int base[kMaxExperts], total[kMaxExperts], offs[kMaxExperts + 1];
   __shared__ int tmp[kFusedThreads / kWave + 1];
   __shared__ int own[kFusedTokens * kMaxTopK];
@@ -348,14 +358,13 @@ __global__ __launch_bounds__(kFusedThreads) void count_scatter_kernel(
   for (int j = 0; j < k; ++j) {
     const int rj = __shfl(row, j, kWave);
     if (rj < 0) continue;
-    uint8_t *dst = x_perm + static_cast<size_t>(rj) * row_bytes;
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
       const int c = u * kWave + l;
-      if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
+      if (c < nchunk) st16(xp_chunk(x_perm, row_bytes, kb_rows, rj, c), v[u]);
     }
   }
-  if (nchunk > CPL * kWave) copy_row<CPL>(x, row_bytes, t, k, row, x_perm, CPL * kWave);
+  if (nchunk > CPL * kWave) copy_row<CPL>(x, row_bytes, t, k, row, x_perm, kb_rows, CPL * kWave);
 }
 
 // ---------------------------------------------------------------- ExpertChoice
@@ -388,7 +397,7 @@ __global__ __launch_bounds__(kFusedThreads) void ec_permute_kernel(
     const float *__restrict__ ec_w, int T, int E, int C, uint8_t *__restrict__ x_perm,
     int32_t *__restrict__ row_token, int32_t *__restrict__ slot_row, float *__restrict__ slot_w,
     int32_t *__restrict__ tok_ptr, int32_t *__restrict__ expert_count, int32_t *__restrict__ expert_load,
-    int32_t *__restrict__ expert_offset) {
+    int32_t *__restrict__ expert_offset, int64_t kb_rows) {
   __shared__ int p0[kMaxExperts], p1[kMaxExperts];
   __shared__ uint32_t mask[kEcPermTokens][kEcMaskWords];
   __shared__ int tok_off[kEcPermTokens + 1];
@@ -466,11 +475,11 @@ __global__ __launch_bounds__(kFusedThreads) void ec_permute_kernel(
   int cnt = 0;
   for (int q = 0; q < kEcMaskWords; ++q) cnt += __popc(mask[w][q]);
   for (int j = 0; j < cnt; ++j) {
-    uint8_t *dst = x_perm + static_cast<size_t>(rows_of[w][j]) * row_bytes;
+    const int rj = rows_of[w][j];
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
       const int c = u * kWave + l;
-      if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
+      if (c < nchunk) st16(xp_chunk(x_perm, row_bytes, kb_rows, rj, c), v[u]);
     }
   }
   if (nchunk > CPL * kWave) {
@@ -483,11 +492,11 @@ __global__ __launch_bounds__(kFusedThreads) void ec_permute_kernel(
         if (c < nchunk) v[u] = ld16_stream(src + static_cast<size_t>(c) * 16);
       }
       for (int j = 0; j < cnt; ++j) {
-        uint8_t *dst = x_perm + static_cast<size_t>(rows_of[w][j]) * row_bytes;
+        const int rj = rows_of[w][j];
 #pragma unroll
         for (int u = 0; u < CPL; ++u) {
           const int c = c0 + u * kWave + l;
-          if (c < nchunk) st16(dst + static_cast<size_t>(c) * 16, v[u]);
+          if (c < nchunk) st16(xp_chunk(x_perm, row_bytes, kb_rows, rj, c), v[u]);
         }
       }
     }
@@ -518,7 +527,8 @@ hipError_t launch_permute_topk(const PermuteArgs &a, hipStream_t st) {
 #define MOE_COUNT_SCATTER(CPL)                                                                                 \
   count_scatter_kernel<CPL><<<blocks, kFusedThreads, 0, st>>>(x, a.row_bytes, a.topk_idx, a.T, a.k, a.E, ebits, \
                                                               a.cap, a.expert_count, a.expert_load,             \
-                                                              a.expert_offset, xp, a.row_token, a.slot_row)
+                                                              a.expert_offset, xp, a.row_token, a.slot_row,     \
+                                                              a.kb_rows)
     if (per_lane <= 2) MOE_COUNT_SCATTER(2);
     else if (per_lane <= 4) MOE_COUNT_SCATTER(4);
     else MOE_COUNT_SCATTER(8);
@@ -532,7 +542,7 @@ hipError_t launch_permute_topk(const PermuteArgs &a, hipStream_t st) {
   scan_scatter_kernel<CPL><<<blocks, kFusedThreads, 0, st>>>(x, a.row_bytes, a.topk_idx, a.T, a.k, a.E, a.cap, \
                                                              a.blk, nblk, a.rank, a.expert_count,              \
                                                              a.expert_load, a.expert_offset, xp, a.row_token,  \
-                                                             a.slot_row)
+                                                             a.slot_row, a.kb_rows)
     if (per_lane <= 2) MOE_SCAN_SCATTER(2);
     else if (per_lane <= 4) MOE_SCAN_SCATTER(4);
     else MOE_SCAN_SCATTER(8);
@@ -545,7 +555,8 @@ hipError_t launch_permute_topk(const PermuteArgs &a, hipStream_t st) {
     const int blocks = (a.T + kScatterTokens - 1) / kScatterTokens;
 #define MOE_SCATTER(CPL)                                                                                      \
   scatter_kernel<CPL><<<blocks, kThreads, 0, st>>>(x, a.row_bytes, a.topk_idx, a.T, a.k, a.E, a.cap, a.blk,   \
-                                                   a.rank, a.expert_offset, xp, a.row_token, a.slot_row)
+                                                   a.rank, a.expert_offset, xp, a.row_token, a.slot_row,       \
+                                                   a.kb_rows)
     if (per_lane <= 2) MOE_SCATTER(2);
     else if (per_lane <= 4) MOE_SCATTER(4);
     else MOE_SCATTER(8);
@@ -562,7 +573,7 @@ hipError_t launch_permute_ec(const PermuteEcArgs &a, hipStream_t st) {
 #define MOE_EC_PERMUTE(CPL)                                                                                     \
   ec_permute_kernel<CPL><<<blocks > 0 ? blocks : 1, kFusedThreads, 0, st>>>(                                   \
       x, a.row_bytes, a.ec_token, a.ec_w, a.T, a.E, a.C, xp, a.row_token, a.slot_row, a.slot_w, a.tok_ptr,     \
-      a.expert_count, a.expert_load, a.expert_offset)
+      a.expert_count, a.expert_load, a.expert_offset, a.kb_rows)
   if (per_lane <= 2) MOE_EC_PERMUTE(2);
   else if (per_lane <= 4) MOE_EC_PERMUTE(4);
   else MOE_EC_PERMUTE(8);

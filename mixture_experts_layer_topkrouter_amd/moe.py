@@ -109,7 +109,8 @@ def load_library() -> ctypes.CDLL:
         "moe_layer_fwd": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_packed_weight_bytes": ([CP, ctypes.c_int32, ctypes.POINTER(sz)], ctypes.c_int),
         "moe_pack_weights": ([CP, ctypes.c_int32, P, P, P], ctypes.c_int),
-        "moe_expert_ffn_packed": ([CP, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "moe_permute_packed": ([CP, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "moe_expert_ffn_packed": ([CP, P, ctypes.c_int32, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_layer_fwd_packed": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "moe_layer_bwd_workspace": ([CP, ctypes.POINTER(BwdLayout)], ctypes.c_int),
         "moe_layer_fwd_train": ([CP, P, P, P, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
@@ -230,17 +231,23 @@ def permute_scratch_bytes(cfg: MoeConfig) -> int:
 
 
 def permute(cfg: MoeConfig, x, x_perm, row_token, slot_row, expert_count, expert_load, expert_offset, *,
-            topk_idx=None, ec_token=None, ec_w=None, slot_w=None, tok_ptr=None, scratch=None, stream=None):
+            topk_idx=None, ec_token=None, ec_w=None, slot_w=None, tok_ptr=None, scratch=None, stream=None,
+            kblocked: bool = False):
+    """moe_permute, or moe_permute_packed (x_perm written K-blocked,
+    [d/32][rows][32]) when kblocked is set."""
     n, dt = _dims(cfg), torch_dtype(cfg)
     T, E, d, rows = n["T"], n["E"], n["d"], n["rows"]
-    _check(load_library().moe_permute(
+    lib = load_library()
+    fn = lib.moe_permute_packed if kblocked else lib.moe_permute
+    _check(fn(
         ctypes.byref(cfg), _arg(x, "x", dt, T * d), _arg(topk_idx, "topk_idx", _I32, T * n["k"]),
         _arg(ec_token, "ec_token", _I32, E * n["C"]), _arg(ec_w, "ec_w", _F32, E * n["C"]),
         _arg(x_perm, "x_perm", dt, rows * d), _arg(row_token, "row_token", _I32, rows),
         _arg(slot_row, "slot_row", _I32, n["slots"]), _arg(slot_w, "slot_w", _F32, n["slots"]),
         _arg(tok_ptr, "tok_ptr", _I32, T + 1), _arg(expert_count, "expert_count", _I32, E),
         _arg(expert_load, "expert_load", _I32, E), _arg(expert_offset, "expert_offset", _I32, E + 1),
-        _arg(scratch, "scratch", None, 0), _nbytes(scratch), _stream(stream)), "moe_permute")
+        _arg(scratch, "scratch", None, 0), _nbytes(scratch), _stream(stream)),
+        "moe_permute_packed" if kblocked else "moe_permute")
 
 
 def permute_noalloc(cfg: MoeConfig, x, x_perm, row_token, slot_row, expert_count, expert_load, expert_offset, *,
@@ -320,12 +327,15 @@ def pack_weights(cfg: MoeConfig, which: int, w, packed=None, stream=None) -> tor
 
 
 def expert_ffn_packed(cfg: MoeConfig, x_perm, expert_offset, w1_packed, w2_packed, h, y_perm, workspace=None,
-                      stream=None):
-    """moe_expert_ffn_packed: expert_ffn on weights packed by pack_weights."""
+                      stream=None, x_kblocked: bool = False):
+    """moe_expert_ffn_packed: expert_ffn on weights packed by pack_weights;
+    x_kblocked says x_perm is K-blocked (permute(kblocked=True)); h is
+    written K-blocked."""
     n, dt = _dims(cfg), torch_dtype(cfg)
     rows, d = n["rows"], n["d"]
     _check(load_library().moe_expert_ffn_packed(
-        ctypes.byref(cfg), _arg(x_perm, "x_perm", dt, rows * d), _arg(expert_offset, "expert_offset", _I32, n["E"] + 1),
+        ctypes.byref(cfg), _arg(x_perm, "x_perm", dt, rows * d), 1 if x_kblocked else 0,
+        _arg(expert_offset, "expert_offset", _I32, n["E"] + 1),
         _packed_arg(cfg, w1_packed, PACK_W1), _packed_arg(cfg, w2_packed, PACK_W2), _arg(h, "h", dt, rows * cfg.d_ff),
         _arg(y_perm, "y_perm", dt, rows * d), _arg(workspace, "workspace", None, 0), _nbytes(workspace),
         _stream(stream)), "moe_expert_ffn_packed")

@@ -87,7 +87,17 @@ def sample_tokens(w: W.Workload, n: int, extra=(), seed: int = 1) -> np.ndarray:
     return np.array(sorted(base | set(pick)), np.int32)
 
 
-def check_routing_topk(w: W.Workload, layer, inp):
+def x_perm_rows(layer, n: int, kblocked: bool = False) -> np.ndarray:
+    """The first n rows of the layer's x_perm as bf16 bits; kblocked: the
+    buffer holds the K-blocked order ([d/32][rows][32]) of the packed path."""
+    xp = moe.to_host_bits(layer.view("x_perm"))
+    if kblocked:
+        R, K = xp.shape
+        xp = xp.reshape(K // 32, R, 32).transpose(1, 0, 2).reshape(R, K)
+    return xp[:n]
+
+
+def check_routing_topk(w: W.Workload, layer, inp, kblocked: bool = False):
     """Bit-exact routing and permutation against the oracle fed the GPU's logits."""
     lg = layer.view("logits").cpu().numpy()
     ref_lg = oracle.logits(inp["x"], inp["wr"], inp["bias"], inp["bias_stride"])
@@ -108,8 +118,7 @@ def check_routing_topk(w: W.Workload, layer, inp):
     n = d.n_rows
     assert np.array_equal(layer.view("row_token").cpu().numpy()[:n], d.row_token)
     # x_perm rows are the token rows, bit for bit
-    xp = moe.to_host_bits(layer.view("x_perm")[:n])
-    assert np.array_equal(xp, inp["x"][d.row_token]), "x_perm is not x[row_token]"
+    assert np.array_equal(x_perm_rows(layer, n, kblocked), inp["x"][d.row_token]), "x_perm is not x[row_token]"
     return lg, ref_idx, d
 
 
@@ -125,7 +134,7 @@ def check_output_topk(w: W.Workload, layer, inp, lg, toks):
     return err
 
 
-def check_routing_ec(w: W.Workload, layer, inp):
+def check_routing_ec(w: W.Workload, layer, inp, kblocked: bool = False):
     lg = layer.view("logits").cpu().numpy()
     ref_lg = oracle.logits(inp["x"], inp["wr"], inp["bias"], inp["bias_stride"])
     err = np.max(np.abs(lg - ref_lg)) / max(np.max(np.abs(ref_lg)), 1e-30)
@@ -154,8 +163,7 @@ def check_routing_ec(w: W.Workload, layer, inp):
     assert np.array_equal(sr, rows[order].astype(np.int32)), "CSR slot rows"
     assert np.array_equal(sw, ecw.ravel()[sr])
     n = w.E * C
-    xp = moe.to_host_bits(layer.view("x_perm")[:n])
-    assert np.array_equal(xp, inp["x"][ref_ec.ravel()])
+    assert np.array_equal(x_perm_rows(layer, n, kblocked), inp["x"][ref_ec.ravel()])
     return lg, sc, ref_ec
 
 

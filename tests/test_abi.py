@@ -108,11 +108,17 @@ def test_packed_argument_errors():
     assert lib.moe_pack_weights(ctypes.byref(cfg), 0, ctypes.c_void_p(264), ctypes.c_void_p(4096), None) == 1
     assert lib.moe_pack_weights(ctypes.byref(_cfg(dtype=0)), 0, fake, ctypes.c_void_p(4096), None) == 2
     # the packed FFN and layer refuse configurations they cannot run
-    st = lib.moe_expert_ffn_packed(ctypes.byref(_cfg(dtype=0)), fake, fake, fake, fake, fake, fake, fake, 1 << 30,
-                                   None)
+    st = lib.moe_expert_ffn_packed(ctypes.byref(_cfg(dtype=0)), fake, 0, fake, fake, fake, fake, fake, fake,
+                                   1 << 30, None)
     assert st == 2
-    st = lib.moe_expert_ffn_packed(ctypes.byref(_cfg(d_ff=200)), fake, fake, fake, fake, fake, fake, fake, 1 << 30,
-                                   None)
+    st = lib.moe_expert_ffn_packed(ctypes.byref(_cfg(d_ff=200)), fake, 1, fake, fake, fake, fake, fake, fake,
+                                   1 << 30, None)
+    assert st == 2
+    st = lib.moe_expert_ffn_packed(ctypes.byref(cfg), fake, 2, fake, fake, fake, fake, fake, fake, 1 << 30, None)
+    assert st == 1  # x_perm order neither row-major nor K-blocked
+    # the K-blocked permutation: packable configurations only
+    st = lib.moe_permute_packed(ctypes.byref(_cfg(dtype=0)), fake, fake, None, None, fake, fake, fake, None, None,
+                                fake, fake, fake, fake, 1 << 20, None)
     assert st == 2
     st = lib.moe_layer_fwd_packed(ctypes.byref(_cfg(d_ff_shared=72)), fake, fake, None, 0, fake, fake, fake, fake,
                                   fake, fake, 1 << 30, None)

@@ -50,6 +50,17 @@ def _bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def kblock(a: np.ndarray) -> np.ndarray:
+    """[rows, K] -> the K-blocked order [K/32][rows][32] include/moe.h describes."""
+    R, K = a.shape
+    return np.ascontiguousarray(a.reshape(R, K // 32, 32).transpose(1, 0, 2)).reshape(R, K)
+
+
+def unkblock(a: np.ndarray) -> np.ndarray:
+    R, K = a.shape
+    return np.ascontiguousarray(a.reshape(K // 32, R, 32).transpose(1, 0, 2)).reshape(R, K)
+
+
 def expected_packed(w: np.ndarray, n_out: int, swiglu: bool) -> np.ndarray:
     """The packed order of include/moe.h, from its description: column tiles
     of 256 weight rows (SwiGLU: 128 gate rows, then the matching up rows), K
@@ -134,12 +145,23 @@ def test_packed_ffn_matches_unpacked_and_oracle(act, d, d_ff, counts, tag):
     moe.expert_ffn(cfg, xd, offd, w1d, w2d, h0, y0, ws)
     w1p = moe.pack_weights(cfg, moe.PACK_W1, w1d)
     w2p = moe.pack_weights(cfg, moe.PACK_W2, w2d)
-    h1 = torch.full((rows, d_ff), 7.0, dtype=torch.bfloat16, device="cuda")
-    y1 = torch.full((rows, d), 7.0, dtype=torch.bfloat16, device="cuda")
-    moe.expert_ffn_packed(cfg, xd, offd, w1p, w2p, h1, y1, ws)
-    torch.cuda.synchronize()
+    # x_perm row-major, then K-blocked (as moe_permute_packed writes it): the
+    # same bits; h comes out K-blocked
+    xkb = torch.from_numpy(kblock(_bits(x)).view(np.int16)).view(torch.bfloat16).cuda()
+    outs = []
+    for x_in, kb in ((xd, False), (xkb, True)):
+        h1 = torch.full((rows, d_ff), 7.0, dtype=torch.bfloat16, device="cuda")
+        y1 = torch.full((rows, d), 7.0, dtype=torch.bfloat16, device="cuda")
+        moe.expert_ffn_packed(cfg, x_in, offd, w1p, w2p, h1, y1, ws, x_kblocked=kb)
+        torch.cuda.synchronize()
+        outs.append((h1, y1))
+    (h1, y1), (h2, y2) = outs
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "K-blocked x_perm changes y"
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16)), "K-blocked x_perm changes h"
+    # h rows of the kept rows (the rest of the buffer is not written)
+    h1_rows = unkblock(_bits(h1))[:rows]
     if tag != "mid":
-        assert torch.equal(h1.view(torch.int16), h0.view(torch.int16)), "h differs from the unpacked FFN"
+        assert np.array_equal(h1_rows, _bits(h0)[:rows]), "h differs from the unpacked FFN"
         assert torch.equal(y1.view(torch.int16), y0.view(torch.int16)), "y differs from the unpacked FFN"
     got = host_float(y1)
     xb, w1b, w2b = _bits(x), _bits(w1), _bits(w2)
@@ -159,6 +181,58 @@ def test_packed_ffn_matches_unpacked_and_oracle(act, d, d_ff, counts, tag):
             say(f"  expert {e}: max rel err {err:.3e}, element-wise {elem_rel_err(got[chk], ref):.3e} "
                 f"over {len(chk)} rows")
         assert err <= TOL_Y[W.BF16], e
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T,d,E,k,cf,routing,path", [
+    (700, 256, 12, 6, 0.0, W.SOFTMAX_ALL, "one launch"),
+    (3000, 8192, 8, 2, 0.0, W.SOFTMAX_TOPK, "one launch, two passes per row"),
+    (6000, 512, 16, 2, 1.0, W.SOFTMAX_ALL, "scan in every workgroup, capacity drops"),
+    (40000, 128, 256, 2, 0.0, W.SOFTMAX_ALL, "separate scan launch"),
+    (1500, 320, 16, 2, 0.0, W.EXPERT_CHOICE, "ExpertChoice"),
+])
+def test_permute_packed_is_permute_kblocked(T, d, E, k, cf, routing, path):
+    """moe_permute_packed: every output of moe_permute, with x_perm in the
+    K-blocked order (bit for bit once reordered on the host)."""
+    say(f"[permute packed] {path}: T={T} d={d} E={E} k={k} cf={cf}")
+    rng = np.random.default_rng(5)
+    ec = routing == W.EXPERT_CHOICE
+    C = 200 if ec else 0
+    cfg = moe.MoeConfig(T, d, E, 0 if ec else k, 128, 0, cf, C, W.BF16, W.SWIGLU, routing)
+    rows = moe.max_rows(cfg)
+    x = _bf16(rng.standard_normal((T, d))).cuda()
+    kw = {}
+    if ec:
+        tok = np.sort(np.stack([rng.choice(T, C, replace=False) for _ in range(E)]), axis=1).astype(np.int32)
+        kw = dict(ec_token=torch.from_numpy(tok).cuda(), ec_w=torch.rand(E, C, device="cuda"),
+                  slot_w=torch.empty(E * C, device="cuda"), tok_ptr=torch.empty(T + 1, dtype=torch.int32,
+                                                                                  device="cuda"))
+    else:
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        kw = dict(topk_idx=torch.from_numpy(idx).cuda(),
+                  scratch=torch.empty(max(moe.permute_scratch_bytes(cfg), 16), dtype=torch.uint8, device="cuda"))
+    outs = []
+    for kb in (False, True):
+        o = dict(x_perm=torch.zeros((rows, d), dtype=torch.bfloat16, device="cuda"),
+                 row_token=torch.full((rows,), -7, dtype=torch.int32, device="cuda"),
+                 slot_row=torch.empty(E * C if ec else T * k, dtype=torch.int32, device="cuda"),
+                 cnt=torch.empty(E, dtype=torch.int32, device="cuda"),
+                 load=torch.empty(E, dtype=torch.int32, device="cuda"),
+                 off=torch.empty(E + 1, dtype=torch.int32, device="cuda"))
+        moe.permute(cfg, x, o["x_perm"], o["row_token"], o["slot_row"], o["cnt"], o["load"], o["off"],
+                    kblocked=kb, **kw)
+        torch.cuda.synchronize()
+        if ec:
+            o["slot_w"], o["tok_ptr"] = kw["slot_w"].clone(), kw["tok_ptr"].clone()
+        outs.append({n: t.cpu() for n, t in o.items()})
+    plain, packed = outs
+    for n in plain:
+        if n != "x_perm":
+            assert torch.equal(plain[n], packed[n]), n
+    used = int(plain["off"][-1])
+    xp = plain["x_perm"].view(torch.int16).numpy().view(np.uint16)
+    xk = unkblock(packed["x_perm"].view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(xp[:used], xk[:used]), "K-blocked x_perm differs"
 
 
 def _run_both(w: W.Workload):
@@ -187,10 +261,10 @@ def test_packed_layer_matches_layer_fwd_small(name):
         assert torch.equal(layer.y.view(torch.int16), y_plain.view(torch.int16)), "packed layer differs"
     toks = np.arange(w.T, dtype=np.int32)
     if w.routing == W.EXPERT_CHOICE:
-        lg, sc, _ = check_routing_ec(w, layer, inp)
+        lg, sc, _ = check_routing_ec(w, layer, inp, kblocked=True)
         check_output_ec(w, layer, inp, lg, sc, toks)
     else:
-        lg, _, _ = check_routing_topk(w, layer, inp)
+        lg, _, _ = check_routing_topk(w, layer, inp, kblocked=True)
         check_output_topk(w, layer, inp, lg, toks)
 
 
@@ -210,8 +284,8 @@ def test_packed_layer_full_size(name):
     assert torch.equal(layer.y.view(torch.int16), y_plain.view(torch.int16)), "packed layer differs"
     cover = tile_cover_tokens(w, layer)
     if w.routing == W.EXPERT_CHOICE:
-        lg, sc, _ = check_routing_ec(w, layer, inp)
+        lg, sc, _ = check_routing_ec(w, layer, inp, kblocked=True)
         check_output_ec(w, layer, inp, lg, sc, sample_tokens(w, 8, extra=list(cover)))
     else:
-        lg, _, _ = check_routing_topk(w, layer, inp)
+        lg, _, _ = check_routing_topk(w, layer, inp, kblocked=True)
         check_output_topk(w, layer, inp, lg, sample_tokens(w, 8, extra=list(cover)))
