@@ -50,3 +50,52 @@ def test_random_shapes_match_oracle(w):
     else:
         lg, _, _ = check_routing_topk(w, layer, inp)
         check_output_topk(w, layer, inp, lg, toks)
+
+
+@st.composite
+def packable_shapes(draw):
+    """bf16 shapes the packed path takes: d_model, d_ff, d_ff_shared multiples of 64."""
+    E = draw(st.integers(1, 40))
+    k = draw(st.integers(1, min(E, 8)))
+    T = draw(st.integers(1, 1200))
+    d = 64 * draw(st.integers(1, 10))
+    d_ff = 64 * draw(st.integers(1, 14))
+    act = draw(st.sampled_from([W.GELU, W.SWIGLU]))
+    routing = draw(st.sampled_from([W.SOFTMAX_ALL, W.SOFTMAX_TOPK, W.EXPERT_CHOICE]))
+    cf = draw(st.sampled_from([0.0, 0.5, 1.0, 1.25]))
+    shared = draw(st.sampled_from([0, 64 * draw(st.integers(1, 6))]))
+    C = draw(st.integers(1, T)) if routing == W.EXPERT_CHOICE else 0
+    return W.Workload("sweep_packed", T=T, d=d, E=E, k=k, d_ff=d_ff, act=act, dtype=W.BF16,
+                      routing=routing, cf=0.0 if C else cf, ec_capacity=C, d_ff_shared=shared,
+                      wr_std=1.0 / np.sqrt(d))
+
+
+@pytest.mark.gpu
+@settings(max_examples=30, deadline=None, derandomize=True, phases=[Phase.explicit, Phase.generate],
+          report_multiple_bugs=False, suppress_health_check=list(HealthCheck))
+@given(w=packable_shapes())
+def test_random_shapes_packed_path(w):
+    """moe_layer_fwd_packed on random packable shapes: routing, K-blocked
+    permutation and every token's output against the oracle, and the bits of
+    moe_layer_fwd wherever both orders run the same GEMM kernel (at most 128
+    or at least 192 rows per expert on average)."""
+    import torch
+    from mixture_experts_layer_topkrouter_amd import moe
+    say(f"[sweep packed] T={w.T} d={w.d} E={w.E} k={w.k} d_ff={w.d_ff} shared={w.d_ff_shared} act={w.act} "
+        f"routing={w.routing} cf={w.cf} C={w.ec_capacity}")
+    layer, inp = run_layer(w)
+    y_plain = layer.y.clone()
+    layer.pack()
+    layer.y.fill_(7.0)
+    layer.forward(packed=True)
+    torch.cuda.synchronize()
+    avg = moe.max_rows(layer.cfg) // w.E
+    if not 128 < avg < 192:
+        assert torch.equal(layer.y.view(torch.int16), y_plain.view(torch.int16)), "packed layer differs"
+    toks = np.arange(w.T, dtype=np.int32)
+    if w.routing == W.EXPERT_CHOICE:
+        lg, sc, _ = check_routing_ec(w, layer, inp, kblocked=True)
+        check_output_ec(w, layer, inp, lg, sc, toks)
+    else:
+        lg, _, _ = check_routing_topk(w, layer, inp, kblocked=True)
+        check_output_topk(w, layer, inp, lg, toks)
