@@ -136,7 +136,8 @@ def test_packed_argument_errors():
 
 
 @pytest.mark.parametrize("T,d,E,k,d_ff", [(64, 512, 8, 2, 1024), (1200, 256, 16, 1, 512), (4096, 256, 8, 2, 8192),
-                                          (700, 264, 4, 2, 264), (16, 64, 4, 1, 64)])
+                                          (700, 264, 4, 2, 264), (16, 64, 4, 1, 64), (2400, 256, 16, 1, 8192),
+                                          (2400, 264, 16, 1, 8192)])
 def test_ffn_workspace_rule(T, d, E, k, d_ff):
     cfg = _cfg(num_tokens=T, d_model=d, num_experts=E, top_k=k, d_ff=d_ff)
     assert moe.expert_ffn_workspace_bytes(cfg) == expected_ffn_workspace(W.BF16, T * k // E, d, d_ff)
