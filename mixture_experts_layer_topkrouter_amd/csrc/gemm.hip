@@ -383,8 +383,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   // (TN: its first column), B at the expert's weights (TN: the column
   // tile's first column); a stage advances them by a_step / b_step bytes
   const int64_t kfirst = static_cast<int64_t>(job.k0) + static_cast<int64_t>(job.kb) * DK;
+  // K-blocked A: the tile's K stage is the 256 row pieces starting at row0
+  // of the stage's 32-wide slice
+  static_assert(kKbRowBytes == DK * 2, "a K-blocked row piece is one stage of one row");
+  const bool a_kb = LAY == LAY_NT && p.a_kb;
   const char *A = static_cast<const char *>(p.A) +
-                  (AT ? kfirst * p.lda + row0 : static_cast<int64_t>(row0) * p.lda + job.kb * DK) * 2;  // K-blocked: below
+                  (a_kb ? (static_cast<int64_t>(job.kb) * p.max_rows + row0) * kKbRowBytes
+                        : (AT ? kfirst * p.lda + row0 : static_cast<int64_t>(row0) * p.lda + job.kb * DK) * 2);
   // packed B: the stage blocks of column tile nt follow each other, 16 KB
   // apart, and a stage is read as one contiguous block
   static_assert(kPackK == DK && kPackBlockBytes == DSTAGE * 2, "a packed block is one B stage");
@@ -395,11 +400,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
                           : (BT ? (LAY == LAY_TN ? 0 : static_cast<int64_t>(e) * p.b_stride) + kfirst * p.ldb +
                                       static_cast<int64_t>(nt) * BN
                                 : static_cast<int64_t>(e) * p.b_stride + job.kb * DK) * 2);
-  // K-blocked A: the tile's K stage is the 256 row pieces starting at row0
-  // of the stage's 32-wide slice
-  static_assert(kKbRowBytes == DK * 2, "a K-blocked row piece is one stage of one row");
-  const bool a_kb = LAY == LAY_NT && p.a_kb;
-  if (a_kb) A = static_cast<const char *>(p.A) + (static_cast<int64_t>(job.kb) * p.max_rows + row0) * kKbRowBytes;
   const int64_t a_step = a_kb ? p.max_rows * kKbRowBytes : AT ? static_cast<int64_t>(DK) * p.lda * 2 : DK * 2;
   const int64_t b_step = packed ? kPackBlockBytes : BT ? static_cast<int64_t>(DK) * p.ldb * 2 : DK * 2;
 
