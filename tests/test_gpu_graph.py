@@ -1,4 +1,4 @@
-"""moe_layer_fwd captured into a HIP graph (torch.cuda.CUDAGraph over the
+"""moe_layer_fwd and moe_layer_fwd_packed captured into a HIP graph (torch.cuda.CUDAGraph over the
 caller's stream; the library's shared-expert side stream joins the capture
 through its fork / join events) and replayed: every replay, with eager calls
 and synchronisations between the replays, must give the eager result bit for
@@ -27,24 +27,36 @@ def bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
 
 
+# the packed path (moe_layer_fwd_packed): widths multiples of 64
+PACKED_CASES = {
+    "decode_small": CASES["decode_small"],
+    "finegrained_small": W.small_variant(W.WORKLOADS["finegrained_shared_bf16"], T=700, d=256, E=12, d_ff=192,
+                                         d_ff_shared=320, wr_std=1.0 / 16.0),
+    "correlated_ec_small": W.small_variant(W.WORKLOADS["correlated_ec_bf16"], T=1500, d=256, E=16, d_ff=256,
+                                           ec_capacity=200),
+}
+
+
 @pytest.mark.gpu
-@pytest.mark.parametrize("name", list(CASES))
-def test_layer_fwd_graph_replays_match_eager(name):
-    w = CASES[name]
+@pytest.mark.parametrize("name,packed", [(n, False) for n in CASES] + [(n, True) for n in PACKED_CASES])
+def test_layer_fwd_graph_replays_match_eager(name, packed):
+    w = (PACKED_CASES if packed else CASES)[name]
     layer = moe.MoELayer(moe.make_config(w), moe.upload(W.make_inputs(w, seed=3)))
-    layer.forward()
+    if packed:
+        layer.pack()
+    layer.forward(packed=packed)
     torch.cuda.synchronize()
     ref = bits(layer.y)
 
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
-        layer.forward()  # warm-up on the capture stream
+        layer.forward(packed=packed)  # warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=cap):
-        layer.forward()
+        layer.forward(packed=packed)
     torch.cuda.synchronize()
 
     for rep in range(4):
@@ -53,6 +65,6 @@ def test_layer_fwd_graph_replays_match_eager(name):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bits(layer.y), ref), f"replay {rep} differs from the eager result"
-        layer.forward()  # eager work between the replays
+        layer.forward(packed=packed)  # eager work between the replays
         torch.cuda.synchronize()
         assert np.array_equal(bits(layer.y), ref), f"eager call after replay {rep} differs"
