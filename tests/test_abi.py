@@ -127,6 +127,12 @@ def test_packed_argument_errors():
     st = lib.moe_layer_fwd_packed(ctypes.byref(cfg), fake, fake, None, 0, fake, fake, None, None, fake, fake,
                                   1 << 30, None)
     assert st == 1
+    # an empty batch is a no-op on the packed path too (nothing is enqueued;
+    # empty buffers may be NULL)
+    empty = _cfg(num_tokens=0, d_ff_shared=128)
+    assert lib.moe_layer_fwd_packed(ctypes.byref(empty), None, None, None, 0, None, None, None, None, None, None, 0,
+                                    None) == 0
+    assert lib.moe_expert_ffn_packed(ctypes.byref(empty), None, 1, None, None, None, None, None, None, 0, None) == 0
     # the binding checks the packed buffer's size before the call
     small = torch.empty(16, dtype=torch.uint8)
     with pytest.raises(ValueError, match="needs at least"):
