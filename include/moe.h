@@ -26,7 +26,9 @@
  *   expert_offset[E] (device) holds the number actually used.
  * - Same inputs give bitwise-identical outputs (no floating-point atomics).
  * - Pointers to floating-point tensors must be 16-byte aligned; d_model and
- *   d_ff (and d_ff_shared) must be multiples of 8.
+ *   d_ff (and d_ff_shared) must be multiples of 8.  Widths of 2^22 or more,
+ *   moe_max_rows() of 2^25 - 256 or more, or any GEMM operand past 2^31
+ *   elements return MOE_ERR_UNSUPPORTED (32-bit offsets).
  * - T = 0 is valid: every call returns MOE_OK and buffers whose size is zero
  *   may be NULL; moe_permute still writes the (zero) counts and offsets.
  */

@@ -65,11 +65,16 @@ int64_t max_rows_of(const moe_config *c) {
   return a < lim ? a : lim;
 }
 
-// 32-bit element offsets inside the GEMM kernels must not overflow.
+// 32-bit element offsets inside the GEMM kernels must not overflow, and the
+// byte offsets of a tile's A rows must stay below the 2^31-byte range of the
+// range-checked loads that turn pad rows into zeros: 256 row-major rows of
+// width below 2^22, or K-blocked slices of fewer than 2^25 - 256 rows.
 bool gemm_fits(const moe_config *c, int64_t rows, int dff) {
   const int64_t lim = INT32_MAX;
   const int64_t n_up = c->act == MOE_ACT_SWIGLU ? 2 : 1;
-  return rows * c->d_model < lim && rows * dff < lim && n_up * dff * c->d_model < lim;
+  const int64_t wlim = int64_t{1} << 22, rlim = (int64_t{1} << 25) - 256;
+  return rows * c->d_model < lim && rows * dff < lim && n_up * dff * c->d_model < lim && c->d_model < wlim &&
+         dff < wlim && rows < rlim;
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }

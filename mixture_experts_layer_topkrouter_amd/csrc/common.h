@@ -129,6 +129,27 @@ __device__ __forceinline__ void dma16_nt(uint32_t voff, const void *sbase, uint3
                : "memory", "m0");
 }
 
+// The same 16-byte direct-to-LDS load issued as a range-checked buffer load
+// (MUBUF, raw: stride 0, num_records = kDmaRange bytes from sbase): a lane
+// whose offset is kDmaSkip reads no memory and its 16 LDS bytes are written
+// as zeros.  Rows a GEMM tile holds past its last real row load this way, so
+// they multiply as zeros instead of as copies of a real row: the results of
+// the real rows are the same, but a matrix core fed zeros draws less power,
+// and this power-limited card then runs a higher clock.  Every real offset
+// must stay below kDmaRange (the host bounds the widths accordingly).
+constexpr uint32_t kDmaRange = 0x80000000u;
+constexpr uint32_t kDmaSkip = 0x80000000u;
+__device__ __forceinline__ void dma16_zp(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  // words: base[31:0]; base[47:32] with stride 0; num_records; the gfx9
+  // raw-buffer format word (32-bit data format, no swizzle, no index add)
+  const u32x4 rsrc = {static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32), kDmaRange, 0x00020000u};
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(m0v)
+               : "memory", "m0");
+}
+
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)p));

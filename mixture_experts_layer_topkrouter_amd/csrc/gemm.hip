@@ -416,7 +416,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
   // [(WAVES*i+w)*64, +64), i.e. rows (WAVES*i+w)*16 .. +16; lane l -> row
   // r = q/4, stored chunk q%4, which holds logical chunk (q%4) ^ ((r>>2)&3).
   // Per-lane byte offsets from A / B (they fit 32 bits: the host limits every
-  // operand to 2^31 elements).
+  // operand to 2^31 elements, and the widths below 2^22, so that a row-major
+  // A tile's offsets stay below kDmaRange).
   // [K][.] operands: LDS chunk slot q is row kk = q/32, stored chunk q%32,
   // which holds logical chunk (q%32) ^ tr_swz(kk); columns past the operand's
   // width (partial tiles) read its last valid 8 columns instead.
@@ -432,8 +433,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
       const int col = min(tc * 8, p.m_rows - row0 - 8);
       a_off[i] = static_cast<uint32_t>((static_cast<int64_t>(kk) * p.lda + col) * 2);
     } else {
-      a_off[i] = a_kb ? static_cast<uint32_t>(min(r, rows - 1) * kKbRowBytes + c * 16)
-                      : static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
+      // rows past the tile's last real row load as zeros (dma16_zp)
+      a_off[i] = r >= rows ? kDmaSkip
+                 : a_kb    ? static_cast<uint32_t>(r * kKbRowBytes + c * 16)
+                           : static_cast<uint32_t>((static_cast<int64_t>(r) * p.lda + c * 8) * 2);
     }
     if constexpr (BT) {
       const int col = min(tc * 8, p.n_out - nt * BN - 8);
@@ -451,12 +454,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
                         : static_cast<uint32_t>((static_cast<int64_t>(br) * p.ldb + c * 8) * 2);
     }
   }
+  // A loads: range-checked for the row-major layouts, so pad rows land as
+  // zeros; the [K][M] layout clamps its columns instead
+  auto dma_a = [&](uint32_t off, const char *src, uint32_t lds) {
+    if constexpr (AT) dma16(off, src, lds);
+    else dma16_zp(off, src, lds);
+  };
   // stage st of this piece: K elements [st*DK, st*DK + DK) past A / B
   auto issue = [&](auto S, int st) {
     const uint32_t base = lds_addr_of(slot(S));
 #pragma unroll
     for (int i = 0; i < ND / 2; ++i) {
-      dma16(a_off[i], A + st * a_step, base + (WAVES * i + w) * 64 * 16);
+      dma_a(a_off[i], A + st * a_step, base + (WAVES * i + w) * 64 * 16);
       dma16(b_off[i], B + st * b_step, base + DSTAGE * 2 + (WAVES * i + w) * 64 * 16);
     }
   };
@@ -606,7 +615,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_dma_kernel(GemmParams p)
           } else if ((t & 3) == kLoadSlot) {
             if (refill) {
               const int dd = t >> 2, ii = dd >> 1;
-              if ((dd & 1) == 0) dma16(a_off[ii], A + (kt + 5) * a_step, dbase + (WAVES * ii + w) * 64 * 16);
+              if ((dd & 1) == 0) dma_a(a_off[ii], A + (kt + 5) * a_step, dbase + (WAVES * ii + w) * 64 * 16);
               else dma16(b_off[ii], B + (kt + 5) * b_step, dbase + DSTAGE * 2 + (WAVES * ii + w) * 64 * 16);
             }
           }

@@ -123,8 +123,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
   for (int i = 0; i < C::A_INSTR; ++i) {
     const int r = 8 * (w + 4 * i) + (l >> 3);
     const int c = (l & 7) ^ ((r >> 1) & 7);
-    a_off[i] = a_kb ? static_cast<uint32_t>((c >> 2) * kb_slice + min(r, rows - 1) * kKbRowBytes + (c & 3) * 16)
-                    : static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * p.lda + c * 8) * 2);
+    // rows past the tile's last real row load as zeros (dma16_zp)
+    a_off[i] = r >= rows ? kDmaSkip
+               : a_kb    ? static_cast<uint32_t>((c >> 2) * kb_slice + r * kKbRowBytes + (c & 3) * 16)
+                         : static_cast<uint32_t>((static_cast<int64_t>(r) * p.lda + c * 8) * 2);
   }
 #pragma unroll
   for (int i = 0; i < C::B_INSTR; ++i) {
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_skinny_kernel(GemmParams p
   auto issue = [&](auto S, int st) {
     const uint32_t base = lds_addr_of(slot(S));
 #pragma unroll
-    for (int i = 0; i < C::A_INSTR; ++i) dma16(a_off[i], A + st * a_step, base + (w + 4 * i) * 1024);
+    for (int i = 0; i < C::A_INSTR; ++i) dma16_zp(a_off[i], A + st * a_step, base + (w + 4 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_INSTR; ++i)
       if constexpr (BNT) dma16_nt(b_off[i], B + st * b_step, base + C::A_ELEMS * 2 + (w + 4 * i) * 1024);

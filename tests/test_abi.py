@@ -206,6 +206,23 @@ def test_unsupported_and_workspace_errors():
     assert st == 1
 
 
+@pytest.mark.parametrize("kw", [dict(d_model=1 << 22), dict(d_ff=1 << 22), dict(d_ff_shared=1 << 22)])
+def test_widths_past_the_range_checked_loads_are_unsupported(kw):
+    """A GEMM tile's A rows are loaded through range-checked buffer loads
+    (pad rows past an expert's last row come in as zeros), whose byte
+    offsets must stay below 2^31: a width of 2^22 or more is refused on the
+    host, before anything is enqueued (the fake pointers are never used)."""
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(256)
+    cfg = _cfg(num_tokens=1, num_experts=1, top_k=1, act=0, **kw)
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), fake, fake, None, 0, fake, fake, fake, fake, fake, fake, 1 << 62,
+                           None)
+    assert st == 2
+    if "d_ff_shared" not in kw:
+        st = lib.moe_expert_ffn(ctypes.byref(cfg), fake, fake, fake, fake, fake, fake, fake, 1 << 62, None)
+        assert st == 2
+
+
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
 def test_backward_workspace_layout(name):
     """Rows of the backward's padded layout: each expert's block rounded up to
