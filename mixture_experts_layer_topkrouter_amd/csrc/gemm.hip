@@ -814,8 +814,14 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
   }
 }
 
-// fp32 path: plain FMA tiles (64 rows x 64 B rows x 16), 4x4 per thread.
-constexpr int F_BM = 64, F_BN = 64, F_BK = 16;
+// fp32 path: plain FMA tiles (64 rows x 64 B rows), 4x4 per thread, K in
+// 64-wide chunks staged through LDS; the next chunk is loaded into registers
+// while the current one is multiplied, so a tile pays about one memory round
+// trip per chunk instead of one per 16 K values (the fp32 workloads are small
+// enough that these round trips, not bandwidth, set the time).  Each output
+// still sums its products in K order.
+constexpr int F_BM = 64, F_BN = 64, F_BK = 64;
+constexpr int F_LD = F_BM * F_BK / kThreads;  // elements of A (and of B) a thread stages per chunk
 
 template <int ACT>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
@@ -831,14 +837,17 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < p.K; k0 += F_BK) {
+  // element i of this thread's share: row r = q / F_BK, K offset kk = q % F_BK
+  // of the chunk (q = tid + i * kThreads), so a wave reads whole 256-B runs
+  float ra[F_LD], rb[F_LD];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < F_LD; ++i) {
       const int q = tid + i * kThreads;
       const int r = q / F_BK, kk = q % F_BK;
       const int gk = k0 + kk;
       const int64_t ar = row0 + min(r, rows - 1);
-      sA[kk][r] = gk < p.K ? A[ar * p.lda + gk] : 0.f;
+      ra[i] = gk < p.K ? A[ar * p.lda + gk] : 0.f;
       int br;
       if (ACT == ACT_SWIGLU) {
         const int col = nt * (F_BN / 2) + (r & (F_BN / 2 - 1));
@@ -847,9 +856,19 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
         const int col = nt * F_BN + r;
         br = col < p.n_out ? col : 0;
       }
-      sB[kk][r] = gk < p.K ? B[static_cast<int64_t>(br) * p.ldb + gk] : 0.f;
+      rb[i] = gk < p.K ? B[static_cast<int64_t>(br) * p.ldb + gk] : 0.f;
+    }
+  };
+  load(0);
+  for (int k0 = 0; k0 < p.K; k0 += F_BK) {
+#pragma unroll
+    for (int i = 0; i < F_LD; ++i) {
+      const int q = tid + i * kThreads;
+      sA[q % F_BK][q / F_BK] = ra[i];
+      sB[q % F_BK][q / F_BK] = rb[i];
     }
     __syncthreads();
+    if (k0 + F_BK < p.K) load(k0 + F_BK);
 #pragma unroll
     for (int kk = 0; kk < F_BK; ++kk) {
       float a[4], b[4];

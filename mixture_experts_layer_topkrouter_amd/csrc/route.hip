@@ -395,20 +395,50 @@ __global__ __launch_bounds__(NW * kWave) void route_bf16_kernel(
 
 constexpr int kF32Rows = 16;
 
+// fp32 logits: the workgroup's 16 token rows and the router's rows are
+// staged through LDS in 64-wide chunks of d (coalesced loads, one memory
+// round trip per chunk); thread i owns logits i, i + 256, ... of the tile
+// (row i / E, expert i % E) and adds its products in d order.
+constexpr int kF32Chunk = 64;
+
 template <int NT>
 __global__ __launch_bounds__(kRouteThreads) void route_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
     int64_t bias_stride, int T, int d, int E, int k, int routing, float *__restrict__ logits,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, float *__restrict__ scores) {
+  constexpr int DC = kF32Chunk;
   __shared__ float tile[kF32Rows * 256];
+  __shared__ float sx[kF32Rows][DC + 1];
+  __shared__ float sw[16 * NT][DC + 1];
   const int t0 = blockIdx.x * kF32Rows;
-  for (int i = threadIdx.x; i < kF32Rows * E; i += blockDim.x) {
-    const int r = i / E, e = i - (i / E) * E;
-    const int t = t0 + r;
-    float s = 0.f;
-    if (t < T)
-      for (int kk = 0; kk < d; ++kk) s = fmaf(x[(int64_t)t * d + kk], wr[(int64_t)e * d + kk], s);
-    tile[r * E + e] = s;
+  float acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = 0.f;
+  for (int c0 = 0; c0 < d; c0 += DC) {
+    const int n = min(DC, d - c0);
+    __syncthreads();  // every thread is done with the previous chunk
+    for (int q = threadIdx.x; q < kF32Rows * DC; q += kRouteThreads) {
+      const int r = q / DC, kk = q - (q / DC) * DC;
+      sx[r][kk] = (t0 + r < T && kk < n) ? x[static_cast<int64_t>(t0 + r) * d + c0 + kk] : 0.f;
+    }
+    for (int q = threadIdx.x; q < E * DC; q += kRouteThreads) {
+      const int e = q / DC, kk = q - (q / DC) * DC;
+      sw[e][kk] = kk < n ? wr[static_cast<int64_t>(e) * d + c0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int i = threadIdx.x + j * kRouteThreads;
+      if (i >= kF32Rows * E) continue;
+      const int r = i / E, e = i - (i / E) * E;
+      if (t0 + r >= T) continue;
+      for (int kk = 0; kk < n; ++kk) acc[j] = fmaf(sx[r][kk], sw[e][kk], acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int i = threadIdx.x + j * kRouteThreads;
+    if (i < kF32Rows * E) tile[(i / E) * E + i % E] = t0 + i / E < T ? acc[j] : 0.f;
   }
   __syncthreads();
   finish_logits(tile, E, kF32Rows, t0, T, E, bias, bias_stride, logits);
