@@ -814,13 +814,14 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(GemmParams p) {
   }
 }
 
-// fp32 path: plain FMA tiles (64 rows x 64 B rows), 4x4 per thread, K in
-// 64-wide chunks staged through LDS; the next chunk is loaded into registers
-// while the current one is multiplied, so a tile pays about one memory round
-// trip per chunk instead of one per 16 K values (the fp32 workloads are small
-// enough that these round trips, not bandwidth, set the time).  Each output
-// still sums its products in K order.
-constexpr int F_BM = 64, F_BN = 64, F_BK = 64;
+// fp32 path: plain FMA tiles (32 rows x 32 B rows), 2x2 outputs per thread,
+// K in 64-wide chunks staged through LDS, the next chunk loaded into
+// registers while the current one is multiplied.  The fp32 workloads are
+// small: memory round trips (one per chunk) and each workgroup's own work,
+// not bandwidth, set their time, hence small tiles and wide chunks.  Each
+// output still sums its products in K order.
+constexpr int F_BM = 32, F_BN = 32, F_BK = 64;
+constexpr int F_TM = F_BM / 16;  // outputs per thread along each tile side (16 x 16 threads)
 constexpr int F_LD = F_BM * F_BK / kThreads;  // elements of A (and of B) a thread stages per chunk
 
 template <int ACT>
@@ -832,11 +833,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const float *A = static_cast<const float *>(p.A);
   const float *B = static_cast<const float *>(p.B) + static_cast<int64_t>(e) * p.b_stride;
-  float acc[4][4];
+  float acc[F_TM][F_TM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < F_TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int j = 0; j < F_TM; ++j) acc[i][j] = 0.f;
   // element i of this thread's share: row r = q / F_BK, K offset kk = q % F_BK
   // of the chunk (q = tid + i * kThreads), so a wave reads whole 256-B runs
   float ra[F_LD], rb[F_LD];
@@ -871,37 +872,40 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
     if (k0 + F_BK < p.K) load(k0 + F_BK);
 #pragma unroll
     for (int kk = 0; kk < F_BK; ++kk) {
-      float a[4], b[4];
+      float a[F_TM], b[F_TM];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty * 4 + i];
+      for (int i = 0; i < F_TM; ++i) a[i] = sA[kk][ty * F_TM + i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int bc = (ACT == ACT_SWIGLU) ? ((j < 2) ? tx * 2 + j : F_BN / 2 + tx * 2 + (j - 2)) : tx * 4 + j;
+      for (int j = 0; j < F_TM; ++j) {
+        // SwiGLU: the first half of a thread's columns are gates, the second
+        // half the matching up columns, F_BN / 2 further
+        constexpr int H = F_TM / 2;
+        const int bc = (ACT == ACT_SWIGLU) ? ((j < H) ? tx * H + j : F_BN / 2 + tx * H + (j - H)) : tx * F_TM + j;
         b[j] = sB[kk][bc];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < F_TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < F_TM; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
     __syncthreads();
   }
   float *C = static_cast<float *>(p.C);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lr = ty * 4 + i;
+  for (int i = 0; i < F_TM; ++i) {
+    const int lr = ty * F_TM + i;
     if (lr >= rows) continue;
     float *crow = C + static_cast<int64_t>(row0 + lr) * p.ldc;
     if (ACT == ACT_SWIGLU) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = nt * (F_BN / 2) + tx * 2 + j;
-        if (col < p.n_out) crow[col] = silu(acc[i][j]) * acc[i][j + 2];
+      for (int j = 0; j < F_TM / 2; ++j) {
+        const int col = nt * (F_BN / 2) + tx * (F_TM / 2) + j;
+        if (col < p.n_out) crow[col] = silu(acc[i][j]) * acc[i][j + F_TM / 2];
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = nt * F_BN + tx * 4 + j;
+      for (int j = 0; j < F_TM; ++j) {
+        const int col = nt * F_BN + tx * F_TM + j;
         if (col < p.n_out) crow[col] = (ACT == ACT_GELU) ? gelu_erf(acc[i][j]) : acc[i][j];
       }
     }
