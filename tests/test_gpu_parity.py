@@ -47,6 +47,10 @@ SMALL = {
     "correlated_small": W.small_variant(WL["correlated_top2_bf16"], T=1500, d=256, E=16, d_ff=200),
     "correlated_ec_small": W.small_variant(WL["correlated_ec_bf16"], T=1500, d=256, E=16, d_ff=200,
                                            ec_capacity=187),
+    # fp32 with 200 experts (the router's widest tile: 16 logits per thread,
+    # the router rows staged 64 columns at a time) and d_model 136 (a partial
+    # last column chunk), capacity drops
+    "fp32_many_experts_small": W.small_variant(WL["tiny_top2_fp32"], T=300, d=136, E=200, k=4, d_ff=72),
     # d_model not a multiple of the router's 64-wide K stages (its last stage
     # holds 8 columns), 24 experts padded to 32, 6 slots, 333 tokens (a
     # partial token tile)
