@@ -312,6 +312,12 @@ __global__ __launch_bounds__(NW * kWave) void route_bf16_kernel(
     for (int jj = 0; jj < LPW; ++jj) {
       if (jj == LPW - 1 && NHI && w >= NHI) break;  // wave-uniform
       const int i = w + NW * jj;
+      // with one load per wave per stage, a wave whose rows are all padding
+      // rows of W_r (experts E..EP-1, whose logits are never read) skips it:
+      // it then has no loads in flight, and the waits of the other waves
+      // still cover every row that is read
+      if constexpr (LPW == 1 && NHI == 0)
+        if (!is_x[jj] && RPI * i - BT >= E) break;
       uint32_t off = voff[jj];
       if (tail) {
         const int over = s * CPR + lchunk[jj] - (nchunk - 1);  // chunks past the last real one
